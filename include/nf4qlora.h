@@ -1,0 +1,237 @@
+/*
+ * nf4qlora.h - C ABI of the MI355X (gfx950) NF4 + LoRA layer-streaming library.
+ *
+ * The library computes the hot path of layer-streamed QLoRA training: a frozen
+ * linear layer stored as 4-bit NormalFloat (NF4) codes with one float32 absmax
+ * per 64 weights, a trainable rank-r LoRA adapter beside it, forward and
+ * backward, and a decoder stack fed one layer at a time from pinned host
+ * memory through two device buffers.
+ *
+ * Sources (the Soup pages): the frozen base streams from host RAM one decoder
+ * layer at a time while only the LoRA adapter trains (Soup README intro,
+ * "Citing Soup"; blog "The trick: layer streaming"); it is stored as NF4,
+ * quantised once offline, and dequantised on the fly per layer (soup-cli
+ * 0.72.2 docs "NF4 streaming (quantization: 4bit)"); copies come from
+ * page-locked memory into two pre-allocated device buffers so they overlap
+ * compute, and a pageable store falls back with its cost reported (CHANGELOG
+ * [0.72.0]; docs "Layer Streaming", "Honest scope" and "Troubleshooting");
+ * streaming is a pure scheduling change, so a streamed run is bit-identical to
+ * a resident one (blog "Why the evidence is better than usual"; CHANGELOG
+ * [0.72.2] "Correctness"). The NF4 codebook, block size, scale format and
+ * rounding are not on the pages; the library follows the QLoRA paper
+ * (Dettmers et al. 2023, section 3), with block 64 and a float32 absmax.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless the argument says "host".
+ *  - Matrices are row-major. x is [M x K], the frozen weight W is [N x K]
+ *    (K contiguous), LoRA A is [r x K], B is [N x r], s = alpha / r.
+ *  - bf16 tensors are IEEE bfloat16 (uint16 storage), float32 is IEEE binary32.
+ *  - Every call validates all of its arguments before it enqueues anything; on
+ *    an error (status < 0) nothing has been enqueued and the outputs are
+ *    untouched. ql_last_error() then names the offending argument and rule.
+ *  - Calls are asynchronous on the given stream(s) unless stated otherwise.
+ *    Buffers must stay alive until the stream has passed the call.
+ *  - The library never mutates its inputs and keeps no state between calls,
+ *    except one 4-byte device flag per device used by nf4_quantize.
+ *  - The caller allocates every buffer (device memory, pinned host store,
+ *    workspaces); the *_workspace / *_layout calls give the sizes.
+ *  - Results are deterministic: no atomics take part in any reduction, and
+ *    kernel selection does not depend on pointer values.
+ */
+#ifndef NF4QLORA_H
+#define NF4QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ql_status;
+
+enum {
+  QL_OK = 0,
+  /* Success, but the host store is pageable: copies could not overlap compute
+     (docs "Layer Streaming": the pageable fallback runs and reports its cost). */
+  QL_WARN_PAGEABLE_HOST = 1,
+  QL_ERR_ARG = -1,         /* null pointer, bad enum, bad flag */
+  QL_ERR_SHAPE = -2,       /* K % 64, N % 16, negative sizes, mismatched shapes */
+  QL_ERR_ALIGN = -3,       /* pointer not aligned as the call requires */
+  QL_ERR_RANK = -4,        /* LoRA rank outside 1..64 (the pages refuse r < 1) */
+  QL_ERR_NONFINITE = -5,   /* nf4_quantize met NaN or Inf */
+  QL_ERR_WORKSPACE = -6,   /* a workspace or buffer is smaller than required */
+  QL_ERR_HIP = -7,         /* a HIP runtime call failed */
+  QL_ERR_UNSUPPORTED = -8  /* a valid request this build does not implement */
+};
+
+enum { QL_BF16 = 0, QL_F32 = 1 };
+
+/* A hipStream_t passed as an opaque pointer; NULL means the null stream. */
+typedef void* ql_stream;
+
+/* Thread-local message for the last failing call on this thread ("" if none). */
+const char* ql_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int32_t ql_abi_version(void);
+
+/* The 16 float32 NF4 levels the library uses, copied to host memory `out`. */
+ql_status nf4_codebook(float* out /* host [16] */);
+
+/* ---------------------------------------------------------------- NF4 codec
+ * nf4_quantize: block-wise NF4 quantisation of w (float32, n elements,
+ * row-major flattened; n % 64 == 0). For each block of 64 consecutive
+ * elements: absmax = max |w|; each element's code is the index of the nearest
+ * NF4 level to fl32(w / absmax) (ties to the lower index); an all-zero block
+ * gets code 7 (the zero level) and absmax 0. Byte i of `packed` holds element
+ * 2i in its high nibble and element 2i+1 in its low nibble.
+ * Quantisation is offline, done once per tensor (docs "NF4 streaming": "the
+ * base is quantised once, offline, one tensor at a time").
+ *   packed: uint8 [n/2], absmax: float32 [n/64]; all 16-byte aligned.
+ * Non-finite input is refused with QL_ERR_NONFINITE. To detect it the call
+ * waits for the stream to finish the kernel (it is synchronous). On
+ * QL_ERR_NONFINITE the outputs hold unspecified values.
+ */
+ql_status nf4_quantize(const float* w, int64_t n, uint8_t* packed, float* absmax, ql_stream s);
+
+/* nf4_dequant: out[i] = fl32(level[code_i] * absmax[i / 64]); with
+ * out_dtype == QL_BF16 that float32 value rounded to nearest even bfloat16.
+ * This is the standalone form of the per-layer dequantisation the Soup README
+ * ("Citing Soup", v3 retraction) names as streaming's largest own cost; the
+ * GEMMs below fuse it instead. n % 64 == 0; pointers 16-byte aligned.
+ */
+ql_status nf4_dequant(const uint8_t* packed, const float* absmax, int64_t n,
+                      int32_t out_dtype, void* out, ql_stream s);
+
+/* ------------------------------------------------------- NF4 + LoRA linear */
+typedef struct {
+  const uint8_t* packed; /* uint8 [N*K/2] as written by nf4_quantize */
+  const float* absmax;   /* float32 [N*K/64] */
+  int64_t N, K;          /* out-features, in-features; K % 64 == 0, N % 16 == 0 */
+} ql_nf4_weight;
+
+typedef struct {
+  const void* A;  /* bf16 [r x K] */
+  const void* B;  /* bf16 [N x r] */
+  int32_t r;      /* 1..64 */
+  float alpha;    /* scale s = alpha / r */
+} ql_lora;
+
+/* Workspace sizes (bytes) of qlora_linear_fwd and qlora_linear_bwd for a shape. */
+ql_status qlora_linear_workspace(int64_t M, int64_t N, int64_t K, int32_t r,
+                                 size_t* fwd_bytes, size_t* bwd_bytes);
+
+/* qlora_linear_fwd: the frozen NF4 linear with its LoRA adapter,
+ *   U = bf16(x A^T)                    -> u_save, bf16 [M x r] (kept for the backward)
+ *   y = bf16(x W^T + s U B^T)          -> y, bf16 [M x N]
+ * with W = bf16(fl32(level * absmax)) dequantised inside the GEMM's tile
+ * loader (never materialised) and float32 accumulation. s B is rounded to
+ * bf16 as an MFMA operand (exact when s is a power of two).
+ * Forward of the LoRA linear on the pages (blog: "only the LoRA adapter
+ * actually trains"; docs "NF4 streaming": NF4 dequantised on the fly).
+ *   x: bf16 [M x K]; M >= 0 (M == 0 is a no-op); 16-byte aligned pointers.
+ *   ws: device workspace of at least fwd_bytes from qlora_linear_workspace.
+ */
+ql_status qlora_linear_fwd(const void* x, int64_t M, ql_nf4_weight W, ql_lora L,
+                           void* y, void* u_save, void* ws, size_t ws_bytes, ql_stream s);
+
+/* qlora_linear_bwd: gradients of the linear above for upstream dY (bf16 [M x N]):
+ *   G  = bf16(dY B)                    (internal, [M x r])
+ *   dX = bf16(dY W + s G A)            -> dx, bf16 [M x K]; skipped if dx == NULL
+ *   dB = s dY^T U                      -> dB, float32 [N x r]
+ *   dA = s G^T x                       -> dA, float32 [r x K]
+ * There is no gradient for the frozen W (blog: "only the LoRA adapter actually
+ * trains"). With accumulate != 0, dA and dB are added to their current values
+ * (float32), else overwritten. Reductions over M use a fixed order.
+ *   u_saved: the U written by qlora_linear_fwd for the same x.
+ *   ws: device workspace of at least bwd_bytes from qlora_linear_workspace.
+ */
+ql_status qlora_linear_bwd(const void* dy, const void* x, const void* u_saved, int64_t M,
+                           ql_nf4_weight W, ql_lora L, void* dx, float* dA, float* dB,
+                           int32_t accumulate, void* ws, size_t ws_bytes, ql_stream s);
+
+/* ----------------------------------------------------- layer-streamed stack
+ * A stack of n_layers decoder-layer stand-ins, each
+ *   n1 = RMSNorm(h); q,k,v = P_q,P_k,P_v(n1); a = repeat_kv(v);
+ *   h = h + P_o(a); n2 = RMSNorm(h); g,u = P_gate,P_up(n2);
+ *   h = h + P_down(silu(g) * u)
+ * with every P an NF4 + LoRA linear (shapes: q,o [H x H]; k,v [kv x H];
+ * gate,up [I x H]; down [H x I]). RMSNorm has unit gain; repeat_kv gives head
+ * j of `a` the kv head j / (H / kv_dim). q and k feed nothing in this
+ * attention-free stand-in: they are computed and saved, their gradients are 0.
+ *
+ * The frozen NF4 weights live in one "store" of n_layers records (layout from
+ * stream_layer_stack_layout). Streamed mode (resident == 0): the store is HOST
+ * memory, ideally page-locked; each layer's record is copied with one
+ * asynchronous host-to-device copy on the `copy` stream into one of two device
+ * slots, while the `compute` stream works on the other slot; events order the
+ * two (docs "Layer Streaming": "two pre-allocated VRAM buffers", "stream_buffers:
+ * 2  # double-buffering"). Peak device memory for weights is the two slots.
+ * Resident mode (resident == 1): the store is a DEVICE buffer, nothing is
+ * copied and the same kernels run in the same order on the same bytes, so the
+ * results are bit-identical to streamed mode (blog "Why the evidence is better
+ * than usual": streaming is a pure scheduling change).
+ * A pageable host store still works, but its copies cannot overlap compute;
+ * the call then returns QL_WARN_PAGEABLE_HOST (docs "Layer Streaming":
+ * pageable fallback with its cost reported).
+ */
+typedef struct {
+  int32_t n_layers, hidden, inter, kv_dim, head_dim, r;
+  float alpha, rms_eps;
+  int32_t n_buffers;  /* device slots; must be 2 */
+  int32_t resident;   /* 0: host store, streamed; 1: device store, no copies */
+} ql_stack_cfg;
+
+enum { QL_PROJ_Q = 0, QL_PROJ_K, QL_PROJ_V, QL_PROJ_O, QL_PROJ_GATE, QL_PROJ_UP, QL_PROJ_DOWN,
+       QL_NPROJ };
+
+/* Store layout. layer_offsets (host int64 [n_layers + 1]) gets each record's
+ * byte offset and the total; proj_offsets (host int64 [2 * QL_NPROJ], may be
+ * NULL) gets, within a record, the byte offset of projection p's packed codes
+ * at [2p] and of its absmax at [2p+1]. Every offset is a multiple of 256. */
+ql_status stream_layer_stack_layout(const ql_stack_cfg* cfg, int64_t* layer_offsets,
+                                    int64_t* proj_offsets, size_t* store_bytes);
+
+/* Buffer sizes for M tokens: slots (2 device layer buffers), saved activations
+ * (written by the forward, read by the backward), and workspace. */
+ql_status stream_layer_stack_workspace(const ql_stack_cfg* cfg, int64_t M, size_t* slots_bytes,
+                                       size_t* saved_bytes, size_t* ws_bytes);
+
+enum { QL_SAVED_H_IN = 0, QL_SAVED_N1, QL_SAVED_Q, QL_SAVED_K, QL_SAVED_V, QL_SAVED_H_MID,
+       QL_SAVED_N2, QL_SAVED_GATE, QL_SAVED_UP, QL_SAVED_ACT, QL_SAVED_U0 /* + QL_PROJ_* */,
+       QL_SAVED_COUNT = QL_SAVED_U0 + QL_NPROJ };
+
+/* Byte offsets (host int64 [QL_SAVED_COUNT]) of each saved tensor within one
+ * layer's part of `saved`, and that part's size; layer l starts at
+ * l * per_layer_bytes. All saved tensors are bf16, row-major with M rows. */
+ql_status stream_layer_stack_saved_layout(const ql_stack_cfg* cfg, int64_t M, int64_t* offsets,
+                                          size_t* per_layer_bytes);
+
+/* Forward over all layers: y (bf16 [M x H]) = stack(x0). lora is a HOST array
+ * of n_layers * QL_NPROJ adapters (device A, B; r and alpha must equal cfg's),
+ * indexed [layer * QL_NPROJ + proj]. */
+ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
+                                 const ql_lora* lora, const void* x0, int64_t M, void* y,
+                                 void* saved, size_t saved_bytes, void* slots, size_t slots_bytes,
+                                 void* ws, size_t ws_bytes, ql_stream compute, ql_stream copy);
+
+/* Backward over all layers, last to first, from dy (bf16 [M x H]) at the
+ * output: dx0 (bf16 [M x H], may be NULL) and dA / dB (HOST arrays of
+ * n_layers * QL_NPROJ device float32 pointers, [r x K] and [N x r]).
+ * reuse_fwd_slots != 0 skips the copies of the last two layers, which a
+ * stream_layer_stack_fwd call with the same cfg, store and slots left in the
+ * slots; it requires that nothing wrote the slots since and that the same
+ * compute stream is used (2L-2 copies per forward + backward instead of 2L). */
+ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
+                                 const ql_lora* lora, const void* dy, int64_t M,
+                                 const void* saved, size_t saved_bytes, void* dx0,
+                                 float* const* dA, float* const* dB, int32_t accumulate,
+                                 int32_t reuse_fwd_slots, void* slots, size_t slots_bytes,
+                                 void* ws, size_t ws_bytes, ql_stream compute, ql_stream copy);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4QLORA_H */

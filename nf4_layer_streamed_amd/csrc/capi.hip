@@ -1,0 +1,812 @@
+// C ABI: argument validation, the NF4 + LoRA linear, and the layer streamer.
+// Every entry point validates all arguments before it enqueues anything.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "ql_internal.h"
+
+namespace ql {
+
+static thread_local char g_err[512];
+
+ql_status set_error(ql_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+static void clear_error() { g_err[0] = 0; }
+
+static inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+static inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+#define QL_TRY(expr)                 \
+  do {                               \
+    ql_status rc_ = (expr);          \
+    if (rc_ != QL_OK) return rc_;    \
+  } while (0)
+
+// ------------------------------------------------------------ small helpers
+static ql_status check_ptr(const char* fn, const char* name, const void* p, size_t align) {
+  if (!p) return set_error(QL_ERR_ARG, "%s: %s is NULL", fn, name);
+  if (!aligned(p, align))
+    return set_error(QL_ERR_ALIGN, "%s: %s (%p) must be %zu-byte aligned", fn, name, p, align);
+  return QL_OK;
+}
+
+static ql_status check_weight(const char* fn, const ql_nf4_weight& W) {
+  if (W.N <= 0 || W.K <= 0) return set_error(QL_ERR_SHAPE, "%s: W.N (%lld) and W.K (%lld) must be > 0", fn,
+                                             (long long)W.N, (long long)W.K);
+  if (W.K % 64) return set_error(QL_ERR_SHAPE, "%s: W.K (%lld) must be a multiple of 64 (NF4 block)", fn,
+                                 (long long)W.K);
+  if (W.N % 16) return set_error(QL_ERR_SHAPE, "%s: W.N (%lld) must be a multiple of 16", fn, (long long)W.N);
+  QL_TRY(check_ptr(fn, "W.packed", W.packed, 16));
+  QL_TRY(check_ptr(fn, "W.absmax", W.absmax, 16));
+  return QL_OK;
+}
+
+static ql_status check_lora(const char* fn, const ql_lora& L) {
+  if (L.r < 1 || L.r > 64)
+    return set_error(QL_ERR_RANK, "%s: LoRA rank r (%d) must be in 1..64", fn, (int)L.r);
+  if (!(L.alpha == L.alpha) || L.alpha == __builtin_inff() || L.alpha == -__builtin_inff())
+    return set_error(QL_ERR_ARG, "%s: LoRA alpha must be finite", fn);
+  QL_TRY(check_ptr(fn, "L.A", L.A, 16));
+  QL_TRY(check_ptr(fn, "L.B", L.B, 16));
+  return QL_OK;
+}
+
+// per-device flag for nf4_quantize's non-finite check
+static std::mutex g_flag_mu;
+static int* g_flag[64] = {};
+
+static ql_status device_flag(int** out) {
+  int dev = 0;
+  QL_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return set_error(QL_ERR_UNSUPPORTED, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_flag_mu);
+  if (!g_flag[dev]) QL_HIP_CHECK(hipMalloc((void**)&g_flag[dev], 256));
+  *out = g_flag[dev];
+  return QL_OK;
+}
+
+// --------------------------------------------------------- linear helpers
+struct LinearWs {
+  size_t fwd, bwd;
+  size_t bt_off, g_off, scratch_off;
+};
+
+static LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
+  LinearWs w;
+  w.fwd = align256(skinny_ws_bytes(M, K, r, 1));
+  w.bt_off = 0;
+  w.g_off = align256((size_t)r * N * 2);
+  w.scratch_off = w.g_off + align256((size_t)M * r * 2);
+  size_t scratch = skinny_ws_bytes(M, N, r, 1);
+  size_t c1 = colred_ws_bytes(M, N, r), c2 = colred_ws_bytes(M, K, r);
+  if (c1 > scratch) scratch = c1;
+  if (c2 > scratch) scratch = c2;
+  w.bwd = w.scratch_off + align256(scratch);
+  return w;
+}
+
+// ---------------------------------------------------------- stack layout
+struct StackLayout {
+  int64_t N[QL_NPROJ], K[QL_NPROJ];
+  int64_t packed_off[QL_NPROJ], absmax_off[QL_NPROJ];
+  int64_t rec;  // bytes per layer record (multiple of 256)
+};
+
+static ql_status check_cfg(const char* fn, const ql_stack_cfg* c) {
+  if (!c) return set_error(QL_ERR_ARG, "%s: cfg is NULL", fn);
+  if (c->n_layers < 1) return set_error(QL_ERR_SHAPE, "%s: n_layers (%d) must be >= 1", fn, c->n_layers);
+  if (c->hidden < 64 || c->hidden % 64)
+    return set_error(QL_ERR_SHAPE, "%s: hidden (%d) must be a positive multiple of 64", fn, c->hidden);
+  if (c->inter < 64 || c->inter % 64)
+    return set_error(QL_ERR_SHAPE, "%s: inter (%d) must be a positive multiple of 64", fn, c->inter);
+  if (c->head_dim < 64 || c->head_dim % 64)
+    return set_error(QL_ERR_SHAPE, "%s: head_dim (%d) must be a positive multiple of 64", fn, c->head_dim);
+  if (c->kv_dim < c->head_dim || c->kv_dim % c->head_dim || c->hidden % c->kv_dim)
+    return set_error(QL_ERR_SHAPE,
+                     "%s: kv_dim (%d) must be a multiple of head_dim (%d) that divides hidden (%d)", fn,
+                     c->kv_dim, c->head_dim, c->hidden);
+  if (c->r < 1 || c->r > 64) return set_error(QL_ERR_RANK, "%s: r (%d) must be in 1..64", fn, c->r);
+  if (c->n_buffers != 2)
+    return set_error(QL_ERR_UNSUPPORTED, "%s: n_buffers (%d) must be 2 (double buffering)", fn, c->n_buffers);
+  if (c->resident != 0 && c->resident != 1)
+    return set_error(QL_ERR_ARG, "%s: resident (%d) must be 0 or 1", fn, c->resident);
+  if (!(c->rms_eps > 0.f) || !(c->alpha == c->alpha))
+    return set_error(QL_ERR_ARG, "%s: rms_eps must be > 0 and alpha finite", fn);
+  return QL_OK;
+}
+
+static StackLayout stack_layout(const ql_stack_cfg* c) {
+  StackLayout s;
+  const int64_t H = c->hidden, I = c->inter, KV = c->kv_dim;
+  const int64_t n[QL_NPROJ] = {H, KV, KV, H, I, I, H};
+  const int64_t k[QL_NPROJ] = {H, H, H, H, H, H, I};
+  size_t off = 0;
+  for (int p = 0; p < QL_NPROJ; ++p) {
+    s.N[p] = n[p];
+    s.K[p] = k[p];
+    s.packed_off[p] = (int64_t)off;
+    off += align256((size_t)(n[p] * k[p] / 2));
+  }
+  for (int p = 0; p < QL_NPROJ; ++p) {
+    s.absmax_off[p] = (int64_t)off;
+    off += align256((size_t)(n[p] * (k[p] / 64) * 4));
+  }
+  s.rec = (int64_t)align256(off);
+  return s;
+}
+
+struct SavedLayout {
+  int64_t off[QL_SAVED_COUNT];
+  size_t per_layer;
+};
+
+static SavedLayout saved_layout(const ql_stack_cfg* c, int64_t M) {
+  SavedLayout s;
+  const int64_t H = c->hidden, I = c->inter, KV = c->kv_dim, r = c->r;
+  const int64_t cols[QL_SAVED_COUNT] = {H, H, H, KV, KV, H, H, I, I, I, r, r, r, r, r, r, r};
+  size_t off = 0;
+  for (int i = 0; i < QL_SAVED_COUNT; ++i) {
+    s.off[i] = (int64_t)off;
+    off += align256((size_t)(M * cols[i] * 2));
+  }
+  s.per_layer = off;
+  return s;
+}
+
+// internal temporaries of the stack (offsets into ws)
+struct StackWs {
+  size_t dhA, dhB, dhmid, dact, dg, du, dn, da32, dv, bt, G[5], scratch, total;
+};
+
+static StackWs stack_ws(const ql_stack_cfg* c, int64_t M) {
+  const int64_t H = c->hidden, I = c->inter, KV = c->kv_dim, r = c->r;
+  StackWs w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  w.dhA = take(M * H * 2);
+  w.dhB = take(M * H * 2);
+  w.dhmid = take(M * H * 2);
+  w.dact = take(M * I * 2);
+  w.dg = take(M * I * 2);
+  w.du = take(M * I * 2);
+  w.dn = take(M * H * 2);
+  w.da32 = take(M * H * 4);
+  w.dv = take(M * KV * 2);
+  const int64_t maxN = H > I ? H : I;
+  w.bt = take((size_t)r * maxN * 2);
+  for (int i = 0; i < 5; ++i) w.G[i] = take((size_t)M * r * 2);
+  size_t sc = 0;
+  auto mx = [&](size_t v) { if (v > sc) sc = v; };
+  mx(skinny_ws_bytes(M, H, r, 3));
+  mx(skinny_ws_bytes(M, I, r, 1));
+  mx(colred_ws_bytes(M, H, r));
+  mx(colred_ws_bytes(M, I, r));
+  mx(colred_ws_bytes(M, KV, r));
+  w.scratch = take(sc);
+  w.total = off;
+  return w;
+}
+
+// -------------------------------------------------------------- one layer
+struct LayerW {
+  const uint8_t* packed[QL_NPROJ];
+  const float* absmax[QL_NPROJ];
+};
+
+static LayerW layer_weights(const StackLayout& L, const uint8_t* base) {
+  LayerW w;
+  for (int p = 0; p < QL_NPROJ; ++p) {
+    w.packed[p] = base + L.packed_off[p];
+    w.absmax[p] = (const float*)(base + L.absmax_off[p]);
+  }
+  return w;
+}
+
+static inline const uint16_t* u16(const void* p) { return (const uint16_t*)p; }
+static inline uint16_t* u16w(void* p) { return (uint16_t*)p; }
+
+static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const LayerW& W,
+                           const ql_lora* lo, int64_t M, const SavedLayout& SV, uint8_t* sv,
+                           uint16_t* h_out, uint8_t* ws, const StackWs& WS, hipStream_t st) {
+  const int64_t H = c->hidden, I = c->inter, KV = c->kv_dim;
+  const int r = c->r;
+  const float s = c->alpha / (float)r;
+  auto S = [&](int i) { return (uint16_t*)(sv + SV.off[i]); };
+  void* scratch = ws + WS.scratch;
+  const uint16_t* h_in = S(QL_SAVED_H_IN);
+
+  QL_TRY(launch_rmsnorm_fwd(h_in, M, H, c->rms_eps, S(QL_SAVED_N1), st));
+  {  // LoRA down of q, k, v (they share n1)
+    SkinnyArgs a{};
+    a.X = S(QL_SAVED_N1); a.M = M; a.K = H; a.ldx = H; a.r = r; a.nseg = 3;
+    for (int p = 0; p < 3; ++p) { a.Bt[p] = u16(lo[p].A); a.out[p] = S(QL_SAVED_U0 + p); }
+    QL_TRY(launch_skinny(a, scratch, st));
+  }
+  {  // q | k | v in one launch
+    FwdArgs a{};
+    a.X = S(QL_SAVED_N1); a.M = M; a.K = H; a.ldx = H; a.r = r; a.s = s; a.nseg = 3;
+    const int outs[3] = {QL_SAVED_Q, QL_SAVED_K, QL_SAVED_V};
+    for (int p = 0; p < 3; ++p) {
+      FwdSeg& g = a.seg[p];
+      g.packed = W.packed[p]; g.absmax = W.absmax[p]; g.U = S(QL_SAVED_U0 + p); g.B = u16(lo[p].B);
+      g.out = S(outs[p]); g.N = SL.N[p]; g.ldo = SL.N[p]; g.col0 = 0; g.resid = nullptr;
+    }
+    QL_TRY(launch_gemm_fwd(a, st));
+  }
+  const int n_rep = (int)(H / KV);
+  {  // o: input a = repeat_kv(v) read through the column remap; residual h_in
+    SkinnyArgs u{};
+    u.X = S(QL_SAVED_V); u.M = M; u.K = H; u.ldx = KV; u.head_dim = c->head_dim; u.n_rep = n_rep;
+    u.r = r; u.nseg = 1; u.Bt[0] = u16(lo[QL_PROJ_O].A); u.out[0] = S(QL_SAVED_U0 + QL_PROJ_O);
+    QL_TRY(launch_skinny(u, scratch, st));
+    FwdArgs a{};
+    a.X = S(QL_SAVED_V); a.M = M; a.K = H; a.ldx = KV; a.head_dim = c->head_dim; a.n_rep = n_rep;
+    a.r = r; a.s = s; a.nseg = 1;
+    FwdSeg& g = a.seg[0];
+    g.packed = W.packed[QL_PROJ_O]; g.absmax = W.absmax[QL_PROJ_O]; g.U = S(QL_SAVED_U0 + QL_PROJ_O);
+    g.B = u16(lo[QL_PROJ_O].B); g.out = S(QL_SAVED_H_MID); g.N = H; g.ldo = H; g.resid = h_in;
+    QL_TRY(launch_gemm_fwd(a, st));
+  }
+  QL_TRY(launch_rmsnorm_fwd(S(QL_SAVED_H_MID), M, H, c->rms_eps, S(QL_SAVED_N2), st));
+  {  // gate | up
+    SkinnyArgs u{};
+    u.X = S(QL_SAVED_N2); u.M = M; u.K = H; u.ldx = H; u.r = r; u.nseg = 2;
+    u.Bt[0] = u16(lo[QL_PROJ_GATE].A); u.out[0] = S(QL_SAVED_U0 + QL_PROJ_GATE);
+    u.Bt[1] = u16(lo[QL_PROJ_UP].A); u.out[1] = S(QL_SAVED_U0 + QL_PROJ_UP);
+    QL_TRY(launch_skinny(u, scratch, st));
+    FwdArgs a{};
+    a.X = S(QL_SAVED_N2); a.M = M; a.K = H; a.ldx = H; a.r = r; a.s = s; a.nseg = 2;
+    const int outs[2] = {QL_SAVED_GATE, QL_SAVED_UP};
+    for (int q = 0; q < 2; ++q) {
+      const int p = QL_PROJ_GATE + q;
+      FwdSeg& g = a.seg[q];
+      g.packed = W.packed[p]; g.absmax = W.absmax[p]; g.U = S(QL_SAVED_U0 + p); g.B = u16(lo[p].B);
+      g.out = S(outs[q]); g.N = I; g.ldo = I; g.resid = nullptr;
+    }
+    QL_TRY(launch_gemm_fwd(a, st));
+  }
+  QL_TRY(launch_swiglu_fwd(S(QL_SAVED_GATE), S(QL_SAVED_UP), M * I, S(QL_SAVED_ACT), st));
+  {  // down, residual h_mid
+    SkinnyArgs u{};
+    u.X = S(QL_SAVED_ACT); u.M = M; u.K = I; u.ldx = I; u.r = r; u.nseg = 1;
+    u.Bt[0] = u16(lo[QL_PROJ_DOWN].A); u.out[0] = S(QL_SAVED_U0 + QL_PROJ_DOWN);
+    QL_TRY(launch_skinny(u, scratch, st));
+    FwdArgs a{};
+    a.X = S(QL_SAVED_ACT); a.M = M; a.K = I; a.ldx = I; a.r = r; a.s = s; a.nseg = 1;
+    FwdSeg& g = a.seg[0];
+    g.packed = W.packed[QL_PROJ_DOWN]; g.absmax = W.absmax[QL_PROJ_DOWN];
+    g.U = S(QL_SAVED_U0 + QL_PROJ_DOWN); g.B = u16(lo[QL_PROJ_DOWN].B);
+    g.out = h_out; g.N = H; g.ldo = H; g.resid = S(QL_SAVED_H_MID);
+    QL_TRY(launch_gemm_fwd(a, st));
+  }
+  return QL_OK;
+}
+
+// G = bf16(dY B) for one projection (B [N x r] transposed into ws first)
+static ql_status lora_g(const uint16_t* dy, int64_t M, int64_t N, const ql_lora& lo, int r,
+                        uint16_t* bt, uint16_t* G, void* scratch, hipStream_t st) {
+  QL_TRY(launch_transpose_bf16(u16(lo.B), N, r, bt, st));
+  SkinnyArgs a{};
+  a.X = dy; a.M = M; a.K = N; a.ldx = N; a.r = r; a.nseg = 1; a.Bt[0] = bt; a.out[0] = G;
+  return launch_skinny(a, scratch, st);
+}
+
+// dB = s dY^T U (transposed store into [N x r]) and dA = s G^T X
+static ql_status lora_grads(const uint16_t* dy, int64_t N, const uint16_t* U, const uint16_t* X,
+                            int64_t ldx, int head_dim, int n_rep, int64_t K, const uint16_t* G,
+                            int64_t M, int r, float s, float* dA, float* dB, int accumulate,
+                            void* scratch, hipStream_t st) {
+  ColRedArgs b{};
+  b.Z = dy; b.M = M; b.C = N; b.ldz = N; b.V = U; b.r = r; b.s = s; b.out = dB;
+  b.transpose_out = 1; b.accumulate = accumulate;
+  QL_TRY(launch_colred(b, scratch, st));
+  ColRedArgs a{};
+  a.Z = X; a.M = M; a.C = K; a.ldz = ldx; a.head_dim = head_dim; a.n_rep = n_rep; a.V = G; a.r = r;
+  a.s = s; a.out = dA; a.transpose_out = 0; a.accumulate = accumulate;
+  return launch_colred(a, scratch, st);
+}
+
+static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const LayerW& W,
+                           const ql_lora* lo, int64_t M, const SavedLayout& SV, const uint8_t* sv,
+                           const uint16_t* dh, uint16_t* dh_out, float* const* dA, float* const* dB,
+                           int accumulate, uint8_t* ws, const StackWs& WS, hipStream_t st) {
+  const int64_t H = c->hidden, I = c->inter, KV = c->kv_dim;
+  const int r = c->r;
+  const float s = c->alpha / (float)r;
+  auto S = [&](int i) { return (const uint16_t*)(sv + SV.off[i]); };
+  auto T = [&](size_t off) { return (uint16_t*)(ws + off); };
+  void* scratch = ws + WS.scratch;
+  uint16_t* bt = T(WS.bt);
+  const int n_rep = (int)(H / KV);
+
+  // down: dact = dh W_d + s G_d A_d
+  uint16_t* Gd = T(WS.G[0]);
+  QL_TRY(lora_g(dh, M, H, lo[QL_PROJ_DOWN], r, bt, Gd, scratch, st));
+  {
+    BwdArgs a{};
+    a.M = M; a.K = I; a.r = r; a.s = s; a.out = T(WS.dact); a.nseg = 1;
+    a.seg[0] = BwdSeg{dh, W.packed[QL_PROJ_DOWN], W.absmax[QL_PROJ_DOWN], Gd, u16(lo[QL_PROJ_DOWN].A), H};
+    QL_TRY(launch_gemm_bwd(a, st));
+  }
+  QL_TRY(lora_grads(dh, H, S(QL_SAVED_U0 + QL_PROJ_DOWN), S(QL_SAVED_ACT), I, 0, 0, I, Gd, M, r, s,
+                    dA[QL_PROJ_DOWN], dB[QL_PROJ_DOWN], accumulate, scratch, st));
+  // SwiGLU
+  QL_TRY(launch_swiglu_bwd(S(QL_SAVED_GATE), S(QL_SAVED_UP), T(WS.dact), M * I, T(WS.dg), T(WS.du), st));
+  // gate + up: dn2 = dg W_g + s G_g A_g + du W_u + s G_u A_u
+  uint16_t* Gg = T(WS.G[1]);
+  uint16_t* Gu = T(WS.G[2]);
+  QL_TRY(lora_g(T(WS.dg), M, I, lo[QL_PROJ_GATE], r, bt, Gg, scratch, st));
+  QL_TRY(lora_g(T(WS.du), M, I, lo[QL_PROJ_UP], r, bt, Gu, scratch, st));
+  {
+    BwdArgs a{};
+    a.M = M; a.K = H; a.r = r; a.s = s; a.out = T(WS.dn); a.nseg = 2;
+    a.seg[0] = BwdSeg{T(WS.dg), W.packed[QL_PROJ_GATE], W.absmax[QL_PROJ_GATE], Gg, u16(lo[QL_PROJ_GATE].A), I};
+    a.seg[1] = BwdSeg{T(WS.du), W.packed[QL_PROJ_UP], W.absmax[QL_PROJ_UP], Gu, u16(lo[QL_PROJ_UP].A), I};
+    QL_TRY(launch_gemm_bwd(a, st));
+  }
+  QL_TRY(lora_grads(T(WS.dg), I, S(QL_SAVED_U0 + QL_PROJ_GATE), S(QL_SAVED_N2), H, 0, 0, H, Gg, M, r, s,
+                    dA[QL_PROJ_GATE], dB[QL_PROJ_GATE], accumulate, scratch, st));
+  QL_TRY(lora_grads(T(WS.du), I, S(QL_SAVED_U0 + QL_PROJ_UP), S(QL_SAVED_N2), H, 0, 0, H, Gu, M, r, s,
+                    dA[QL_PROJ_UP], dB[QL_PROJ_UP], accumulate, scratch, st));
+  // RMSNorm 2 + residual
+  QL_TRY(launch_rmsnorm_bwd(S(QL_SAVED_H_MID), T(WS.dn), dh, M, H, c->rms_eps, T(WS.dhmid), st));
+  const uint16_t* dhm = T(WS.dhmid);
+  // o: da = dh_mid W_o + s G_o A_o (float32), dv = head-group sum
+  uint16_t* Go = T(WS.G[3]);
+  QL_TRY(lora_g(dhm, M, H, lo[QL_PROJ_O], r, bt, Go, scratch, st));
+  {
+    BwdArgs a{};
+    a.M = M; a.K = H; a.r = r; a.s = s; a.out = ws + WS.da32; a.out_f32 = 1; a.nseg = 1;
+    a.seg[0] = BwdSeg{dhm, W.packed[QL_PROJ_O], W.absmax[QL_PROJ_O], Go, u16(lo[QL_PROJ_O].A), H};
+    QL_TRY(launch_gemm_bwd(a, st));
+  }
+  QL_TRY(lora_grads(dhm, H, S(QL_SAVED_U0 + QL_PROJ_O), S(QL_SAVED_V), KV, c->head_dim, n_rep, H, Go, M,
+                    r, s, dA[QL_PROJ_O], dB[QL_PROJ_O], accumulate, scratch, st));
+  QL_TRY(launch_repeat_kv_bwd((const float*)(ws + WS.da32), M, H, KV, c->head_dim, T(WS.dv), st));
+  // v: dn1 = dv W_v + s G_v A_v
+  uint16_t* Gv = T(WS.G[4]);
+  QL_TRY(lora_g(T(WS.dv), M, KV, lo[QL_PROJ_V], r, bt, Gv, scratch, st));
+  {
+    BwdArgs a{};
+    a.M = M; a.K = H; a.r = r; a.s = s; a.out = T(WS.dn); a.nseg = 1;
+    a.seg[0] = BwdSeg{T(WS.dv), W.packed[QL_PROJ_V], W.absmax[QL_PROJ_V], Gv, u16(lo[QL_PROJ_V].A), KV};
+    QL_TRY(launch_gemm_bwd(a, st));
+  }
+  QL_TRY(lora_grads(T(WS.dv), KV, S(QL_SAVED_U0 + QL_PROJ_V), S(QL_SAVED_N1), H, 0, 0, H, Gv, M, r, s,
+                    dA[QL_PROJ_V], dB[QL_PROJ_V], accumulate, scratch, st));
+  // q, k feed nothing: their adapter gradients are exactly zero
+  if (!accumulate) {
+    for (int p = 0; p < 2; ++p) {
+      QL_TRY(launch_zero_f32(dA[p], (int64_t)r * H, st));
+      QL_TRY(launch_zero_f32(dB[p], SL.N[p] * r, st));
+    }
+  }
+  // RMSNorm 1 + residual
+  QL_TRY(launch_rmsnorm_bwd(S(QL_SAVED_H_IN), T(WS.dn), dhm, M, H, c->rms_eps, dh_out, st));
+  return QL_OK;
+}
+
+// ------------------------------------------------------------- the streamer
+enum PtrKind { PK_DEVICE, PK_PINNED, PK_PAGEABLE };
+
+static PtrKind pointer_kind(const void* p) {
+  hipPointerAttribute_t at;
+  memset(&at, 0, sizeof(at));
+  hipError_t e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return PK_PAGEABLE;
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) return PK_DEVICE;
+  if (at.type == hipMemoryTypeHost) return PK_PINNED;
+  return PK_PAGEABLE;
+}
+
+struct Events {
+  hipEvent_t ready[2] = {nullptr, nullptr}, free_[2] = {nullptr, nullptr};
+  ~Events() {
+    for (int i = 0; i < 2; ++i) {
+      if (ready[i]) (void)hipEventDestroy(ready[i]);
+      if (free_[i]) (void)hipEventDestroy(free_[i]);
+    }
+  }
+  ql_status create() {
+    for (int i = 0; i < 2; ++i) {
+      QL_HIP_CHECK(hipEventCreateWithFlags(&ready[i], hipEventDisableTiming));
+      QL_HIP_CHECK(hipEventCreateWithFlags(&free_[i], hipEventDisableTiming));
+    }
+    return QL_OK;
+  }
+};
+
+struct StackCall {
+  StackLayout SL;
+  SavedLayout SV;
+  StackWs WS;
+  size_t store_need, slots_need, saved_need;
+  bool pageable = false;
+};
+
+static ql_status validate_stack(const char* fn, const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
+                                const ql_lora* lora, int64_t M, const void* saved, size_t saved_bytes,
+                                const void* slots, size_t slots_bytes, const void* ws, size_t ws_bytes,
+                                StackCall& sc) {
+  QL_TRY(check_cfg(fn, cfg));
+  if (M < 0) return set_error(QL_ERR_SHAPE, "%s: M (%lld) must be >= 0", fn, (long long)M);
+  sc.SL = stack_layout(cfg);
+  sc.SV = saved_layout(cfg, M);
+  sc.WS = stack_ws(cfg, M);
+  sc.store_need = (size_t)sc.SL.rec * cfg->n_layers;
+  sc.slots_need = cfg->resident ? 0 : (size_t)sc.SL.rec * 2;
+  sc.saved_need = sc.SV.per_layer * cfg->n_layers;
+  if (!store) return set_error(QL_ERR_ARG, "%s: store is NULL", fn);
+  if (!aligned(store, 256)) return set_error(QL_ERR_ALIGN, "%s: store must be 256-byte aligned", fn);
+  if (store_bytes < sc.store_need)
+    return set_error(QL_ERR_WORKSPACE, "%s: store_bytes (%zu) < layout size (%zu)", fn, store_bytes,
+                     sc.store_need);
+  const PtrKind pk = pointer_kind(store);
+  if (cfg->resident) {
+    if (pk != PK_DEVICE) return set_error(QL_ERR_ARG, "%s: resident mode needs a device store", fn);
+  } else {
+    if (pk == PK_DEVICE) return set_error(QL_ERR_ARG, "%s: streamed mode needs a host store", fn);
+    sc.pageable = pk == PK_PAGEABLE;
+    if (!slots) return set_error(QL_ERR_ARG, "%s: slots is NULL", fn);
+    if (!aligned(slots, 256)) return set_error(QL_ERR_ALIGN, "%s: slots must be 256-byte aligned", fn);
+    if (slots_bytes < sc.slots_need)
+      return set_error(QL_ERR_WORKSPACE, "%s: slots_bytes (%zu) < 2 layer records (%zu)", fn, slots_bytes,
+                       sc.slots_need);
+  }
+  if (M > 0) {
+    if (!saved) return set_error(QL_ERR_ARG, "%s: saved is NULL", fn);
+    if (!aligned(saved, 256)) return set_error(QL_ERR_ALIGN, "%s: saved must be 256-byte aligned", fn);
+    if (saved_bytes < sc.saved_need)
+      return set_error(QL_ERR_WORKSPACE, "%s: saved_bytes (%zu) < required (%zu)", fn, saved_bytes,
+                       sc.saved_need);
+    if (!ws) return set_error(QL_ERR_ARG, "%s: ws is NULL", fn);
+    if (!aligned(ws, 256)) return set_error(QL_ERR_ALIGN, "%s: ws must be 256-byte aligned", fn);
+    if (ws_bytes < sc.WS.total)
+      return set_error(QL_ERR_WORKSPACE, "%s: ws_bytes (%zu) < required (%zu)", fn, ws_bytes, sc.WS.total);
+  }
+  if (!lora) return set_error(QL_ERR_ARG, "%s: lora is NULL", fn);
+  for (int l = 0; l < cfg->n_layers; ++l)
+    for (int p = 0; p < QL_NPROJ; ++p) {
+      const ql_lora& L = lora[l * QL_NPROJ + p];
+      if (L.r != cfg->r || L.alpha != cfg->alpha)
+        return set_error(QL_ERR_RANK, "%s: lora[%d] r/alpha (%d, %g) differ from cfg (%d, %g)", fn,
+                         l * QL_NPROJ + p, L.r, (double)L.alpha, cfg->r, (double)cfg->alpha);
+      if (!L.A || !L.B) return set_error(QL_ERR_ARG, "%s: lora[%d] has a NULL factor", fn, l * QL_NPROJ + p);
+      if (!aligned(L.A, 16) || !aligned(L.B, 16))
+        return set_error(QL_ERR_ALIGN, "%s: lora[%d] factors must be 16-byte aligned", fn, l * QL_NPROJ + p);
+    }
+  return QL_OK;
+}
+
+}  // namespace ql
+
+using namespace ql;
+
+extern "C" {
+
+const char* ql_last_error(void) { return g_err; }
+
+int32_t ql_abi_version(void) { return 100; }
+
+ql_status nf4_codebook(float* out) {
+  clear_error();
+  if (!out) return set_error(QL_ERR_ARG, "nf4_codebook: out is NULL");
+  memcpy(out, kNF4LevelBitsHost, sizeof(kNF4LevelBitsHost));
+  return QL_OK;
+}
+
+ql_status nf4_quantize(const float* w, int64_t n, uint8_t* packed, float* absmax, ql_stream s) {
+  clear_error();
+  const char* fn = "nf4_quantize";
+  if (n < 0 || n % 64) return set_error(QL_ERR_SHAPE, "%s: n (%lld) must be a non-negative multiple of 64", fn,
+                                        (long long)n);
+  if (n == 0) return QL_OK;
+  QL_TRY(check_ptr(fn, "w", w, 16));
+  QL_TRY(check_ptr(fn, "packed", packed, 16));
+  QL_TRY(check_ptr(fn, "absmax", absmax, 16));
+  hipStream_t st = (hipStream_t)s;
+  int* flag = nullptr;
+  QL_TRY(device_flag(&flag));
+  QL_TRY(launch_clear_i32(flag, 1, st));
+  QL_TRY(launch_nf4_quantize(w, n, packed, absmax, flag, st));
+  int host_flag = 0;
+  QL_HIP_CHECK(hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, st));
+  QL_HIP_CHECK(hipStreamSynchronize(st));
+  if (host_flag) return set_error(QL_ERR_NONFINITE, "%s: w holds NaN or Inf", fn);
+  return QL_OK;
+}
+
+ql_status nf4_dequant(const uint8_t* packed, const float* absmax, int64_t n, int32_t out_dtype, void* out,
+                      ql_stream s) {
+  clear_error();
+  const char* fn = "nf4_dequant";
+  if (n < 0 || n % 64) return set_error(QL_ERR_SHAPE, "%s: n (%lld) must be a non-negative multiple of 64", fn,
+                                        (long long)n);
+  if (out_dtype != QL_BF16 && out_dtype != QL_F32)
+    return set_error(QL_ERR_ARG, "%s: out_dtype (%d) must be QL_BF16 or QL_F32", fn, out_dtype);
+  if (n == 0) return QL_OK;
+  QL_TRY(check_ptr(fn, "packed", packed, 16));
+  QL_TRY(check_ptr(fn, "absmax", absmax, 16));
+  QL_TRY(check_ptr(fn, "out", out, 16));
+  return launch_nf4_dequant(packed, absmax, n, out_dtype == QL_F32, out, (hipStream_t)s);
+}
+
+ql_status qlora_linear_workspace(int64_t M, int64_t N, int64_t K, int32_t r, size_t* fwd_bytes,
+                                 size_t* bwd_bytes) {
+  clear_error();
+  if (M < 0 || N <= 0 || K <= 0 || K % 64 || N % 16)
+    return set_error(QL_ERR_SHAPE, "qlora_linear_workspace: need M >= 0, N % 16 == 0, K % 64 == 0");
+  if (r < 1 || r > 64) return set_error(QL_ERR_RANK, "qlora_linear_workspace: r (%d) must be in 1..64", r);
+  LinearWs w = linear_ws(M, N, K, r);
+  if (fwd_bytes) *fwd_bytes = w.fwd;
+  if (bwd_bytes) *bwd_bytes = w.bwd;
+  return QL_OK;
+}
+
+ql_status qlora_linear_fwd(const void* x, int64_t M, ql_nf4_weight W, ql_lora L, void* y, void* u_save,
+                           void* ws, size_t ws_bytes, ql_stream s) {
+  clear_error();
+  const char* fn = "qlora_linear_fwd";
+  if (M < 0) return set_error(QL_ERR_SHAPE, "%s: M (%lld) must be >= 0", fn, (long long)M);
+  QL_TRY(check_weight(fn, W));
+  QL_TRY(check_lora(fn, L));
+  if (M == 0) return QL_OK;
+  QL_TRY(check_ptr(fn, "x", x, 16));
+  QL_TRY(check_ptr(fn, "y", y, 16));
+  QL_TRY(check_ptr(fn, "u_save", u_save, 16));
+  LinearWs lw = linear_ws(M, W.N, W.K, L.r);
+  if (ws_bytes < lw.fwd) return set_error(QL_ERR_WORKSPACE, "%s: ws_bytes (%zu) < %zu", fn, ws_bytes, lw.fwd);
+  if (lw.fwd) QL_TRY(check_ptr(fn, "ws", ws, 16));
+  hipStream_t st = (hipStream_t)s;
+  SkinnyArgs u{};
+  u.X = u16(x); u.M = M; u.K = W.K; u.ldx = W.K; u.r = L.r; u.nseg = 1; u.Bt[0] = u16(L.A);
+  u.out[0] = u16w(u_save);
+  QL_TRY(launch_skinny(u, ws, st));
+  FwdArgs a{};
+  a.X = u16(x); a.M = M; a.K = W.K; a.ldx = W.K; a.r = L.r; a.s = L.alpha / (float)L.r; a.nseg = 1;
+  FwdSeg& g = a.seg[0];
+  g.packed = W.packed; g.absmax = W.absmax; g.U = u16(u_save); g.B = u16(L.B); g.out = y; g.N = W.N;
+  g.ldo = W.N; g.col0 = 0; g.resid = nullptr;
+  return launch_gemm_fwd(a, st);
+}
+
+ql_status qlora_linear_bwd(const void* dy, const void* x, const void* u_saved, int64_t M, ql_nf4_weight W,
+                           ql_lora L, void* dx, float* dA, float* dB, int32_t accumulate, void* ws,
+                           size_t ws_bytes, ql_stream s) {
+  clear_error();
+  const char* fn = "qlora_linear_bwd";
+  if (M < 0) return set_error(QL_ERR_SHAPE, "%s: M (%lld) must be >= 0", fn, (long long)M);
+  if (accumulate != 0 && accumulate != 1) return set_error(QL_ERR_ARG, "%s: accumulate must be 0 or 1", fn);
+  QL_TRY(check_weight(fn, W));
+  QL_TRY(check_lora(fn, L));
+  QL_TRY(check_ptr(fn, "dA", dA, 16));
+  QL_TRY(check_ptr(fn, "dB", dB, 16));
+  if (M > 0) {
+    QL_TRY(check_ptr(fn, "dy", dy, 16));
+    QL_TRY(check_ptr(fn, "x", x, 16));
+    QL_TRY(check_ptr(fn, "u_saved", u_saved, 16));
+    if (dx) QL_TRY(check_ptr(fn, "dx", dx, 16));
+  }
+  LinearWs lw = linear_ws(M, W.N, W.K, L.r);
+  if (M > 0) {
+    if (ws_bytes < lw.bwd) return set_error(QL_ERR_WORKSPACE, "%s: ws_bytes (%zu) < %zu", fn, ws_bytes, lw.bwd);
+    QL_TRY(check_ptr(fn, "ws", ws, 256));
+  }
+  hipStream_t st = (hipStream_t)s;
+  const float sc = L.alpha / (float)L.r;
+  if (M == 0) {
+    if (!accumulate) {
+      QL_TRY(launch_zero_f32(dA, (int64_t)L.r * W.K, st));
+      QL_TRY(launch_zero_f32(dB, W.N * L.r, st));
+    }
+    return QL_OK;
+  }
+  uint8_t* w8 = (uint8_t*)ws;
+  uint16_t* bt = (uint16_t*)(w8 + lw.bt_off);
+  uint16_t* G = (uint16_t*)(w8 + lw.g_off);
+  void* scratch = w8 + lw.scratch_off;
+  QL_TRY(lora_g(u16(dy), M, W.N, L, L.r, bt, G, scratch, st));
+  if (dx) {
+    BwdArgs a{};
+    a.M = M; a.K = W.K; a.r = L.r; a.s = sc; a.out = dx; a.nseg = 1;
+    a.seg[0] = BwdSeg{u16(dy), W.packed, W.absmax, G, u16(L.A), W.N};
+    QL_TRY(launch_gemm_bwd(a, st));
+  }
+  return lora_grads(u16(dy), W.N, u16(u_saved), u16(x), W.K, 0, 0, W.K, G, M, L.r, sc, dA, dB, accumulate,
+                    scratch, st);
+}
+
+ql_status stream_layer_stack_layout(const ql_stack_cfg* cfg, int64_t* layer_offsets, int64_t* proj_offsets,
+                                    size_t* store_bytes) {
+  clear_error();
+  QL_TRY(check_cfg("stream_layer_stack_layout", cfg));
+  StackLayout SL = stack_layout(cfg);
+  if (layer_offsets)
+    for (int l = 0; l <= cfg->n_layers; ++l) layer_offsets[l] = SL.rec * l;
+  if (proj_offsets)
+    for (int p = 0; p < QL_NPROJ; ++p) {
+      proj_offsets[2 * p] = SL.packed_off[p];
+      proj_offsets[2 * p + 1] = SL.absmax_off[p];
+    }
+  if (store_bytes) *store_bytes = (size_t)SL.rec * cfg->n_layers;
+  return QL_OK;
+}
+
+ql_status stream_layer_stack_workspace(const ql_stack_cfg* cfg, int64_t M, size_t* slots_bytes,
+                                       size_t* saved_bytes, size_t* ws_bytes) {
+  clear_error();
+  QL_TRY(check_cfg("stream_layer_stack_workspace", cfg));
+  if (M < 0) return set_error(QL_ERR_SHAPE, "stream_layer_stack_workspace: M must be >= 0");
+  StackLayout SL = stack_layout(cfg);
+  if (slots_bytes) *slots_bytes = cfg->resident ? 0 : (size_t)SL.rec * 2;
+  if (saved_bytes) *saved_bytes = saved_layout(cfg, M).per_layer * cfg->n_layers;
+  if (ws_bytes) *ws_bytes = stack_ws(cfg, M).total;
+  return QL_OK;
+}
+
+ql_status stream_layer_stack_saved_layout(const ql_stack_cfg* cfg, int64_t M, int64_t* offsets,
+                                          size_t* per_layer_bytes) {
+  clear_error();
+  QL_TRY(check_cfg("stream_layer_stack_saved_layout", cfg));
+  if (M < 0) return set_error(QL_ERR_SHAPE, "stream_layer_stack_saved_layout: M must be >= 0");
+  SavedLayout SV = saved_layout(cfg, M);
+  if (offsets)
+    for (int i = 0; i < QL_SAVED_COUNT; ++i) offsets[i] = SV.off[i];
+  if (per_layer_bytes) *per_layer_bytes = SV.per_layer;
+  return QL_OK;
+}
+
+ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
+                                 const ql_lora* lora, const void* x0, int64_t M, void* y, void* saved,
+                                 size_t saved_bytes, void* slots, size_t slots_bytes, void* ws, size_t ws_bytes,
+                                 ql_stream compute, ql_stream copy) {
+  clear_error();
+  const char* fn = "stream_layer_stack_fwd";
+  StackCall sc;
+  QL_TRY(validate_stack(fn, cfg, store, store_bytes, lora, M, saved, saved_bytes, slots, slots_bytes, ws,
+                        ws_bytes, sc));
+  if (M > 0) {
+    QL_TRY(check_ptr(fn, "x0", x0, 16));
+    QL_TRY(check_ptr(fn, "y", y, 16));
+  }
+  if (M == 0) return sc.pageable ? QL_WARN_PAGEABLE_HOST : QL_OK;
+  hipStream_t C = (hipStream_t)compute, P = (hipStream_t)copy;
+  const int L = cfg->n_layers;
+  const int64_t H = cfg->hidden;
+  uint8_t* sv = (uint8_t*)saved;
+  uint8_t* w8 = (uint8_t*)ws;
+  const uint8_t* st8 = (const uint8_t*)store;
+  uint8_t* sl8 = (uint8_t*)slots;
+  const size_t rec = (size_t)sc.SL.rec;
+  // layer 0 input into the saved area (the backward reads it)
+  QL_HIP_CHECK(hipMemcpyAsync(sv + sc.SV.off[QL_SAVED_H_IN], x0, (size_t)M * H * 2, hipMemcpyDeviceToDevice, C));
+  Events ev;
+  if (!cfg->resident) {
+    QL_TRY(ev.create());
+    for (int l = 0; l < 2 && l < L; ++l) {
+      QL_HIP_CHECK(hipMemcpyAsync(sl8 + l * rec, st8 + l * rec, rec, hipMemcpyHostToDevice, P));
+      QL_HIP_CHECK(hipEventRecord(ev.ready[l], P));
+    }
+  }
+  for (int l = 0; l < L; ++l) {
+    const int slot = l & 1;
+    const uint8_t* base;
+    if (cfg->resident) {
+      base = st8 + l * rec;
+    } else {
+      QL_HIP_CHECK(hipStreamWaitEvent(C, ev.ready[slot], 0));
+      base = sl8 + slot * rec;
+    }
+    uint8_t* svl = sv + (size_t)l * sc.SV.per_layer;
+    uint16_t* h_out = (l + 1 < L) ? (uint16_t*)(sv + (size_t)(l + 1) * sc.SV.per_layer + sc.SV.off[QL_SAVED_H_IN])
+                                  : (uint16_t*)y;
+    QL_TRY(layer_fwd(cfg, sc.SL, layer_weights(sc.SL, base), lora + l * QL_NPROJ, M, sc.SV, svl, h_out, w8,
+                     sc.WS, C));
+    if (!cfg->resident && l + 2 < L) {
+      QL_HIP_CHECK(hipEventRecord(ev.free_[slot], C));
+      QL_HIP_CHECK(hipStreamWaitEvent(P, ev.free_[slot], 0));
+      QL_HIP_CHECK(hipMemcpyAsync(sl8 + slot * rec, st8 + (size_t)(l + 2) * rec, rec, hipMemcpyHostToDevice, P));
+      QL_HIP_CHECK(hipEventRecord(ev.ready[slot], P));
+    }
+  }
+  return sc.pageable ? QL_WARN_PAGEABLE_HOST : QL_OK;
+}
+
+ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
+                                 const ql_lora* lora, const void* dy, int64_t M, const void* saved,
+                                 size_t saved_bytes, void* dx0, float* const* dA, float* const* dB,
+                                 int32_t accumulate, int32_t reuse_fwd_slots, void* slots, size_t slots_bytes,
+                                 void* ws, size_t ws_bytes, ql_stream compute, ql_stream copy) {
+  clear_error();
+  const char* fn = "stream_layer_stack_bwd";
+  StackCall sc;
+  QL_TRY(validate_stack(fn, cfg, store, store_bytes, lora, M, saved, saved_bytes, slots, slots_bytes, ws,
+                        ws_bytes, sc));
+  if (accumulate != 0 && accumulate != 1) return set_error(QL_ERR_ARG, "%s: accumulate must be 0 or 1", fn);
+  if (reuse_fwd_slots != 0 && reuse_fwd_slots != 1)
+    return set_error(QL_ERR_ARG, "%s: reuse_fwd_slots must be 0 or 1", fn);
+  if (!dA || !dB) return set_error(QL_ERR_ARG, "%s: dA / dB arrays are NULL", fn);
+  const int L = cfg->n_layers;
+  for (int i = 0; i < L * QL_NPROJ; ++i) {
+    if (!dA[i] || !dB[i]) return set_error(QL_ERR_ARG, "%s: dA[%d] or dB[%d] is NULL", fn, i, i);
+    if (!aligned(dA[i], 16) || !aligned(dB[i], 16))
+      return set_error(QL_ERR_ALIGN, "%s: dA[%d] / dB[%d] must be 16-byte aligned", fn, i, i);
+  }
+  if (M > 0) {
+    QL_TRY(check_ptr(fn, "dy", dy, 16));
+    if (dx0) QL_TRY(check_ptr(fn, "dx0", dx0, 16));
+  }
+  hipStream_t C = (hipStream_t)compute, P = (hipStream_t)copy;
+  if (M == 0) {
+    if (!accumulate)
+      for (int l = 0; l < L; ++l)
+        for (int p = 0; p < QL_NPROJ; ++p) {
+          QL_TRY(launch_zero_f32(dA[l * QL_NPROJ + p], (int64_t)cfg->r * sc.SL.K[p], C));
+          QL_TRY(launch_zero_f32(dB[l * QL_NPROJ + p], sc.SL.N[p] * cfg->r, C));
+        }
+    return sc.pageable ? QL_WARN_PAGEABLE_HOST : QL_OK;
+  }
+  const uint8_t* sv = (const uint8_t*)saved;
+  uint8_t* w8 = (uint8_t*)ws;
+  const uint8_t* st8 = (const uint8_t*)store;
+  uint8_t* sl8 = (uint8_t*)slots;
+  const size_t rec = (size_t)sc.SL.rec;
+  Events ev;
+  const bool streamed = !cfg->resident;
+  // layers L-1, L-2, ... ; layer l uses slot l % 2 (the forward's mapping)
+  bool have_ready[2] = {false, false};
+  if (streamed) {
+    QL_TRY(ev.create());
+    for (int i = 0; i < 2 && i < L; ++i) {
+      const int l = L - 1 - i;
+      if (reuse_fwd_slots) continue;  // the forward left layers L-1 and L-2 in their slots
+      QL_HIP_CHECK(hipMemcpyAsync(sl8 + (l & 1) * rec, st8 + (size_t)l * rec, rec, hipMemcpyHostToDevice, P));
+      QL_HIP_CHECK(hipEventRecord(ev.ready[l & 1], P));
+      have_ready[l & 1] = true;
+    }
+  }
+  uint16_t* dhA = (uint16_t*)(w8 + sc.WS.dhA);
+  uint16_t* dhB = (uint16_t*)(w8 + sc.WS.dhB);
+  const uint16_t* dh = (const uint16_t*)dy;
+  for (int l = L - 1; l >= 0; --l) {
+    const int slot = l & 1;
+    const uint8_t* base;
+    if (!streamed) {
+      base = st8 + (size_t)l * rec;
+    } else {
+      if (have_ready[slot]) QL_HIP_CHECK(hipStreamWaitEvent(C, ev.ready[slot], 0));
+      base = sl8 + slot * rec;
+    }
+    uint16_t* out = (l == 0 && dx0) ? (uint16_t*)dx0 : (((L - 1 - l) & 1) ? dhB : dhA);
+    QL_TRY(layer_bwd(cfg, sc.SL, layer_weights(sc.SL, base), lora + l * QL_NPROJ, M, sc.SV,
+                     sv + (size_t)l * sc.SV.per_layer, dh, out, dA + l * QL_NPROJ, dB + l * QL_NPROJ,
+                     accumulate, w8, sc.WS, C));
+    dh = out;
+    if (streamed && l - 2 >= 0) {
+      QL_HIP_CHECK(hipEventRecord(ev.free_[slot], C));
+      QL_HIP_CHECK(hipStreamWaitEvent(P, ev.free_[slot], 0));
+      QL_HIP_CHECK(hipMemcpyAsync(sl8 + slot * rec, st8 + (size_t)(l - 2) * rec, rec, hipMemcpyHostToDevice, P));
+      QL_HIP_CHECK(hipEventRecord(ev.ready[slot], P));
+      have_ready[slot] = true;
+    }
+  }
+  return sc.pageable ? QL_WARN_PAGEABLE_HOST : QL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,198 @@
+// Glue of the attention-free decoder-layer stand-in: RMSNorm (unit gain,
+// float32 statistics), SwiGLU silu(g) * u, and the head-group sum that is the
+// backward of repeat_kv. All are memory-bound row or elementwise kernels;
+// reductions run in a fixed lane order, so results are deterministic.
+#include "ql_internal.h"
+
+namespace ql {
+namespace {
+
+__device__ __forceinline__ void unpack8(const uint4 q, float (&f)[8]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// One wave per row, 8 elements per lane per chunk (H % 8 == 0).
+__global__ __launch_bounds__(256) void k_rmsnorm_fwd(const uint16_t* __restrict__ h, int64_t M, int64_t H,
+                                                     float eps, uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const uint4* hr = (const uint4*)(h + row * H);
+  const int64_t nq = H / 8;
+  float ss = 0.f;
+  for (int64_t q = lane; q < nq; q += 64) {
+    float f[8];
+    unpack8(hr[q], f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += f[i] * f[i];
+  }
+  ss = wave_sum(ss);
+  const float rs = 1.0f / sqrtf(ss / (float)H + eps);
+  uint4* orow = (uint4*)(out + row * H);
+  for (int64_t q = lane; q < nq; q += 64) {
+    float f[8];
+    unpack8(hr[q], f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] *= rs;
+    orow[q] = pack8(f);
+  }
+}
+
+// out = bf16(resid + rs * dn - (rs^3 / H) * h * sum(dn * h)), rs = 1/sqrt(mean(h^2) + eps)
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict__ h,
+                                                     const uint16_t* __restrict__ dn,
+                                                     const uint16_t* __restrict__ resid, int64_t M,
+                                                     int64_t H, float eps, uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const uint4* hr = (const uint4*)(h + row * H);
+  const uint4* dr = (const uint4*)(dn + row * H);
+  const uint4* rr = (const uint4*)(resid + row * H);
+  const int64_t nq = H / 8;
+  float ss = 0.f, dot = 0.f;
+  for (int64_t q = lane; q < nq; q += 64) {
+    float a[8], b[8];
+    unpack8(hr[q], a);
+    unpack8(dr[q], b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ss += a[i] * a[i];
+      dot += a[i] * b[i];
+    }
+  }
+  ss = wave_sum(ss);
+  dot = wave_sum(dot);
+  const float rs = 1.0f / sqrtf(ss / (float)H + eps);
+  const float c = rs * rs * rs / (float)H * dot;
+  uint4* orow = (uint4*)(out + row * H);
+  for (int64_t q = lane; q < nq; q += 64) {
+    float a[8], b[8], r[8];
+    unpack8(hr[q], a);
+    unpack8(dr[q], b);
+    unpack8(rr[q], r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = r[i] + (rs * b[i] - c * a[i]);
+    orow[q] = pack8(r);
+  }
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+__global__ __launch_bounds__(256) void k_swiglu_fwd(const uint4* __restrict__ g, const uint4* __restrict__ u,
+                                                    int64_t nq, uint4* __restrict__ act) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += stride) {
+    float gf[8], uf[8], o[8];
+    unpack8(g[q], gf);
+    unpack8(u[q], uf);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = gf[i] * sigmoidf_(gf[i]) * uf[i];
+    act[q] = pack8(o);
+  }
+}
+
+// dg = dact * u * sig(g) (1 + g (1 - sig(g))), du = dact * silu(g)
+__global__ __launch_bounds__(256) void k_swiglu_bwd(const uint4* __restrict__ g, const uint4* __restrict__ u,
+                                                    const uint4* __restrict__ da, int64_t nq,
+                                                    uint4* __restrict__ dg, uint4* __restrict__ du) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += stride) {
+    float gf[8], uf[8], df[8], og[8], ou[8];
+    unpack8(g[q], gf);
+    unpack8(u[q], uf);
+    unpack8(da[q], df);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sg = sigmoidf_(gf[i]);
+      og[i] = df[i] * uf[i] * (sg * (1.0f + gf[i] * (1.0f - sg)));
+      ou[i] = df[i] * (gf[i] * sg);
+    }
+    dg[q] = pack8(og);
+    du[q] = pack8(ou);
+  }
+}
+
+__global__ void k_repeat_kv_bwd(const float* __restrict__ da, int64_t M, int64_t H, int64_t kv, int d,
+                                uint16_t* __restrict__ dv) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= M * kv) return;
+  const int64_t m = idx / kv, c = idx - m * kv;
+  const int64_t g = c / d, i = c - g * d;
+  const int64_t n_rep = H / kv;
+  float s = 0.f;
+  for (int64_t j = 0; j < n_rep; ++j) s += da[m * H + (g * n_rep + j) * d + i];
+  dv[idx] = f32_to_bf16(s);
+}
+
+unsigned grid_for(int64_t n) {
+  int64_t g = (n + 255) / 256;
+  if (g > 256 * 32) g = 256 * 32;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+ql_status launch_rmsnorm_fwd(const uint16_t* h, int64_t M, int64_t H, float eps, uint16_t* out,
+                             hipStream_t st) {
+  if (M == 0) return QL_OK;
+  hipLaunchKernelGGL(k_rmsnorm_fwd, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st, h, M, H, eps, out);
+  QL_HIP_CHECK(hipGetLastError());
+  return QL_OK;
+}
+
+ql_status launch_rmsnorm_bwd(const uint16_t* h, const uint16_t* dn, const uint16_t* resid, int64_t M,
+                             int64_t H, float eps, uint16_t* out, hipStream_t st) {
+  if (M == 0) return QL_OK;
+  hipLaunchKernelGGL(k_rmsnorm_bwd, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st, h, dn, resid, M, H,
+                     eps, out);
+  QL_HIP_CHECK(hipGetLastError());
+  return QL_OK;
+}
+
+ql_status launch_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* act,
+                            hipStream_t st) {
+  const int64_t nq = n / 8;
+  if (nq == 0) return QL_OK;
+  hipLaunchKernelGGL(k_swiglu_fwd, dim3(grid_for(nq)), dim3(256), 0, st, (const uint4*)g, (const uint4*)u,
+                     nq, (uint4*)act);
+  QL_HIP_CHECK(hipGetLastError());
+  return QL_OK;
+}
+
+ql_status launch_swiglu_bwd(const uint16_t* g, const uint16_t* u, const uint16_t* dact, int64_t n,
+                            uint16_t* dg, uint16_t* du, hipStream_t st) {
+  const int64_t nq = n / 8;
+  if (nq == 0) return QL_OK;
+  hipLaunchKernelGGL(k_swiglu_bwd, dim3(grid_for(nq)), dim3(256), 0, st, (const uint4*)g, (const uint4*)u,
+                     (const uint4*)dact, nq, (uint4*)dg, (uint4*)du);
+  QL_HIP_CHECK(hipGetLastError());
+  return QL_OK;
+}
+
+ql_status launch_repeat_kv_bwd(const float* da, int64_t M, int64_t H, int64_t kv, int32_t head_dim,
+                               uint16_t* dv, hipStream_t st) {
+  const int64_t n = M * kv;
+  if (n == 0) return QL_OK;
+  hipLaunchKernelGGL(k_repeat_kv_bwd, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, da, M, H, kv,
+                     head_dim, dv);
+  QL_HIP_CHECK(hipGetLastError());
+  return QL_OK;
+}
+
+}  // namespace ql

@@ -1,0 +1,166 @@
+// Internal declarations of the NF4 + LoRA library (HIP, gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/nf4qlora.h"
+
+namespace ql {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// The 16 NF4 levels as float32 bit patterns, ascending. Construction (QLoRA,
+// Dettmers et al. 2023, section 3): standard-normal quantiles at evenly spaced
+// probabilities from 1 - (1/30 + 1/32)/2 down to 1/2, 8 on the positive side
+// and 7 on the negative side, plus an exact zero, divided by the largest level
+// in double precision and rounded once to float32. Level 0 is -1, level 7 is
+// +0, level 15 is +1.
+static __constant__ const uint32_t kNF4LevelBits[16] = {
+    0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du,
+    0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
+    0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
+
+static const uint32_t kNF4LevelBitsHost[16] = {
+    0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du,
+    0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
+    0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// Round-to-nearest-even float32 -> bfloat16 (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two float32 -> one dword of two bfloat16, `lo` in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Error reporting (thread-local message), defined in capi.hip.
+ql_status set_error(ql_status st, const char* fmt, ...);
+
+#define QL_HIP_CHECK(expr)                                                        \
+  do {                                                                            \
+    hipError_t e_ = (expr);                                                       \
+    if (e_ != hipSuccess)                                                         \
+      return ::ql::set_error(QL_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// ---------------------------------------------------------------- launchers
+// All launchers enqueue on `st` and report launch errors through the status.
+
+ql_status launch_nf4_quantize(const float* w, int64_t n, uint8_t* packed, float* absmax,
+                              int* flag, hipStream_t st);
+ql_status launch_clear_i32(int* p, int n, hipStream_t st);
+ql_status launch_nf4_dequant(const uint8_t* packed, const float* absmax, int64_t n, int out_f32,
+                             void* out, hipStream_t st);
+
+// Segment of a fused NF4 GEMM: one frozen projection with its LoRA factors.
+struct FwdSeg {
+  const uint8_t* packed;  // [N x K/2]
+  const float* absmax;    // [N x K/64]
+  const uint16_t* U;      // bf16 [M x r] (row stride r)
+  const uint16_t* B;      // bf16 [N x r]
+  void* out;              // [M x ldo] at column col0
+  const uint16_t* resid;  // optional bf16 residual with the same layout as out
+  int64_t N;
+  int64_t ldo, col0;
+};
+
+constexpr int kMaxSegs = 3;
+
+struct FwdArgs {
+  const uint16_t* X;  // bf16 [M x ldx], logical columns 0..K-1 (optionally remapped)
+  int64_t M, K, ldx;
+  int32_t r;
+  float s;
+  int32_t head_dim, n_rep;  // repeat_kv remap of X's columns (n_rep 0 = none)
+  int32_t out_f32;
+  int32_t nseg;
+  FwdSeg seg[kMaxSegs];
+};
+
+// Reduction segment of the dX GEMM: dX += dY_s W_s + s G_s A_s.
+struct BwdSeg {
+  const uint16_t* dY;     // bf16 [M x N]
+  const uint8_t* packed;  // [N x K/2]
+  const float* absmax;    // [N x K/64]
+  const uint16_t* G;      // bf16 [M x r]
+  const uint16_t* A;      // bf16 [r x K]
+  int64_t N;
+};
+
+struct BwdArgs {
+  int64_t M, K;
+  int32_t r;
+  float s;
+  void* out;  // [M x K] bf16 or f32
+  int32_t out_f32;
+  const uint16_t* resid;
+  int32_t nseg;
+  BwdSeg seg[kMaxSegs];
+};
+
+ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st);
+ql_status launch_gemm_bwd(const BwdArgs& a, hipStream_t st);
+
+// Skinny NT product with split-K: out_j[m][0..r) = bf16(sum_k X[m][k] * Bt_j[.][k]).
+// X columns optionally remapped by repeat_kv. Up to kMaxSegs projections at once
+// (they share X). Needs splitk_ws_bytes() of workspace.
+struct SkinnyArgs {
+  const uint16_t* X;  // bf16 [M x ldx]
+  int64_t M, K, ldx;
+  int32_t head_dim, n_rep;
+  int32_t r;  // columns per projection
+  int32_t nseg;
+  const uint16_t* Bt[kMaxSegs];  // bf16 [r x K]
+  uint16_t* out[kMaxSegs];       // bf16 [M x r]
+};
+size_t skinny_ws_bytes(int64_t M, int64_t K, int32_t r, int32_t nseg);
+ql_status launch_skinny(const SkinnyArgs& a, void* ws, hipStream_t st);
+
+// Column reduction over rows with a fixed order: out[j][c] = s * sum_m Z[m][c] * V[m][j]
+// (+ out if accumulate); Z columns optionally remapped by repeat_kv; V is [M x r] bf16.
+// transpose_out writes out[c * r + j] instead of out[j * C + c].
+struct ColRedArgs {
+  const uint16_t* Z;  // bf16 [M x ldz]
+  int64_t M, C, ldz;
+  int32_t head_dim, n_rep;
+  const uint16_t* V;  // bf16 [M x r]
+  int32_t r;
+  float s;
+  float* out;
+  int32_t transpose_out, accumulate;
+};
+size_t colred_ws_bytes(int64_t M, int64_t C, int32_t r);
+ql_status launch_colred(const ColRedArgs& a, void* ws, hipStream_t st);
+
+ql_status launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
+                                hipStream_t st);
+ql_status launch_zero_f32(float* p, int64_t n, hipStream_t st);
+
+// Glue of the decoder-layer stand-in.
+ql_status launch_rmsnorm_fwd(const uint16_t* h, int64_t M, int64_t H, float eps, uint16_t* out,
+                             hipStream_t st);
+// out = bf16(resid + d/dh RMSNorm(h) applied to dn)
+ql_status launch_rmsnorm_bwd(const uint16_t* h, const uint16_t* dn, const uint16_t* resid,
+                             int64_t M, int64_t H, float eps, uint16_t* out, hipStream_t st);
+ql_status launch_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* act,
+                            hipStream_t st);
+ql_status launch_swiglu_bwd(const uint16_t* g, const uint16_t* u, const uint16_t* dact, int64_t n,
+                            uint16_t* dg, uint16_t* du, hipStream_t st);
+// dv[m][g*d + i] = bf16(sum_j da[m][(g*n_rep + j)*d + i]), da float32 [M x H]
+ql_status launch_repeat_kv_bwd(const float* da, int64_t M, int64_t H, int64_t kv, int32_t head_dim,
+                               uint16_t* dv, hipStream_t st);
+
+}  // namespace ql

@@ -50,6 +50,11 @@ def _f32(v, mode):
     return np.asarray(v, np.float64).astype(np.float32).astype(np.float64) if mode == "faithful" else v
 
 
+def lora_down(x, A, mode="faithful"):
+    """U = x A^T (bf16 in faithful mode)."""
+    return _r(np.asarray(x, np.float64) @ np.asarray(A, np.float64).T, mode)
+
+
 def fwd(x, packed, absmax, N, K, A, B, alpha, mode="faithful", W=None):
     """Returns (y [M x N], U [M x r]).
 
@@ -63,7 +68,7 @@ def fwd(x, packed, absmax, N, K, A, B, alpha, mode="faithful", W=None):
     s = alpha / r
     if W is None:
         W = weight(packed, absmax, N, K, mode)
-    U = _r(x @ A.T, mode)
+    U = lora_down(x, A, mode)
     y = _r(x @ W.T + s * (U @ B.T), mode)
     return y, U
 

@@ -162,6 +162,27 @@ def dequant_bf16(packed, absmax) -> np.ndarray:
     return round_bf16(dequant_f32(packed, absmax).astype(np.float64))
 
 
+def dequant_rows_bf16(packed, absmax, K, rows) -> np.ndarray:
+    """Rows `rows` of the bf16 dequantised [N x K] weight, as float64 [len(rows) x K]."""
+    rows = np.asarray(rows)
+    p = np.asarray(packed, np.uint8).reshape(-1, K // 2)[rows]
+    a = np.asarray(absmax, np.float32).reshape(-1, K // BLOCK)[rows]
+    return dequant_bf16(p.reshape(-1), a.reshape(-1)).reshape(len(rows), K)
+
+
+def dequant_cols_bf16(packed, absmax, N, K, cols) -> np.ndarray:
+    """Columns `cols` of the bf16 dequantised [N x K] weight, as float64 [N x len(cols)].
+
+    Element (n, k) is nibble k of row n: byte k // 2, high nibble when k is even.
+    """
+    cols = np.asarray(cols)
+    p = np.asarray(packed, np.uint8).reshape(N, K // 2)[:, cols // 2]
+    codes = np.where(cols % 2 == 0, p >> 4, p & 15)
+    a = np.asarray(absmax, np.float32).reshape(N, K // BLOCK)[:, cols // BLOCK]
+    w32 = (codebook()[codes] * a).astype(np.float32)
+    return round_bf16(w32.astype(np.float64))
+
+
 def nearest_code_exact(n: float) -> int:
     """Reference nearest-level rule in exact rational arithmetic (for small brute-force checks)."""
     c = [Fraction(float(x)) for x in codebook()]

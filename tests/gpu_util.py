@@ -1,0 +1,60 @@
+"""Helpers shared by the GPU tests: library loading and the comparison rule."""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import nf4_layer_streamed_amd as ql  # noqa: E402
+
+DEV = "cuda:0"
+TOL = 2e-2  # relative tolerance for GEMM outputs and gradients (bf16 in, fp32 accumulate)
+
+
+def lib():
+    if not os.path.exists(ql.LIB_PATH):
+        from nf4_layer_streamed_amd import build
+        build.build()
+    return ql.load()
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+    lib()
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def close(got, want, tol=TOL, what=""):
+    """Element-wise |g - o| <= tol |o| + tol rms(o); also returns the normwise error."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    rms = float(np.sqrt(np.mean(want * want))) if want.size else 0.0
+    err = np.abs(got - want)
+    bound = tol * np.abs(want) + tol * rms
+    bad = err > bound
+    nrm = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
+    if np.any(bad):
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} elements out of tolerance; worst at {i}: "
+                             f"got {got[i]!r} want {want[i]!r} (rms {rms:.3g}); normwise {nrm:.3g}")
+    return nrm
+
+
+def bf16_bits_t(t):
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def f32_bits_t(t):
+    return t.detach().cpu().view(torch.int32).numpy().view(np.uint32)

@@ -1,0 +1,130 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every function the header declares, and refuses bad arguments before touching
+the device."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import ROOT, lib, ql
+from oracle import nf4 as onf4
+from oracle import stack as ostack
+
+HEADER = os.path.join(ROOT, "include", "nf4qlora.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names) - {"if", "while"})
+
+
+def test_header_declares_the_abi():
+    fns = header_functions()
+    for name in ("nf4_quantize", "nf4_dequant", "qlora_linear_fwd", "qlora_linear_bwd",
+                 "stream_layer_stack_fwd", "stream_layer_stack_bwd"):
+        assert name in fns
+    assert set(fns) == set(ql.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = lib()
+    for name in header_functions():
+        assert hasattr(L, name), name
+    raw = ctypes.CDLL(ql.LIB_PATH)
+    for name in header_functions():
+        getattr(raw, name)
+
+
+def test_abi_version_and_codebook():
+    lib()
+    assert ql.ql_abi_version() == 100
+    assert np.array_equal(ql.nf4_codebook().numpy().view(np.uint32), onf4.codebook().view(np.uint32))
+
+
+def test_workspace_shape_validation():
+    lib()
+    f, b = ql.qlora_linear_workspace(64, 512, 256, 8)
+    assert f > 0 and b > 0
+    for args, st in (((64, 512, 250, 8), ql.QL_ERR_SHAPE), ((64, 500, 256, 8), ql.QL_ERR_SHAPE),
+                     ((64, 512, 256, 0), ql.QL_ERR_RANK), ((64, 512, 256, 65), ql.QL_ERR_RANK),
+                     ((-1, 512, 256, 8), ql.QL_ERR_SHAPE)):
+        with pytest.raises(ql.QlError) as e:
+            ql.qlora_linear_workspace(*args)
+        assert e.value.status == st
+        assert ql.ql_last_error()
+
+
+def test_linear_validation_refuses_before_device_work():
+    # Shape and rank errors are reported before any HIP call is made.
+    lib()
+    x = torch.zeros(64, 256, dtype=torch.bfloat16)
+    W = ql.NF4Weight(torch.zeros(100, dtype=torch.uint8), torch.zeros(4, dtype=torch.float32), 512, 250)
+    L = ql.Lora(torch.zeros(8, 256, dtype=torch.bfloat16), torch.zeros(512, 8, dtype=torch.bfloat16), 8, 16.0)
+    with pytest.raises(ql.QlError) as e:
+        ql.qlora_linear_fwd(x, 64, W, L, x, x, x, stream=0)
+    assert e.value.status == ql.QL_ERR_SHAPE and "W.K" in ql.ql_last_error()
+    W = ql.NF4Weight(torch.zeros(100, dtype=torch.uint8), torch.zeros(4, dtype=torch.float32), 512, 256)
+    L = ql.Lora(L.A, L.B, 0, 16.0)
+    with pytest.raises(ql.QlError) as e:
+        ql.qlora_linear_fwd(x, 64, W, L, x, x, x, stream=0)
+    assert e.value.status == ql.QL_ERR_RANK
+
+
+def test_quantize_dequant_size_validation():
+    lib()
+    w = torch.zeros(100)
+    with pytest.raises(ql.QlError) as e:
+        ql.nf4_quantize(w, torch.zeros(50, dtype=torch.uint8), torch.zeros(2), stream=0)
+    assert e.value.status == ql.QL_ERR_SHAPE
+    with pytest.raises(ql.QlError) as e:
+        ql._check(ql.load().nf4_dequant(None, None, 64, 7, None, None))
+    assert e.value.status == ql.QL_ERR_ARG
+
+
+@pytest.mark.parametrize("name,L,H,I,KV,d,r", [
+    ("smollm2_stack", 30, 576, 1536, 192, 64, 8),
+    ("qwen3b_stack", 36, 2048, 11008, 256, 128, 16),
+    ("llama8b_stack", 32, 4096, 14336, 1024, 128, 16),
+])
+def test_stack_layout_sizes(name, L, H, I, KV, d, r):
+    # The store is the algorithmic 0.5625 B/weight plus at most 256 B of
+    # alignment per tensor; records and tensors are 256-byte aligned; two
+    # slots hold exactly two records.
+    lib()
+    cfg = ql.StackCfg(L, H, I, KV, d, r, 2.0 * r)
+    offs, proj, total = ql.stream_layer_stack_layout(cfg)
+    alg = ostack.nf4_store_bytes(L, H, I, KV)
+    assert alg <= total <= alg + L * 14 * 256
+    assert offs[0] == 0 and offs[-1] == total
+    rec = offs[1]
+    assert all(o % 256 == 0 for o in offs)
+    assert all(a % 256 == 0 and b % 256 == 0 for a, b in proj.values())
+    for p, (po, ao) in proj.items():
+        N, K = cfg.proj_shape(p)
+        assert po + N * K // 2 <= rec and ao + N * K // 64 * 4 <= rec
+    spans = sorted((po, po + cfg.proj_shape(p)[0] * cfg.proj_shape(p)[1] // 2) for p, (po, _) in proj.items())
+    spans += sorted((ao, ao + cfg.proj_shape(p)[0] * cfg.proj_shape(p)[1] // 16) for p, (_, ao) in proj.items())
+    spans.sort()
+    assert all(spans[i][1] <= spans[i + 1][0] for i in range(len(spans) - 1))
+    slots, saved, ws = ql.stream_layer_stack_workspace(cfg, 512)
+    assert slots == 2 * rec
+    offs_s, per = ql.stream_layer_stack_saved_layout(cfg, 512)
+    assert saved == per * L
+
+
+def test_stack_cfg_validation():
+    lib()
+    bad = [ql.StackCfg(0, 576, 1536, 192, 64, 8, 16.0), ql.StackCfg(2, 577, 1536, 192, 64, 8, 16.0),
+           ql.StackCfg(2, 576, 1536, 200, 64, 8, 16.0), ql.StackCfg(2, 576, 1536, 192, 64, 0, 16.0),
+           ql.StackCfg(2, 576, 1536, 192, 64, 8, 16.0, n_buffers=3)]
+    want = [ql.QL_ERR_SHAPE, ql.QL_ERR_SHAPE, ql.QL_ERR_SHAPE, ql.QL_ERR_RANK, ql.QL_ERR_UNSUPPORTED]
+    for cfg, st in zip(bad, want):
+        with pytest.raises(ql.QlError) as e:
+            ql.stream_layer_stack_layout(cfg)
+        assert e.value.status == st, (cfg, ql.ql_last_error())

@@ -212,3 +212,15 @@ def test_dequant_bf16_power_of_two_scales_commute():
         out = nf4.dequant_bf16(nf4.pack(codes), np.array([a], np.float32))
         want = np.ldexp(torch.from_numpy(c.astype(np.float32)).to(torch.bfloat16).double().numpy(), e)
         assert np.array_equal(out, want[codes])
+
+
+def test_row_and_column_dequant_match_full_dequant():
+    g = np.random.default_rng(5)
+    N, K = 48, 256
+    w = (g.standard_normal(N * K) * 0.02).astype(np.float32)
+    packed, absmax = nf4.quantize(w)
+    full = nf4.dequant_bf16(packed, absmax).reshape(N, K)
+    rows = np.array([0, 7, 47])
+    cols = np.array([0, 1, 63, 64, 130, 255])
+    assert np.array_equal(nf4.dequant_rows_bf16(packed, absmax, K, rows), full[rows])
+    assert np.array_equal(nf4.dequant_cols_bf16(packed, absmax, N, K, cols), full[:, cols])
