@@ -28,8 +28,9 @@ EXPORTS = (
     "ql_last_error", "ql_abi_version", "nf4_codebook", "nf4_quantize", "nf4_dequant",
     "qlora_linear_workspace", "qlora_linear_fwd", "qlora_linear_bwd",
     "stream_layer_stack_layout", "stream_layer_stack_workspace", "stream_layer_stack_saved_layout",
-    "stream_layer_stack_fwd", "stream_layer_stack_bwd",
+    "stream_layer_stack_fwd", "stream_layer_stack_bwd", "ql_profile_enable", "ql_profile_read",
 )
+QL_KERNEL_GEMM_FWD, QL_KERNEL_GEMM_BWD = 0, 1
 
 
 class QlError(RuntimeError):
@@ -83,6 +84,9 @@ def load(path=LIB_PATH):
                                          P, SZ, P, P]),
         "stream_layer_stack_bwd": (I32, [ctypes.POINTER(ql_stack_cfg), P, SZ, P, P, I64, P, SZ, P, P, P,
                                          I32, I32, P, SZ, P, SZ, P, P]),
+        "ql_profile_enable": (I32, [I32]),
+        "ql_profile_read": (I32, [I32, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_double),
+                                  ctypes.POINTER(ctypes.c_double)]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -282,3 +286,14 @@ def build_store(cfg, layers, pinned=True, device=None):
             ab = absmax.reshape(-1).view(torch.uint8)
             store[base + ao: base + ao + ab.numel()].copy_(ab)
     return store
+
+
+def ql_profile_enable(on):
+    return _check(load().ql_profile_enable(int(on)))
+
+
+def ql_profile_read(kernel):
+    """-> (launches, total ms, total algorithmic FLOPs) of one fused GEMM kernel."""
+    n, ms, fl = ctypes.c_int64(), ctypes.c_double(), ctypes.c_double()
+    _check(load().ql_profile_read(kernel, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl)))
+    return n.value, ms.value, fl.value

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "ql_internal.h"
 
@@ -494,6 +495,52 @@ static ql_status validate_stack(const char* fn, const ql_stack_cfg* cfg, const v
   return QL_OK;
 }
 
+// ------------------------------------------------------- kernel timing
+struct ProfRec {
+  hipEvent_t a, b;
+  int kernel;
+  double flop;
+};
+static std::mutex g_prof_mu;
+static bool g_prof_on = false;
+static std::vector<ProfRec> g_prof;
+
+bool profiling_on() { return g_prof_on; }
+
+ql_status profile_begin(hipStream_t st, void** token) {
+  ProfRec* r = new ProfRec{};
+  hipError_t e = hipEventCreate(&r->a);
+  if (e == hipSuccess) e = hipEventCreate(&r->b);
+  if (e == hipSuccess) e = hipEventRecord(r->a, st);
+  if (e != hipSuccess) {
+    delete r;
+    return set_error(QL_ERR_HIP, "profiling event: %s", hipGetErrorString(e));
+  }
+  *token = r;
+  return QL_OK;
+}
+
+ql_status profile_end(hipStream_t st, void* token, int kernel, double flop) {
+  ProfRec* r = (ProfRec*)token;
+  r->kernel = kernel;
+  r->flop = flop;
+  hipError_t e = hipEventRecord(r->b, st);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.push_back(*r);
+  delete r;
+  if (e != hipSuccess) return set_error(QL_ERR_HIP, "profiling event: %s", hipGetErrorString(e));
+  return QL_OK;
+}
+
+static void profile_clear() {
+  for (auto& r : g_prof) {
+    (void)hipEventSynchronize(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof.clear();
+}
+
 }  // namespace ql
 
 using namespace ql;
@@ -501,6 +548,36 @@ using namespace ql;
 extern "C" {
 
 const char* ql_last_error(void) { return g_err; }
+
+ql_status ql_profile_enable(int32_t on) {
+  clear_error();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (on) profile_clear();
+  g_prof_on = on != 0;
+  return QL_OK;
+}
+
+ql_status ql_profile_read(int32_t kernel, int64_t* launches, double* ms, double* flop) {
+  clear_error();
+  if (kernel < 0 || kernel >= QL_KERNEL_COUNT)
+    return set_error(QL_ERR_ARG, "ql_profile_read: kernel (%d) out of range", kernel);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int64_t n = 0;
+  double t = 0, f = 0;
+  for (auto& r : g_prof) {
+    if (r.kernel != kernel) continue;
+    QL_HIP_CHECK(hipEventSynchronize(r.b));
+    float e = 0;
+    QL_HIP_CHECK(hipEventElapsedTime(&e, r.a, r.b));
+    ++n;
+    t += e;
+    f += r.flop;
+  }
+  if (launches) *launches = n;
+  if (ms) *ms = t;
+  if (flop) *flop = f;
+  return QL_OK;
+}
 
 int32_t ql_abi_version(void) { return 100; }
 

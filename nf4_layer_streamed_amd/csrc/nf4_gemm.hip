@@ -386,6 +386,12 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_bwd(const BwdArgs a, int tiles_m
   });
 }
 
+#define QL_TRY_PROF(expr)        \
+  do {                           \
+    ql_status rc_ = (expr);      \
+    if (rc_ != QL_OK) return rc_; \
+  } while (0)
+
 bool g_attr_set[64] = {};
 
 ql_status ensure_attrs() {
@@ -416,8 +422,16 @@ ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st) {
   // unused segment starts point past the end so no tile maps to them
   const int s1 = a.nseg > 1 ? start[1] : total + 1;
   const int s2 = a.nseg > 2 ? start[2] : total + 1;
+  void* tok = nullptr;
+  const bool prof = profiling_on();
+  if (prof) QL_TRY_PROF(profile_begin(st, &tok));
   hipLaunchKernelGGL(k_gemm_fwd, dim3(total), dim3(NT), LDS_BYTES, st, a, tiles_m, total, s1, s2);
   QL_HIP_CHECK(hipGetLastError());
+  if (prof) {
+    double flop = 0;
+    for (int s = 0; s < a.nseg; ++s) flop += 2.0 * (double)a.M * (double)a.seg[s].N * (double)(a.K + a.r);
+    QL_TRY_PROF(profile_end(st, tok, QL_KERNEL_GEMM_FWD, flop));
+  }
   return QL_OK;
 }
 
@@ -428,8 +442,16 @@ ql_status launch_gemm_bwd(const BwdArgs& a, hipStream_t st) {
   const int tiles_m = (int)((a.M + BM - 1) / BM);
   const int total = tiles_m * (int)((a.K + BN - 1) / BN);
   if (total == 0) return QL_OK;
+  void* tok = nullptr;
+  const bool prof = profiling_on();
+  if (prof) QL_TRY_PROF(profile_begin(st, &tok));
   hipLaunchKernelGGL(k_gemm_bwd, dim3(total), dim3(NT), LDS_BYTES, st, a, tiles_m, total);
   QL_HIP_CHECK(hipGetLastError());
+  if (prof) {
+    double flop = 0;
+    for (int s = 0; s < a.nseg; ++s) flop += 2.0 * (double)a.M * (double)a.K * (double)(a.seg[s].N + a.r);
+    QL_TRY_PROF(profile_end(st, tok, QL_KERNEL_GEMM_BWD, flop));
+  }
   return QL_OK;
 }
 

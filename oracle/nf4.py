@@ -158,8 +158,17 @@ def bf16_bits(v) -> np.ndarray:
 
 
 def dequant_bf16(packed, absmax) -> np.ndarray:
-    """bf16(fl32(c[code] * absmax)) as float64 values."""
-    return round_bf16(dequant_f32(packed, absmax).astype(np.float64))
+    """bf16(fl32(c[code] * absmax)) as float64 values.
+
+    The value depends only on (code, absmax), so it is evaluated once per
+    block for each of the 16 codes and then looked up by code.
+    """
+    codes = unpack(packed).reshape(-1, BLOCK)
+    absmax = np.asarray(absmax, np.float32).reshape(-1)
+    if absmax.size != codes.shape[0]:
+        raise ValueError("dequant: absmax count does not match the packed size")
+    table = round_bf16((codebook()[None, :] * absmax[:, None]).astype(np.float32).astype(np.float64))
+    return np.take_along_axis(table, codes.astype(np.intp), axis=1).reshape(-1)
 
 
 def dequant_rows_bf16(packed, absmax, K, rows) -> np.ndarray:

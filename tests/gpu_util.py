@@ -58,3 +58,25 @@ def bf16_bits_t(t):
 
 def f32_bits_t(t):
     return t.detach().cpu().view(torch.int32).numpy().view(np.uint32)
+
+
+def close_norm(got, want, tol=TOL, what=""):
+    """Normwise ||g - o|| / ||o|| <= tol (for outputs at the end of deep stacks)."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    nrm = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
+    assert nrm <= tol, f"{what}: normwise error {nrm:.3g} > {tol}"
+    return nrm
+
+
+def as_accurate(got, faithful, exact, what="", slack=1.25, floor=1e-3):
+    """The GPU result is as close to the float64-exact result as the bf16-faithful
+    oracle is: ||g - e|| <= slack ||f - e|| + floor ||e||."""
+    got, faithful, exact = (np.asarray(a, np.float64) for a in (got, faithful, exact))
+    ne = max(np.linalg.norm(exact), 1e-300)
+    eg = float(np.linalg.norm(got - exact) / ne)
+    ef = float(np.linalg.norm(faithful - exact) / ne)
+    assert eg <= slack * ef + floor, f"{what}: gpu-vs-exact {eg:.3g} > {slack} x faithful-vs-exact {ef:.3g} + {floor}"
+    return eg, ef

@@ -224,3 +224,15 @@ def test_row_and_column_dequant_match_full_dequant():
     cols = np.array([0, 1, 63, 64, 130, 255])
     assert np.array_equal(nf4.dequant_rows_bf16(packed, absmax, K, rows), full[rows])
     assert np.array_equal(nf4.dequant_cols_bf16(packed, absmax, N, K, cols), full[:, cols])
+
+
+def test_dequant_bf16_table_form_equals_elementwise_definition():
+    g = np.random.default_rng(6)
+    n = 64 * 3000
+    packed = g.integers(0, 256, n // 2).astype(np.uint8)
+    absmax = np.concatenate([g.uniform(0, 1, 2990), [0.0, 1e-40, 3.4e38, 1.0, 2.0 ** -126, 7.0, 1e-3, 0.05,
+                                                     1e20, 1e-20]]).astype(np.float32)
+    want = nf4.round_bf16(nf4.dequant_f32(packed, absmax).astype(np.float64))
+    got = nf4.dequant_bf16(packed, absmax)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+    assert np.array_equal(got, want)
