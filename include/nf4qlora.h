@@ -84,8 +84,9 @@ ql_status nf4_codebook(float* out /* host [16] */);
  * row-major flattened; n % 64 == 0). For each block of 64 consecutive
  * elements: absmax = max |w|; each element's code is the index of the nearest
  * NF4 level to fl32(w / absmax) (ties to the lower index); an all-zero block
- * gets code 7 (the zero level) and absmax 0. Byte i of `packed` holds element
- * 2i in its high nibble and element 2i+1 in its low nibble.
+ * gets code 7 (the zero level) and absmax 0. Codes are packed 8 to a 32-bit
+ * little-endian word (elements 8w..8w+7 in bytes 4w..4w+3): byte j of word w
+ * holds element 8w+j in its low nibble and element 8w+j+4 in its high nibble.
  * Quantisation is offline, done once per tensor (docs "NF4 streaming": "the
  * base is quantised once, offline, one tensor at a time").
  *   packed: uint8 [n/2], absmax: float32 [n/64]; all 16-byte aligned.

@@ -2,8 +2,10 @@
 //
 // Format (the pages leave it open; QLoRA section 3 with a float32 scale):
 // blocks of 64 consecutive elements of the row-major weight, one float32
-// absmax per block, one 4-bit code per element, element 2i in the high nibble
-// of byte i and 2i+1 in the low nibble.
+// absmax per block, one 4-bit code per element. Codes are packed 8 to a 32-bit
+// little-endian word: byte j of the word holds code j in its low nibble and
+// code j + 4 in its high nibble. (This order lets a decoder split a word into
+// two byte-lane index vectors with one mask and one shift each.)
 #include "ql_internal.h"
 
 namespace ql {
@@ -14,7 +16,7 @@ namespace ql {
 // comparison of a float32 with them is exact, so this is the nearest level
 // with ties going to the lower index.
 __global__ __launch_bounds__(256) void k_nf4_quantize(const float4* __restrict__ w, int64_t nblocks,
-                                                      uint16_t* __restrict__ packed,
+                                                      uint8_t* __restrict__ packed,
                                                       float* __restrict__ absmax, int* flag) {
   __shared__ double mid[15];
   if (threadIdx.x < 15) {
@@ -35,8 +37,7 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float4* __restrict__
   float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
   // max over the 16 lanes of this block (xor offsets stay inside aligned groups of 16)
   for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
-  if (!active) return;
-  if (lane16 == 0) absmax[blk] = m;
+  if (active && lane16 == 0) absmax[blk] = m;
   uint32_t c[4];
   const float e[4] = {v.x, v.y, v.z, v.w};
   for (int i = 0; i < 4; ++i) {
@@ -49,9 +50,11 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float4* __restrict__
       c[i] = k;
     }
   }
-  const uint32_t b0 = (c[0] << 4) | c[1];
-  const uint32_t b1 = (c[2] << 4) | c[3];
-  packed[blk * 16 + lane16] = (uint16_t)(b0 | (b1 << 8));
+  // Lane pair (2w, 2w+1) holds the 8 codes of word w; the even lane's codes are
+  // the low nibbles, the odd lane's the high nibbles.
+  const uint32_t mine = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  const uint32_t other = (uint32_t)__shfl_xor((int)mine, 1, 16);
+  if (active && (lane16 & 1) == 0) ((uint32_t*)packed)[blk * 8 + (lane16 >> 1)] = mine | (other << 4);
 }
 
 __global__ void k_clear_i32(int* p, int n) {
@@ -73,7 +76,7 @@ ql_status launch_nf4_quantize(const float* w, int64_t n, uint8_t* packed, float*
   if (grid > 0x7fffffff) return set_error(QL_ERR_SHAPE, "nf4_quantize: n too large for one launch");
   if (grid == 0) return QL_OK;
   hipLaunchKernelGGL(k_nf4_quantize, dim3((unsigned)grid), dim3(256), 0, st,
-                     (const float4*)w, nblocks, (uint16_t*)packed, absmax, flag);
+                     (const float4*)w, nblocks, packed, absmax, flag);
   QL_HIP_CHECK(hipGetLastError());
   return QL_OK;
 }
@@ -93,11 +96,11 @@ __global__ __launch_bounds__(256) void k_nf4_dequant(const uint32_t* __restrict_
     const uint32_t p = packed[g];
     const float a = absmax[g >> 3];
     float f[8];
-    // byte i (bits 8i..8i+7) holds element 2i (high nibble) and 2i+1 (low nibble)
+    // byte j holds element j (low nibble) and element j + 4 (high nibble)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = lv[(p >> (8 * i + 4)) & 15u] * a;
-      f[2 * i + 1] = lv[(p >> (8 * i)) & 15u] * a;
+    for (int j = 0; j < 4; ++j) {
+      f[j] = lv[(p >> (8 * j)) & 15u] * a;
+      f[j + 4] = lv[(p >> (8 * j + 4)) & 15u] * a;
     }
     if (F32) {
       float4* o = (float4*)out + g * 2;

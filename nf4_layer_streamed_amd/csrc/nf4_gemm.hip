@@ -3,34 +3,61 @@
 // Forward  (NT): Y[M x N]  = X[M x K] W[N x K]^T + U[M x r] (sB)[N x r]^T
 // Backward (NN): dX[M x K] = sum_seg dY[M x N] W[N x K] + G[M x r] (sA)[r x K]
 //
-// W is never materialised: the tile loader reads the packed 4-bit codes and
-// the block's float32 absmax from global memory, decodes each element to
-// bf16(fl32(level[code] * absmax)) in registers, and writes the bf16 tile to
-// LDS, from where the MFMAs read it. This replaces the per-layer dequant pass
-// that the Soup README ("Citing Soup", v3 retraction) measures as streaming's
-// largest own cost. The LoRA adapter's rank-r product is one more K-step of
-// the same loop (K-concatenation [X | U] [W | sB]^T), so y is written once.
+// W is never materialised in memory. Its packed 4-bit codes and per-block
+// float32 absmax are read from global memory and decoded on chip to
+// bf16(fl32(level[code] * absmax)); this replaces the separate per-layer
+// dequantisation pass that the Soup README ("Citing Soup", v3 retraction)
+// measures as streaming's largest own cost. The LoRA adapter's rank-r product
+// is one extra K-step of the same loop (K-concatenation [X | U] [W | sB]^T),
+// so each output is written once.
 //
-// Tiles: 128 x 128 outputs per workgroup of 256 threads (4 waves, 2 x 2, each
-// 64 x 64 = 4 x 4 MFMA 16x16x32 tiles), K-step 64 = one NF4 block, two LDS
-// stages of 32 KB (A and B tiles of 128 rows x 64 bf16). LDS rows are 128 B,
-// split in eight 16-B chunks; chunk c of row r is stored at c ^ (r & 7) so the
-// 16-B fragment reads of eight consecutive rows hit distinct banks.
+// Decode. Within one NF4 block (64 weights of a row) there are only 16
+// distinct values, bf16(level[j] * absmax). A lane computes these 16 values
+// once per row and block (16 multiplies, 8 packed conversions), keeps them as
+// two 16-byte tables (low bytes and high bytes of the bf16 values), and looks
+// codes up four at a time with v_perm_b32 byte selects: two 8-entry selects and
+// a third select on bit 3 of the code, per byte plane.
+//
+// MFMA: v_mfma_f32_32x32x16_bf16. A lane of a 32x32x16 product holds row or
+// column (lane % 32) and 8 consecutive values of the reduction; here lane
+// group g = lane / 32 takes reduction elements [32 g + 8 q, 32 g + 8 q + 8)
+// in sub-step q of a 64-wide K-step (the A and B operands use the same split,
+// so the product sums over all 64). Output: lane holds column lane % 32 and
+// rows 8 i + 4 g + j for accumulator 4 i + j.
+//
+// Forward layout: 256 x BN outputs per workgroup of 4 waves side by side along
+// N (each wave 256 x BN/4). X tiles (256 rows x 64) go through LDS (two stages,
+// rows of 128 B with the 16-B chunks XOR-swizzled by row); each wave decodes
+// its own W rows straight into MFMA B registers, so W never touches LDS and
+// each weight is decoded once per workgroup.
+//
+// dX layout: 256 x BN outputs per workgroup of 4 waves (2 x 2). The reduction
+// runs over N, while the codes are K-contiguous, so each thread decodes one
+// row-block (64 weights) into an LDS tile [n][k], and the MFMA B operand is
+// read from it transposed with ds_read_b64_tr_b16 (gfx950): within a group of
+// 16 lanes, lane 4b + e receives element a of the 8-byte piece addressed by
+// lane 4a + b, which turns four 4-wide row pieces into four 4-tall columns.
+//
 // Workgroups are mapped XCD-aware: the hardware deals workgroups round-robin
 // to the 8 XCDs, so consecutive logical tiles (the M-tiles of one W tile) are
 // made to land on one XCD and share its L2.
+#include <type_traits>
+
 #include "ql_internal.h"
 
 namespace ql {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int NT = 256;
-constexpr int TILE_BYTES = 128 * 128;          // 128 rows x 64 bf16
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // A + B
-constexpr int LDS_BYTES = 2 * STAGE_BYTES + 64;  // two stages + level table
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ int swz(int row, int chunk) { return (row << 7) + ((chunk ^ (row & 7)) << 4); }
+constexpr int NT = 256;
+constexpr int BM = 256;
+constexpr int BK = 64;
+constexpr int A_TILE = BM * BK * 2;  // 32 KB: 256 rows x 128 B
+
+__device__ __forceinline__ int swz_a(int row, int chunk) { return (row << 7) + ((chunk ^ (row & 7)) << 4); }
 
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t n) {
   const uint32_t q = n >> 3, rem = n & 7;
@@ -38,91 +65,113 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t n) {
   return xcd * q + (xcd < rem ? xcd : rem) + local;
 }
 
-// logical column k of X -> physical column with the repeat_kv head remap
 __device__ __forceinline__ int64_t remap_col(int64_t k, int head_dim, int n_rep) {
   if (n_rep <= 0) return k;
   const int64_t head = k / head_dim, i = k - head * head_dim;
   return (head / n_rep) * head_dim + i;
 }
 
-// Decode 8 codes of one dword (element 2i in the high nibble of byte i) with a
-// float32 scale into 4 dwords of bf16 pairs, element order preserved.
-__device__ __forceinline__ uint4 decode8(uint32_t p, float sc, const float* lv) {
-  uint4 q;
-  q.x = pack_bf16x2(lv[(p >> 4) & 15u] * sc, lv[p & 15u] * sc);
-  q.y = pack_bf16x2(lv[(p >> 12) & 15u] * sc, lv[(p >> 8) & 15u] * sc);
-  q.z = pack_bf16x2(lv[(p >> 20) & 15u] * sc, lv[(p >> 16) & 15u] * sc);
-  q.w = pack_bf16x2(lv[(p >> 28) & 15u] * sc, lv[(p >> 24) & 15u] * sc);
-  return q;
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// The MFMA core: one K-step of 64 from LDS stage `st` into the 4 x 4 accumulators.
-__device__ __forceinline__ void mma_step(const uint8_t* st, f32x4_t (&acc)[4][4], int wm, int wn,
-                                         int lane) {
-  const uint8_t* As = st;
-  const uint8_t* Bs = st + TILE_BYTES;
+// 16-entry bf16 table of one row-block as two byte planes:
+// lo[q] = low bytes of entries 4q..4q+3, hi[q] = high bytes.
+struct Lut {
+  uint32_t lo[4], hi[4];
+};
+
+__device__ __forceinline__ Lut make_lut(float a) {
+  uint32_t d[8];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    bf16x8_t a[4], b[4];
-    const int ch = ks * 4 + (lane >> 4);
+  for (int i = 0; i < 8; ++i)
+    d[i] = pack_bf16x2(__builtin_bit_cast(float, kNF4LevelBits[2 * i]) * a,
+                       __builtin_bit_cast(float, kNF4LevelBits[2 * i + 1]) * a);
+  Lut t;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *(const bf16x8_t*)(As + swz(wm * 64 + i * 16 + (lane & 15), ch));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *(const bf16x8_t*)(Bs + swz(wn * 64 + j * 16 + (lane & 15), ch));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  for (int q = 0; q < 4; ++q) {
+    t.lo[q] = perm(d[2 * q + 1], d[2 * q], 0x06040200u);
+    t.hi[q] = perm(d[2 * q + 1], d[2 * q], 0x07050301u);
   }
+  return t;
 }
 
-// A operand rows (bf16, reduction-contiguous) of a main K-step: 4 chunks of
-// 16 B per thread. Rows at or past M are zero.
-__device__ __forceinline__ void load_a_main(uint4 (&ar)[4], const uint16_t* X, int64_t ldx, int64_t M,
-                                            int64_t m0, int64_t k0, int head_dim, int n_rep, int t) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = t + NT * i;
-    const int row = c >> 3, ch = c & 7;
-    const int64_t m = m0 + row;
-    if (m < M) {
-      const int64_t col = remap_col(k0 + ch * 8, head_dim, n_rep);
-      ar[i] = *(const uint4*)(X + m * ldx + col);
-    } else {
-      ar[i] = make_uint4(0, 0, 0, 0);
-    }
-  }
+// Four codes (one per byte, values 0..15, given as their low 3 bits `s3` and a
+// byte-select vector `blend` = 0x03020100 + 4 * bit3) -> byte plane of 4 values.
+__device__ __forceinline__ uint32_t plane4(const uint32_t (&tab)[4], uint32_t s3, uint32_t blend) {
+  const uint32_t r0 = perm(tab[1], tab[0], s3);  // entries 0..7
+  const uint32_t r1 = perm(tab[3], tab[2], s3);  // entries 8..15
+  return perm(r1, r0, blend);
 }
 
-// Same tile for a reduction-contiguous operand with a column limit (ncols % 16 == 0).
-__device__ __forceinline__ void load_a_lim(uint4 (&ar)[4], const uint16_t* X, int64_t ldx, int64_t M,
-                                           int64_t m0, int64_t k0, int64_t ncols, int t) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = t + NT * i;
-    const int row = c >> 3, ch = c & 7;
-    const int64_t m = m0 + row;
-    const int64_t k = k0 + ch * 8;
-    if (m < M && k < ncols)
-      ar[i] = *(const uint4*)(X + m * ldx + k);
-    else
-      ar[i] = make_uint4(0, 0, 0, 0);
-  }
+// One word of 8 codes (byte j: code j low nibble, code j+4 high nibble) ->
+// 8 bf16 in element order, as 4 dwords.
+__device__ __forceinline__ uint4 decode8(uint32_t p, const Lut& t) {
+  const uint32_t s3l = p & 0x07070707u;
+  const uint32_t bl = ((p >> 1) & 0x04040404u) | 0x03020100u;
+  const uint32_t s3h = (p >> 4) & 0x07070707u;
+  const uint32_t bh = ((p >> 5) & 0x04040404u) | 0x03020100u;
+  const uint32_t lo_l = plane4(t.lo, s3l, bl), hi_l = plane4(t.hi, s3l, bl);  // codes 0..3
+  const uint32_t lo_h = plane4(t.lo, s3h, bh), hi_h = plane4(t.hi, s3h, bh);  // codes 4..7
+  uint4 r;
+  r.x = perm(hi_l, lo_l, 0x05010400u);
+  r.y = perm(hi_l, lo_l, 0x07030602u);
+  r.z = perm(hi_h, lo_h, 0x05010400u);
+  r.w = perm(hi_h, lo_h, 0x07030602u);
+  return r;
 }
 
-// A operand of the LoRA step: rows of a [M x r] bf16 matrix, zero past r.
-__device__ __forceinline__ void load_a_rank(uint4 (&ar)[4], const uint16_t* U, int r, int64_t M,
-                                            int64_t m0, int t) {
+// Eight consecutive bf16 s * B[j] (j < r, zero past r) as 4 dwords.
+__device__ __forceinline__ uint4 lora_row8(const uint16_t* row, int j0, int r, float s) {
+  float f[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int e = 0; e < 8; ++e) f[e] = (j0 + e < r) ? s * bf16_to_f32(row[j0 + e]) : 0.f;
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+// Buffer resources: loads through a base in SGPRs and a 32-bit lane offset;
+// a raw buffer load at or past num_records returns zero, which masks the rows
+// past the end of a tile without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+// Buffer-to-LDS DMA (gfx950): each lane's 16 bytes land at lds + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// A tile (256 rows x 64 bf16) by DMA: wave w moves 1-KB blocks b = 4 i + w
+// (rows 8 b .. 8 b + 7); lane l fills row 8 b + l / 8 at physical chunk l % 8,
+// which holds logical chunk (l % 8) ^ (l / 8) under the row swizzle.
+__device__ __forceinline__ int dma_voff(int lane, int w, int ldx) {
+  const int row = 8 * w + (lane >> 3);
+  const int lc = (lane & 7) ^ (lane >> 3);
+  return row * ldx * 2 + lc * 16;
+}
+__device__ __forceinline__ void dma_a_tile(__amdgpu_buffer_rsrc_t r, uint8_t* As, int voff0, int ldx, int w, int soff) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dma16(r, As + (4 * i + w) * 1024, voff0 + i * 32 * ldx * 2, soff);
+}
+
+// A tile of the LoRA step: rows of a [M x r] bf16 matrix, zero past r (outside the main loop).
+__device__ __forceinline__ void load_a_rank(uint4 (&ar)[8], const uint16_t* U, int r, int64_t M, int64_t m0,
+                                            int t) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
     const int c = t + NT * i;
     const int row = c >> 3, ch = c & 7;
     const int64_t m = m0 + row;
     uint32_t w[4] = {0, 0, 0, 0};
-    if (m < M) {
+    if (m < M && ch * 8 < r) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = ch * 8 + e;
@@ -134,40 +183,31 @@ __device__ __forceinline__ void load_a_rank(uint4 (&ar)[4], const uint16_t* U, i
   }
 }
 
-__device__ __forceinline__ void store_a(uint8_t* As, const uint4 (&ar)[4], int t) {
+// Thread t moves chunks c = t + 256 i (i < 8) of a 256 x 64 A tile: row
+// (t >> 3) + 32 i, 16-byte chunk t & 7.
+__device__ __forceinline__ void store_a(uint8_t* As, const uint4 (&ar)[8], int t) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int c = t + NT * i;
-    *(uint4*)(As + swz(c >> 3, c & 7)) = ar[i];
+    *(uint4*)(As + swz_a(c >> 3, c & 7)) = ar[i];
   }
 }
 
-__device__ __forceinline__ void zero_acc(f32x4_t (&acc)[4][4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int q) {
+  return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
 }
 
-// Output of a 16x16 MFMA tile: lane l holds rows 4*(l/16)+v, v = 0..3, column l%16.
-template <typename F>
-__device__ __forceinline__ void for_each_out(const f32x4_t (&acc)[4][4], int wm, int wn, int lane, F f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        f(wm * 64 + i * 16 + 4 * (lane >> 4) + v, wn * 64 + j * 16 + (lane & 15), acc[i][j][v]);
-}
-
-// --------------------------------------------------------------- forward
-__global__ __launch_bounds__(NT, 2) void k_gemm_fwd(const FwdArgs a, int tiles_m, int tiles_total,
+// =============================================================== forward
+// WN: columns per wave (64 or 32); workgroup tile 256 x (4 WN).
+template <int WN>
+__global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m, int tiles_total,
                                                     int seg_tile0_1, int seg_tile0_2) {
+  constexpr int NTW = WN / 32;
+  constexpr int BN = 4 * WN;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  float* lv = (float*)(smem + 2 * STAGE_BYTES);
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
-  if (t < 16) lv[t] = __builtin_bit_cast(float, kNF4LevelBits[t]);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, li = lane & 31;
 
   const int tile = (int)xcd_remap(blockIdx.x, (uint32_t)tiles_total);
   const int sg = tile >= seg_tile0_2 ? 2 : (tile >= seg_tile0_1 ? 1 : 0);
@@ -175,222 +215,389 @@ __global__ __launch_bounds__(NT, 2) void k_gemm_fwd(const FwdArgs a, int tiles_m
   const FwdSeg& S = a.seg[sg];
   const int64_t m0 = (int64_t)(local % tiles_m) * BM;
   const int64_t n0 = (int64_t)(local / tiles_m) * BN;
-  const int64_t K = a.K, KT = K / BK;
-  const int64_t kb = K / 64;  // absmax per row
-  const int steps = (int)KT + 1;
+  const int64_t K = a.K, kb = K / 64, M = a.M, N = S.N;
+  const int KT = (int)(K / BK);
 
-  // B loader coordinates: one row, 32 codes (16 B) per thread
-  const int brow = t >> 1, bhalf = t & 1;
-  const int64_t bn = n0 + brow;
-  const bool bvalid = bn < S.N;
-
-  uint4 ar[4];
-  uint4 bcode;
-  float bsc;
-
-  auto load = [&](int step) {
-    if (step < KT) {
-      const int64_t k0 = (int64_t)step * BK;
-      load_a_main(ar, a.X, a.ldx, a.M, m0, k0, a.head_dim, a.n_rep, t);
-      if (bvalid) {
-        bcode = *(const uint4*)(S.packed + bn * (K / 2) + k0 / 2 + 16 * bhalf);
-        bsc = S.absmax[bn * kb + step];
-      } else {
-        bcode = make_uint4(0, 0, 0, 0);
-        bsc = 0.f;
-      }
-    } else {
-      load_a_rank(ar, S.U, a.r, a.M, m0, t);
-    }
-  };
-  auto store = [&](int step, uint8_t* st) {
-    store_a(st, ar, t);
-    uint8_t* Bs = st + TILE_BYTES;
-    if (step < KT) {
-      const uint32_t p[4] = {bcode.x, bcode.y, bcode.z, bcode.w};
+  // X tile rows m0.. (zero past M), W rows n0.. (zero past N)
+  const int64_t xrows = M - m0 < BM ? M - m0 : BM;
+  const int64_t wrows = N - n0 < BN ? N - n0 : BN;
+  const __amdgpu_buffer_rsrc_t xr = rsrc(a.X + m0 * a.ldx, xrows * a.ldx * 2);
+  const __amdgpu_buffer_rsrc_t cr = rsrc(S.packed + n0 * (K / 2), wrows * (K / 2));
+  const __amdgpu_buffer_rsrc_t sr = rsrc(S.absmax + n0 * kb, wrows * kb * 4);
+  const int xvoff = dma_voff(lane, w, (int)a.ldx);
+  int coff[NTW], soff[NTW];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) *(uint4*)(Bs + swz(brow, 4 * bhalf + d)) = decode8(p[d], bsc, lv);
-    } else {
-      // (s B)[n][j] for j < r, zero past r; 32 columns per thread
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint32_t wv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j0 = 32 * bhalf + 8 * d + 2 * e;
-          float f0 = 0.f, f1 = 0.f;
-          if (bvalid && j0 < a.r) f0 = a.s * bf16_to_f32(S.B[bn * a.r + j0]);
-          if (bvalid && j0 + 1 < a.r) f1 = a.s * bf16_to_f32(S.B[bn * a.r + j0 + 1]);
-          wv[e] = pack_bf16x2(f0, f1);
-        }
-        *(uint4*)(Bs + swz(brow, 4 * bhalf + d)) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-      }
-    }
+  for (int j = 0; j < NTW; ++j) {
+    const int row = w * WN + 32 * j + li;
+    coff[j] = row * (int)(K / 2) + 16 * g;
+    soff[j] = row * (int)kb * 4;
+  }
+  // column of X for K-step `step` (uniform): the repeat_kv remap keeps a
+  // 64-wide step inside one head
+  auto xcol = [&](int step) -> int {
+    const int64_t k0 = (int64_t)step * BK;
+    return (int)remap_col(k0, a.head_dim, a.n_rep) * 2;
   };
 
-  f32x4_t acc[4][4];
-  zero_acc(acc);
-  __syncthreads();  // level table visible
-  load(0);
-  store(0, smem);
+  uint4 bcur[NTW], bnxt[NTW];
+  float snxt[NTW];
+  Lut lut[NTW];
+
+  // global traffic of K-step `step`: B codes and scales into registers, the A tile into LDS
+  auto issue = [&](int step, uint8_t* As) {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      bnxt[j] = bload16(cr, coff[j], step * 32);
+      snxt[j] = bload4f(sr, soff[j], step * 4);
+    }
+    dma_a_tile(xr, As, xvoff, (int)a.ldx, w, xcol(step));
+  };
+
+  f32x16_t acc[8][NTW];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x16_t{};
+
+  auto decoded = [&](int j, int q) { return decode8(word(bcur[j], q), lut[j]); };
+  // next K-step's block tables: lanes g = 0 and 1 share rows, so each builds
+  // the table of one of its rows and takes the other from its partner
+  auto tables_next = [&]() {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) bcur[j] = bnxt[j];
+    if (NTW == 2) {
+      // g is per lane: choose with selects, not array indices
+      const Lut own = make_lut(g ? snxt[NTW - 1] : snxt[0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t olo = (uint32_t)__shfl_xor((int)own.lo[e], 32, 64);
+        const uint32_t ohi = (uint32_t)__shfl_xor((int)own.hi[e], 32, 64);
+        lut[0].lo[e] = g ? olo : own.lo[e];
+        lut[0].hi[e] = g ? ohi : own.hi[e];
+        lut[NTW - 1].lo[e] = g ? own.lo[e] : olo;
+        lut[NTW - 1].hi[e] = g ? own.hi[e] : ohi;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) lut[j] = make_lut(snxt[j]);
+    }
+  };
+
+  // One K-step of MFMAs on LDS stage As. Sub-step q's 16 MFMAs overlap the
+  // LDS reads and B decode of sub-step q + 1; in the last sub-step the next
+  // K-step's tables are built and its first B operands decoded. Scheduling
+  // groups pin the interleaving (LDS reads first, then MFMA / VALU alternating).
+  bf16x8_t af[8], an[8];
+  uint4 bq[NTW], bn[NTW];
+  auto mma_step = [&](const uint8_t* As, auto next_c) {
+    constexpr bool next = decltype(next_c)::value;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q < 3) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) an[i] = *(const bf16x8_t*)(As + swz_a(i * 32 + li, 4 * g + q + 1));
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) bn[j] = decoded(j, q + 1);
+      } else if constexpr (next) {
+        tables_next();
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) bn[j] = decoded(j, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], as_bf16x8(bq[j]), acc[i][j], 0, 0, 0);
+      if (q < 3) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int k = 0; k < 8 * NTW; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (q < 3) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) af[i] = an[i];
+      }
+      if (q < 3 || next) {
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) bq[j] = bn[j];
+      }
+    }
+  };
+
+  // prologue: K-step 0 into stage 0, its tables and first operands ready
+  issue(0, smem);
+  __builtin_amdgcn_s_waitcnt(0);
+  tables_next();
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) bq[j] = decoded(j, 0);
   __syncthreads();
-  for (int step = 0; step < steps; ++step) {
-    uint8_t* cur = smem + (step & 1) * STAGE_BYTES;
-    uint8_t* nxt = smem + ((step + 1) & 1) * STAGE_BYTES;
-    const bool more = step + 1 < steps;
-    if (more) load(step + 1);
-    mma_step(cur, acc, wm, wn, lane);
-    if (more) store(step + 1, nxt);
+  for (int step = 0; step + 1 < KT; ++step) {
+    const uint8_t* As = smem + (step & 1) * A_TILE;
+    uint8_t* An = smem + ((step + 1) & 1) * A_TILE;
+    issue(step + 1, An);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) af[i] = *(const bf16x8_t*)(As + swz_a(i * 32 + li, 4 * g));
+    mma_step(As, std::true_type{});
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA into the other stage has landed
     __syncthreads();
   }
-
-  // epilogue
-  const int64_t M = a.M, N = S.N;
-  for_each_out(acc, wm, wn, lane, [&](int r, int c, float v) {
-    const int64_t m = m0 + r, n = n0 + c;
-    if (m < M && n < N) {
-      const int64_t o = m * S.ldo + S.col0 + n;
-      if (S.resid) v += bf16_to_f32(S.resid[o]);
-      if (a.out_f32)
-        ((float*)S.out)[o] = v;
-      else
-        ((uint16_t*)S.out)[o] = f32_to_bf16(v);
+  {  // last weight step; the LoRA step's A tile (U) goes to the other stage
+    const uint8_t* As = smem + ((KT - 1) & 1) * A_TILE;
+    uint8_t* An = smem + (KT & 1) * A_TILE;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) af[i] = *(const bf16x8_t*)(As + swz_a(i * 32 + li, 4 * g));
+    mma_step(As, std::false_type{});
+    uint4 ar[8];
+    load_a_rank(ar, S.U, a.r, M, m0, t);
+    store_a(An, ar, t);
+    __syncthreads();
+  }
+  // LoRA step: [U | 0] [s B | 0]^T
+  {
+    uint4 lb[NTW][4];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int64_t n = n0 + w * WN + 32 * j + li;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        lb[j][q] = n < N ? lora_row8(S.B + n * a.r, 32 * g + 8 * q, a.r, a.s) : make_uint4(0, 0, 0, 0);
     }
-  });
+    const uint8_t* As = smem + (KT & 1) * A_TILE;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x8_t a8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a8[i] = *(const bf16x8_t*)(As + swz_a(i * 32 + li, 4 * g + q));
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8[i], as_bf16x8(lb[j][q]), acc[i][j], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int64_t n = n0 + w * WN + 32 * j + li;
+      if (n >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = m0 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (m < M) {
+          const int64_t o = m * S.ldo + S.col0 + n;
+          float val = acc[i][j][v];
+          if (S.resid) val += bf16_to_f32(S.resid[o]);
+          if (a.out_f32)
+            ((float*)S.out)[o] = val;
+          else
+            ((uint16_t*)S.out)[o] = f32_to_bf16(val);
+        }
+      }
+    }
 }
 
-// --------------------------------------------------------------- backward dX
-__global__ __launch_bounds__(NT, 2) void k_gemm_bwd(const BwdArgs a, int tiles_m, int tiles_total) {
+// =============================================================== backward dX
+// LDS B tile: [64 reduction rows n][BN output columns k] bf16, rows of 2 BN
+// bytes; the 16-B chunk index is XORed (low 3 bits) with f(n) so that both the
+// row-chunk writes and the transposed 4-row reads are bank-conflict free.
+__device__ __forceinline__ int swz_f(int n) { return ((n & 3) << 1) | ((n >> 2) & 1); }
+
+template <int BN>
+__device__ __forceinline__ int bt_off(int n, int k) {
+  const int chunk = k >> 3;
+  return n * (BN * 2) + ((chunk ^ swz_f(n)) << 4) + ((k & 4) << 1);
+}
+
+// WNB: output columns per wave (128 or 64); workgroup tile 256 x (2 WNB), waves 2 x 2.
+// Reduction order: for each segment its 64-row weight steps, then the LoRA
+// steps of all segments.
+template <int WNB>
+__global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m, int tiles_total) {
+  constexpr int BN = 2 * WNB;
+  constexpr int NTW = WNB / 32;
+  constexpr int B_TILE = 64 * BN * 2;
+  constexpr int STAGE = A_TILE + B_TILE;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  float* lv = (float*)(smem + 2 * STAGE_BYTES);
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
-  if (t < 16) lv[t] = __builtin_bit_cast(float, kNF4LevelBits[t]);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1, g = lane >> 5, li = lane & 31;
 
   const int tile = (int)xcd_remap(blockIdx.x, (uint32_t)tiles_total);
   const int64_t m0 = (int64_t)(tile % tiles_m) * BM;
-  const int64_t k0 = (int64_t)(tile / tiles_m) * BN;  // output columns (in-features)
-  const int64_t K = a.K, kb = K / 64;
+  const int64_t k0 = (int64_t)(tile / tiles_m) * BN;
+  const int64_t K = a.K, kbn = K / 64, M = a.M;
+  const int64_t xrows = M - m0 < BM ? M - m0 : BM;
 
-  // step enumeration: per segment ceil(N/64) weight steps then one LoRA step
-  const int ns0 = (int)((a.seg[0].N + BK - 1) / BK) + 1;
-  const int ns1 = a.nseg > 1 ? (int)((a.seg[1].N + BK - 1) / BK) + 1 : 0;
-  const int ns2 = a.nseg > 2 ? (int)((a.seg[2].N + BK - 1) / BK) + 1 : 0;
-  const int steps = ns0 + ns1 + ns2;
+  // weight steps per segment and their total
+  const int nw0 = (int)((a.seg[0].N + BK - 1) / BK);
+  const int nw1 = a.nseg > 1 ? (int)((a.seg[1].N + BK - 1) / BK) : 0;
+  const int nw2 = a.nseg > 2 ? (int)((a.seg[2].N + BK - 1) / BK) : 0;
+  const int WS = nw0 + nw1 + nw2;
 
-  // transposed-decode coordinates: 4 rows (n) x 8 columns (k) per thread
-  const int cg = t & 15, rg = t >> 4;
-  const int64_t kcol = k0 + 8 * cg;
-  const bool kvalid = kcol < K;
-  // LoRA-step B coordinates: one column k, 32 ranks
-  const int lk = t & 127, lhalf = t >> 7;
+  // decode coordinates: one row (reduction index) and one 64-wide block of output columns
+  constexpr int UNITS = 64 * (BN / 64);
+  const bool dthread = t < UNITS;
+  const int drow = t & 63, dblk = (t >> 6) % (BN / 64);
+  const int64_t dk = k0 + 64 * dblk;
+  const bool dkval = dthread && dk < K;
+  const int xoff = ((t >> 3) * 0 + (t & 7) * 8) * 2;  // column part; the row part depends on the segment
 
-  uint4 ar[4];
-  uint32_t bp[4];
-  float bs[4];
+  uint4 ar[8];
+  uint4 bc0, bc1;
+  float bsc;
 
-  // step -> (segment, index within it); the last index of a segment is its LoRA step
-  auto locate = [&](int step, int& sg, int& j, int& nst) {
-    if (step < ns0) { sg = 0; j = step; nst = ns0; }
-    else if (step < ns0 + ns1) { sg = 1; j = step - ns0; nst = ns1; }
-    else { sg = 2; j = step - ns0 - ns1; nst = ns2; }
+  // per weight step: segment, first reduction row
+  auto seg_of = [&](int step, int& sg, int64_t& nb) {
+    if (step < nw0) { sg = 0; nb = (int64_t)step * BK; }
+    else if (step < nw0 + nw1) { sg = 1; nb = (int64_t)(step - nw0) * BK; }
+    else { sg = 2; nb = (int64_t)(step - nw0 - nw1) * BK; }
   };
-  auto load = [&](int step) {
-    int sg, j, nst;
-    locate(step, sg, j, nst);
+  auto issue = [&](int step) {
+    int sg;
+    int64_t nb;
+    seg_of(step, sg, nb);
     const BwdSeg& S = a.seg[sg];
-    if (j < nst - 1) {
-      const int64_t n0 = (int64_t)j * BK;
-      load_a_lim(ar, S.dY, S.N, a.M, m0, n0, S.N, t);
+    const int ldy = (int)S.N;
+    const __amdgpu_buffer_rsrc_t yr = rsrc(S.dY + m0 * S.N, xrows * S.N * 2);
+    const int kmax = (int)(S.N - nb);  // columns of dY left in this segment
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t n = n0 + 4 * rg + i;
-        if (n < S.N && kvalid) {
-          bp[i] = *(const uint32_t*)(S.packed + n * (K / 2) + kcol / 2);
-          bs[i] = S.absmax[n * kb + kcol / 64];
-        } else {
-          bp[i] = 0;
-          bs[i] = 0.f;
-        }
-      }
-    } else {
-      load_a_rank(ar, S.G, a.r, a.M, m0, t);
+    for (int i = 0; i < 8; ++i) {
+      const int row = (t >> 3) + 32 * i;
+      const uint4 v = bload16(yr, (row * ldy) * 2 + xoff, (int)nb * 2);
+      ar[i] = ((t & 7) * 8 < kmax) ? v : make_uint4(0, 0, 0, 0);
+    }
+    const int64_t nrows = S.N - nb < BK ? S.N - nb : BK;
+    const __amdgpu_buffer_rsrc_t cr = rsrc(S.packed + nb * (K / 2), nrows * (K / 2));
+    const __amdgpu_buffer_rsrc_t sr = rsrc(S.absmax + nb * kbn, nrows * kbn * 4);
+    const int co = drow * (int)(K / 2) + (int)(dk / 2);
+    bc0 = bload16(cr, co, 0);
+    bc1 = bload16(cr, co + 16, 0);
+    bsc = bload4f(sr, (drow * (int)kbn + (int)(dk / 64)) * 4, 0);
+    if (!dkval) {
+      bc0 = bc1 = make_uint4(0, 0, 0, 0);
+      bsc = 0.f;
     }
   };
-  auto store = [&](int step, uint8_t* st) {
-    int sg, j, nst;
-    locate(step, sg, j, nst);
-    const BwdSeg& S = a.seg[sg];
-    store_a(st, ar, t);
-    uint8_t* Bs = st + TILE_BYTES;
-    if (j < nst - 1) {
-      // element e of the dword: byte e/2, high nibble when e is even
+  auto store_b = [&](uint8_t* Bs) {
+    const Lut lut = make_lut(bsc);
+    const uint32_t p[8] = {bc0.x, bc0.y, bc0.z, bc0.w, bc1.x, bc1.y, bc1.z, bc1.w};
+    if (dthread) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = 8 * (e >> 1) + ((e & 1) ? 0 : 4);
-        const float f0 = lv[(bp[0] >> sh) & 15u] * bs[0];
-        const float f1 = lv[(bp[1] >> sh) & 15u] * bs[1];
-        const float f2 = lv[(bp[2] >> sh) & 15u] * bs[2];
-        const float f3 = lv[(bp[3] >> sh) & 15u] * bs[3];
-        const int kr = 8 * cg + e;
-        uint2 v;
-        v.x = pack_bf16x2(f0, f1);
-        v.y = pack_bf16x2(f2, f3);
-        *(uint2*)(Bs + (kr << 7) + ((((rg >> 1) ^ (kr & 7))) << 4) + ((rg & 1) << 3)) = v;
-      }
-    } else {
-      // (s A)^T: row k of the tile holds s * A[j][k] for j < r
-      const int64_t k = k0 + lk;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint32_t wv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int jj = 32 * lhalf + 8 * d + 2 * e;
-          float f0 = 0.f, f1 = 0.f;
-          if (k < K && jj < a.r) f0 = a.s * bf16_to_f32(S.A[(int64_t)jj * K + k]);
-          if (k < K && jj + 1 < a.r) f1 = a.s * bf16_to_f32(S.A[(int64_t)(jj + 1) * K + k]);
-          wv[e] = pack_bf16x2(f0, f1);
-        }
-        *(uint4*)(Bs + swz(lk, 4 * lhalf + d)) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-      }
+      for (int c = 0; c < 8; ++c) *(uint4*)(Bs + bt_off<BN>(drow, 64 * dblk + 8 * c)) = decode8(p[c], lut);
     }
   };
 
-  f32x4_t acc[4][4];
-  zero_acc(acc);
+  f32x16_t acc[4][NTW];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x16_t{};
+
+  // transposed-read coordinates: within each group of 16 lanes, lane 4 ra + cbq
+  // addresses row ra (of four) and the 4-column piece cbq (of four)
+  const int h = lane >> 4, s16 = lane & 15, ra = s16 >> 2, cbq = s16 & 3;
+  auto mma_step = [&](const uint8_t* st) {
+    const uint8_t* As = st;
+    const uint8_t* Bs = st + A_TILE;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x8_t af[4], bf[NTW];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8_t*)(As + swz_a(wm * 128 + i * 32 + li, 2 * q + g));
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        // lanes 32 g + c (c < 32) need column c and reduction rows 16 q + 8 g .. + 8
+        const int col = wn * WNB + 32 * j + 16 * (h & 1) + 4 * cbq;
+        const int row = 16 * q + 8 * (h >> 1) + ra;
+        const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(Bs + bt_off<BN>(row, col)));
+        const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(Bs + bt_off<BN>(row + 4, col)));
+        const i16x8_t v = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        bf[j] = __builtin_bit_cast(bf16x8_t, v);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // weight steps: stage s & 1 holds step s; step s + 1 is in registers while s computes
+  issue(0);
+  store_a(smem, ar, t);
+  store_b(smem + A_TILE);
+  if (WS > 1) issue(1);
   __syncthreads();
-  load(0);
-  store(0, smem);
-  __syncthreads();
-  for (int step = 0; step < steps; ++step) {
-    uint8_t* cur = smem + (step & 1) * STAGE_BYTES;
-    uint8_t* nxt = smem + ((step + 1) & 1) * STAGE_BYTES;
-    const bool more = step + 1 < steps;
-    if (more) load(step + 1);
-    mma_step(cur, acc, wm, wn, lane);
-    if (more) store(step + 1, nxt);
+  for (int step = 0; step < WS; ++step) {
+    uint8_t* nx = smem + ((step + 1) & 1) * STAGE;
+    mma_step(smem + (step & 1) * STAGE);
+    if (step + 1 < WS) {
+      store_a(nx, ar, t);
+      store_b(nx + A_TILE);
+      if (step + 2 < WS) issue(step + 2);
+    }
     __syncthreads();
   }
-
-  const int64_t M = a.M;
-  for_each_out(acc, wm, wn, lane, [&](int r, int c, float v) {
-    const int64_t m = m0 + r, k = k0 + c;
-    if (m < M && k < K) {
-      const int64_t o = m * K + k;
-      if (a.resid) v += bf16_to_f32(a.resid[o]);
-      if (a.out_f32)
-        ((float*)a.out)[o] = v;
-      else
-        ((uint16_t*)a.out)[o] = f32_to_bf16(v);
+  // LoRA steps: A = G_s, B rows j < r = s A_s[j][k0 ..], zero past r
+  for (int sg = 0; sg < a.nseg; ++sg) {
+    const BwdSeg& S = a.seg[sg];
+    uint8_t* st = smem + ((WS + sg) & 1) * STAGE;
+    load_a_rank(ar, S.G, a.r, M, m0, t);
+    store_a(st, ar, t);
+    if (dthread) {
+      const bool live = drow < a.r && dk < K;
+      const uint4* src = (const uint4*)(S.A + (int64_t)drow * K + dk);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint4 lv4 = live ? src[c] : make_uint4(0, 0, 0, 0);
+        const uint32_t wv[4] = {lv4.x, lv4.y, lv4.z, lv4.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = pack_bf16x2(a.s * __builtin_bit_cast(float, wv[e] << 16),
+                             a.s * __builtin_bit_cast(float, wv[e] & 0xffff0000u));
+        *(uint4*)(st + A_TILE + bt_off<BN>(drow, 64 * dblk + 8 * c)) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
     }
-  });
+    __syncthreads();
+    mma_step(st);
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int64_t k = k0 + wn * WNB + 32 * j + li;
+      if (k >= K) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (m < M) {
+          const int64_t o = m * K + k;
+          float val = acc[i][j][v];
+          if (a.resid) val += bf16_to_f32(a.resid[o]);
+          if (a.out_f32)
+            ((float*)a.out)[o] = val;
+          else
+            ((uint16_t*)a.out)[o] = f32_to_bf16(val);
+        }
+      }
+    }
 }
 
-#define QL_TRY_PROF(expr)        \
-  do {                           \
-    ql_status rc_ = (expr);      \
+#define QL_TRY_PROF(expr)         \
+  do {                            \
+    ql_status rc_ = (expr);       \
     if (rc_ != QL_OK) return rc_; \
   } while (0)
+
+constexpr int FWD_LDS = 2 * A_TILE;
+template <int BN>
+constexpr int bwd_lds() { return 2 * (A_TILE + 64 * BN * 2); }
 
 bool g_attr_set[64] = {};
 
@@ -398,34 +605,60 @@ ql_status ensure_attrs() {
   int dev = 0;
   QL_HIP_CHECK(hipGetDevice(&dev));
   if (dev >= 0 && dev < 64 && !g_attr_set[dev]) {
-    QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_fwd,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES));
-    QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_bwd,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES));
+    QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_fwd<64>, hipFuncAttributeMaxDynamicSharedMemorySize, FWD_LDS));
+    QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_fwd<32>, hipFuncAttributeMaxDynamicSharedMemorySize, FWD_LDS));
+    QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_bwd<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     bwd_lds<256>()));
+    QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_bwd<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     bwd_lds<128>()));
     g_attr_set[dev] = true;
   }
   return QL_OK;
 }
 
+int cu_count() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
 }  // namespace
 
+// Tile width: the wide tile (256 columns) unless it leaves CUs idle in the
+// first wave of workgroups and the narrow one does not. The choice depends on
+// shapes only, so resident and streamed runs pick the same kernels.
 ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st) {
   if (a.M == 0) return QL_OK;
-  ql_status rc = ensure_attrs();
-  if (rc != QL_OK) return rc;
+  QL_TRY_PROF(ensure_attrs());
   const int tiles_m = (int)((a.M + BM - 1) / BM);
-  int start[kMaxSegs + 1] = {0, 0, 0, 0};
-  for (int s = 0; s < a.nseg; ++s) start[s + 1] = start[s] + tiles_m * (int)((a.seg[s].N + BN - 1) / BN);
-  for (int s = a.nseg; s < kMaxSegs; ++s) start[s + 1] = start[s];
-  const int total = start[a.nseg];
+  auto count = [&](int bn, int* start) {
+    start[0] = 0;
+    for (int s = 0; s < kMaxSegs; ++s)
+      start[s + 1] = start[s] + (s < a.nseg ? tiles_m * (int)((a.seg[s].N + bn - 1) / bn) : 0);
+    return start[a.nseg];
+  };
+  int st256[kMaxSegs + 1], st128[kMaxSegs + 1];
+  const int t256 = count(256, st256), t128 = count(128, st128);
+  const bool wide = t256 >= cu_count() || t128 <= t256;
+  const int* start = wide ? st256 : st128;
+  const int total = wide ? t256 : t128;
   if (total == 0) return QL_OK;
-  // unused segment starts point past the end so no tile maps to them
   const int s1 = a.nseg > 1 ? start[1] : total + 1;
   const int s2 = a.nseg > 2 ? start[2] : total + 1;
   void* tok = nullptr;
   const bool prof = profiling_on();
   if (prof) QL_TRY_PROF(profile_begin(st, &tok));
-  hipLaunchKernelGGL(k_gemm_fwd, dim3(total), dim3(NT), LDS_BYTES, st, a, tiles_m, total, s1, s2);
+  if (wide)
+    hipLaunchKernelGGL(k_gemm_fwd<64>, dim3(total), dim3(NT), FWD_LDS, st, a, tiles_m, total, s1, s2);
+  else
+    hipLaunchKernelGGL(k_gemm_fwd<32>, dim3(total), dim3(NT), FWD_LDS, st, a, tiles_m, total, s1, s2);
   QL_HIP_CHECK(hipGetLastError());
   if (prof) {
     double flop = 0;
@@ -437,15 +670,20 @@ ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st) {
 
 ql_status launch_gemm_bwd(const BwdArgs& a, hipStream_t st) {
   if (a.M == 0) return QL_OK;
-  ql_status rc = ensure_attrs();
-  if (rc != QL_OK) return rc;
+  QL_TRY_PROF(ensure_attrs());
   const int tiles_m = (int)((a.M + BM - 1) / BM);
-  const int total = tiles_m * (int)((a.K + BN - 1) / BN);
+  const int t256 = tiles_m * (int)((a.K + 255) / 256);
+  const int t128 = tiles_m * (int)((a.K + 127) / 128);
+  const bool wide = t256 >= cu_count() || t128 <= t256;
+  const int total = wide ? t256 : t128;
   if (total == 0) return QL_OK;
   void* tok = nullptr;
   const bool prof = profiling_on();
   if (prof) QL_TRY_PROF(profile_begin(st, &tok));
-  hipLaunchKernelGGL(k_gemm_bwd, dim3(total), dim3(NT), LDS_BYTES, st, a, tiles_m, total);
+  if (wide)
+    hipLaunchKernelGGL(k_gemm_bwd<128>, dim3(total), dim3(NT), bwd_lds<256>(), st, a, tiles_m, total);
+  else
+    hipLaunchKernelGGL(k_gemm_bwd<64>, dim3(total), dim3(NT), bwd_lds<128>(), st, a, tiles_m, total);
   QL_HIP_CHECK(hipGetLastError());
   if (prof) {
     double flop = 0;

@@ -19,7 +19,9 @@ reading taken here:
   (IEEE correctly rounded division); code = index of the nearest codebook
   value, ties to the lower index; a block of zeros gets code 7 (the exact
   zero) and absmax 0; non-finite input is refused.
-* packing: byte i holds element 2i in its high nibble, 2i+1 in its low nibble.
+* packing: 8 consecutive codes per 32-bit little-endian word (bytes 4w..4w+3
+  hold elements 8w..8w+7); byte j of the word holds element 8w+j in its low
+  nibble and element 8w+j+4 in its high nibble.
 * dequant: w_hat = fl32(c[code] * absmax) (one float32 multiply); the bf16
   form is that value rounded to nearest even.
 """
@@ -102,19 +104,24 @@ def quantize(w, codes_out=False):
 
 
 def pack(codes) -> np.ndarray:
-    """Two 4-bit codes per byte: element 2i in the high nibble, 2i+1 in the low nibble."""
+    """Two 4-bit codes per byte, in words of 8 codes: within each group of 8
+    consecutive codes c0..c7 (4 bytes), byte j = c_j | (c_{j+4} << 4)."""
     codes = np.asarray(codes, np.uint8).reshape(-1)
-    if codes.size % 2:
-        raise ValueError("pack: odd number of codes")
-    return ((codes[0::2] << 4) | (codes[1::2] & 0xF)).astype(np.uint8)
+    if codes.size % 8:
+        raise ValueError("pack: code count must be a multiple of 8")
+    g = codes.reshape(-1, 8)
+    return ((g[:, :4] & 0xF) | (g[:, 4:] << 4)).astype(np.uint8).reshape(-1)
 
 
 def unpack(packed) -> np.ndarray:
     packed = np.asarray(packed, np.uint8).reshape(-1)
-    out = np.empty(packed.size * 2, np.uint8)
-    out[0::2] = packed >> 4
-    out[1::2] = packed & 0xF
-    return out
+    if packed.size % 4:
+        raise ValueError("unpack: byte count must be a multiple of 4")
+    b = packed.reshape(-1, 4)
+    out = np.empty((b.shape[0], 8), np.uint8)
+    out[:, :4] = b & 0xF
+    out[:, 4:] = b >> 4
+    return out.reshape(-1)
 
 
 def dequant_f32(packed, absmax) -> np.ndarray:
@@ -182,11 +189,13 @@ def dequant_rows_bf16(packed, absmax, K, rows) -> np.ndarray:
 def dequant_cols_bf16(packed, absmax, N, K, cols) -> np.ndarray:
     """Columns `cols` of the bf16 dequantised [N x K] weight, as float64 [N x len(cols)].
 
-    Element (n, k) is nibble k of row n: byte k // 2, high nibble when k is even.
+    Element (n, k): word k // 8 of row n, byte (k % 8) % 4 of it, low nibble
+    when k % 8 < 4, high nibble otherwise.
     """
     cols = np.asarray(cols)
-    p = np.asarray(packed, np.uint8).reshape(N, K // 2)[:, cols // 2]
-    codes = np.where(cols % 2 == 0, p >> 4, p & 15)
+    byte = (cols // 8) * 4 + (cols % 8) % 4
+    p = np.asarray(packed, np.uint8).reshape(N, K // 2)[:, byte]
+    codes = np.where(cols % 8 < 4, p & 15, p >> 4)
     a = np.asarray(absmax, np.float32).reshape(N, K // BLOCK)[:, cols // BLOCK]
     w32 = (codebook()[codes] * a).astype(np.float32)
     return round_bf16(w32.astype(np.float64))

@@ -167,10 +167,14 @@ def test_nonfinite_refused():
 
 
 def test_pack_nibble_order_and_all_bytes():
-    assert nf4.pack([1, 2]).tolist() == [0x12]
-    assert nf4.unpack(np.array([0xA5], np.uint8)).tolist() == [0xA, 0x5]
+    # codes 0..7 -> bytes (c0 | c4 << 4, c1 | c5 << 4, c2 | c6 << 4, c3 | c7 << 4)
+    assert nf4.pack(list(range(8))).tolist() == [0x40, 0x51, 0x62, 0x73]
+    assert nf4.pack([1, 2, 3, 4, 5, 6, 7, 8]).view(np.uint32).tolist() == [0x84736251]
+    assert nf4.unpack(np.array([0xA5, 0, 0, 0x3C], np.uint8)).tolist() == [5, 0, 0, 0xC, 0xA, 0, 0, 3]
     allb = np.arange(256, dtype=np.uint8)
     assert np.array_equal(nf4.pack(nf4.unpack(allb)), allb)
+    codes = np.random.default_rng(0).integers(0, 16, 4096).astype(np.uint8)
+    assert np.array_equal(nf4.unpack(nf4.pack(codes)), codes)
 
 
 def test_quantisation_error_bound():
