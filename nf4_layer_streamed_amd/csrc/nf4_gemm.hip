@@ -51,6 +51,7 @@ namespace {
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;
 constexpr int BM = 256;
@@ -124,8 +125,18 @@ __device__ __forceinline__ uint4 decode8(uint32_t p, const Lut& t) {
 // Eight consecutive bf16 s * B[j] (j < r, zero past r) as 4 dwords.
 __device__ __forceinline__ uint4 lora_row8(const uint16_t* row, int j0, int r, float s) {
   float f[8];
+  if ((r & 7) == 0) {  // 16-byte aligned groups of 8
+    uint4 v = j0 < r ? *(const uint4*)(row + j0) : make_uint4(0, 0, 0, 0);
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = (j0 + e < r) ? s * bf16_to_f32(row[j0 + e]) : 0.f;
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = s * __builtin_bit_cast(float, wv[e] << 16);
+      f[2 * e + 1] = s * __builtin_bit_cast(float, wv[e] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (j0 + e < r) ? s * bf16_to_f32(row[j0 + e]) : 0.f;
+  }
   return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
                     pack_bf16x2(f[6], f[7]));
 }
@@ -133,9 +144,14 @@ __device__ __forceinline__ uint4 lora_row8(const uint16_t* row, int j0, int r, f
 // Buffer resources: loads through a base in SGPRs and a 32-bit lane offset;
 // a raw buffer load at or past num_records returns zero, which masks the rows
 // past the end of a tile without branches.
+// Base and size are made provably wave-uniform so the descriptor lives in SGPRs.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
   const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+  const uint64_t p = (uint64_t)base;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)n), 0x00020000);
 }
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
@@ -172,11 +188,16 @@ __device__ __forceinline__ void load_a_rank(uint4 (&ar)[8], const uint16_t* U, i
     const int64_t m = m0 + row;
     uint32_t w[4] = {0, 0, 0, 0};
     if (m < M && ch * 8 < r) {
+      if ((r & 7) == 0) {  // 16-byte aligned groups of 8
+        const uint4 v = *(const uint4*)(U + m * r + ch * 8);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = ch * 8 + e;
-        const uint32_t h = j < r ? (uint32_t)U[m * r + j] : 0u;
-        w[e >> 1] |= h << ((e & 1) * 16);
+        for (int e = 0; e < 8; ++e) {
+          const int j = ch * 8 + e;
+          const uint32_t h = j < r ? (uint32_t)U[m * r + j] : 0u;
+          w[e >> 1] |= h << ((e & 1) * 16);
+        }
       }
     }
     ar[i] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -200,14 +221,44 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int q) {
 }
 
 // =============================================================== forward
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]); only vmcnt is limited here.
+// vmcnt(n) together with lgkmcnt(0). The K-loop's barriers use explicit waits
+// rather than __syncthreads, whose release fence would also wait for the
+// A-tile DMA issued two steps ahead (DMA writes to LDS count in vmcnt).
+constexpr int vm_lgkm_wait(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
+
+constexpr int FWD_STAGES = 3;
+// One forward LDS stage: the X tile (256 rows x 128 B, swizzled), the codes of
+// the workgroup's BN weight rows for one K-step (BN rows x 32 B) and their
+// absmax (256 floats; rows past BN are loaded as zeros and never read).
+template <int BN>
+constexpr int fwd_stage_bytes() { return A_TILE + BN * 32 + 1024; }
+
+// DMA of 4-byte elements: lane l's word lands at lds + 4 * l.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
+}
+
 // WN: columns per wave (64 or 32); workgroup tile 256 x (4 WN).
+// Every global read of the K-loop is a buffer-to-LDS DMA issued two K-steps
+// ahead into a three-stage ring: while step s computes from stage s mod 3,
+// step s + 2's X tile, codes and scales stream into stage (s + 2) mod 3. A
+// barrier between sub-steps 2 and 3 of step s certifies step s + 1's data
+// (each wave first waits for its own DMAs of it) and that no wave still reads
+// stage s mod 3's neighbour that is refilled next.
 template <int WN>
 __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m, int tiles_total,
                                                     int seg_tile0_1, int seg_tile0_2) {
   constexpr int NTW = WN / 32;
   constexpr int BN = 4 * WN;
+  constexpr int STAGE = fwd_stage_bytes<BN>();
+  constexpr int CODES = A_TILE, SCALES = A_TILE + BN * 32;
+  // DMA instructions per wave per K-step: 8 for X, BN / 128 for codes, 1 for scales
+  constexpr int NDMA = 8 + BN / 128 + 1;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, li = lane & 31;
+  const int t = threadIdx.x, lane = t & 63, g = lane >> 5, li = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
 
   const int tile = (int)xcd_remap(blockIdx.x, (uint32_t)tiles_total);
   const int sg = tile >= seg_tile0_2 ? 2 : (tile >= seg_tile0_1 ? 1 : 0);
@@ -224,33 +275,52 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
   const __amdgpu_buffer_rsrc_t xr = rsrc(a.X + m0 * a.ldx, xrows * a.ldx * 2);
   const __amdgpu_buffer_rsrc_t cr = rsrc(S.packed + n0 * (K / 2), wrows * (K / 2));
   const __amdgpu_buffer_rsrc_t sr = rsrc(S.absmax + n0 * kb, wrows * kb * 4);
-  const int xvoff = dma_voff(lane, w, (int)a.ldx);
-  int coff[NTW], soff[NTW];
-#pragma unroll
-  for (int j = 0; j < NTW; ++j) {
-    const int row = w * WN + 32 * j + li;
-    coff[j] = row * (int)(K / 2) + 16 * g;
-    soff[j] = row * (int)kb * 4;
-  }
-  // column of X for K-step `step` (uniform): the repeat_kv remap keeps a
-  // 64-wide step inside one head
-  auto xcol = [&](int step) -> int {
-    const int64_t k0 = (int64_t)step * BK;
-    return (int)remap_col(k0, a.head_dim, a.n_rep) * 2;
+  const int ldx = __builtin_amdgcn_readfirstlane((int)a.ldx);
+  const int xvoff = dma_voff(lane, w, ldx);
+  // codes: DMA instruction c moves rows 32 c .. 32 c + 31 (lane l: row 32 c + l / 2,
+  // bytes 16 (l % 2) ..), landing contiguously at CODES + 1024 c
+  const int cvoff = (lane >> 1) * (int)(K / 2) + 16 * (lane & 1);
+  // scales: wave w moves rows 64 w + lane, landing at SCALES + 256 w
+  const int svoff = (64 * w + lane) * (int)kb * 4;
+
+  // Byte column of X for the K-step whose A tile is DMAed next (uniform). The
+  // repeat_kv remap keeps a 64-wide step inside one head: step k0 = 64 t reads
+  // column (head / n_rep) * head_dim + (k0 mod head_dim), head = k0 / head_dim.
+  // Kept as running counters (ci: column in head, hr: head mod n_rep, hq:
+  // head / n_rep) so the loop has no divisions or branches.
+  const int hd = a.n_rep > 0 ? a.head_dim : (1 << 30);
+  const int nrep = a.n_rep > 0 ? a.n_rep : 1;
+  int ci = 0, hr = 0, hq = 0;
+  auto xcol_next = [&]() -> int {
+    const int c = 2 * (hq * hd + ci);
+    ci += BK;
+    const bool wrap = ci >= hd;
+    ci = wrap ? 0 : ci;
+    hr += wrap ? 1 : 0;
+    const bool wrap2 = hr >= nrep;
+    hr = wrap2 ? 0 : hr;
+    hq += wrap2 ? 1 : 0;
+    return c;
   };
+  auto stage = [&](int s) -> uint8_t* { return smem + (s % FWD_STAGES) * STAGE; };
 
-  uint4 bcur[NTW], bnxt[NTW];
-  float snxt[NTW];
-  Lut lut[NTW];
-
-  // global traffic of K-step `step`: B codes and scales into registers, the A tile into LDS
-  auto issue = [&](int step, uint8_t* As) {
+  // DMA part h (0 or 1) of K-step `step` into its stage: half of the X tile
+  // (1-KB blocks 4 i + w, i in [4 h, 4 h + 4)); part 0 also moves the codes
+  // and scales. Steps are DMAed in order.
+  int sc = 0;
+  auto dma_part = [&](int step, int h) {
+    uint8_t* st = stage(step);
+    if (h == 0) sc = xcol_next();
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      bnxt[j] = bload16(cr, coff[j], step * 32);
-      snxt[j] = bload4f(sr, soff[j], step * 4);
+    for (int i = 4 * h; i < 4 * h + 4; ++i) dma16(xr, st + (4 * i + w) * 1024, xvoff + i * 32 * ldx * 2, sc);
+    if (h == 0) {
+#pragma unroll
+      for (int cc = 0; cc < BN / 128; ++cc) {
+        const int c = w + 4 * cc;
+        dma16(cr, st + CODES + 1024 * c, cvoff + 32 * c * (int)(K / 2), step * 32);
+      }
+      dma4(sr, st + SCALES + 256 * w, svoff, step * 4);
     }
-    dma_a_tile(xr, As, xvoff, (int)a.ldx, w, xcol(step));
   };
 
   f32x16_t acc[8][NTW];
@@ -259,47 +329,73 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[i][j] = f32x16_t{};
 
+  uint4 bcur[NTW];
+  Lut lut[NTW];
+  const int code_lane = CODES + (w * WN + li) * 32 + 16 * g;
   auto decoded = [&](int j, int q) { return decode8(word(bcur[j], q), lut[j]); };
-  // next K-step's block tables: lanes g = 0 and 1 share rows, so each builds
-  // the table of one of its rows and takes the other from its partner
-  auto tables_next = [&]() {
+  // Codes and block tables of the K-step in stage st. (All LDS reads of the
+  // K-loop are typed loads; ordering against the DMAs is carried by the
+  // explicit waits before each barrier.) Lane (li, g) takes the
+  // 16 code bytes 16 g.. of rows w WN + 32 j + li. With two row groups the
+  // lanes g = 0 and 1 hold the same rows, so each builds the table of one
+  // (row group g) and the halves swap them (v_permlane32_swap: lanes 32..63 of
+  // the first operand trade places with lanes 0..31 of the second).
+  auto tables = [&](const uint8_t* st) {
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) bcur[j] = bnxt[j];
-    if (NTW == 2) {
-      // g is per lane: choose with selects, not array indices
-      const Lut own = make_lut(g ? snxt[NTW - 1] : snxt[0]);
+    for (int j = 0; j < NTW; ++j) {
+      const u32x4_t v = *(const u32x4_t*)(st + code_lane + 1024 * j);
+      bcur[j] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    if constexpr (NTW == 2) {
+      const float sc_own = *(const float*)(st + SCALES + 4 * (w * WN + 32 * g + li));
+      const Lut own = make_lut(sc_own);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t olo = (uint32_t)__shfl_xor((int)own.lo[e], 32, 64);
-        const uint32_t ohi = (uint32_t)__shfl_xor((int)own.hi[e], 32, 64);
-        lut[0].lo[e] = g ? olo : own.lo[e];
-        lut[0].hi[e] = g ? ohi : own.hi[e];
-        lut[NTW - 1].lo[e] = g ? own.lo[e] : olo;
-        lut[NTW - 1].hi[e] = g ? own.hi[e] : ohi;
+        const auto xl = __builtin_amdgcn_permlane32_swap(own.lo[e], own.lo[e], false, false);
+        const auto xh = __builtin_amdgcn_permlane32_swap(own.hi[e], own.hi[e], false, false);
+        lut[0].lo[e] = xl[0];
+        lut[1].lo[e] = xl[1];
+        lut[0].hi[e] = xh[0];
+        lut[1].hi[e] = xh[1];
       }
     } else {
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) lut[j] = make_lut(snxt[j]);
+      lut[0] = make_lut(*(const float*)(st + SCALES + 4 * (w * WN + li)));
     }
   };
 
-  // One K-step of MFMAs on LDS stage As. Sub-step q's 16 MFMAs overlap the
-  // LDS reads and B decode of sub-step q + 1; in the last sub-step the next
-  // K-step's tables are built and its first B operands decoded. Scheduling
-  // groups pin the interleaving (LDS reads first, then MFMA / VALU alternating).
+  // One K-step of MFMAs on the stage of `step`. Sub-step q's MFMAs overlap the
+  // LDS reads and B decode of sub-step q + 1. HAS_NEXT: between sub-steps 2
+  // and 3 the workgroup meets at a barrier (every wave's reads of this stage
+  // done, its DMAs of step + 1 landed), after which sub-step 3 prefetches step
+  // + 1's first A fragments, codes and tables, so the next step starts without
+  // waiting. DMA: step + 2's data is issued in sub-steps 0 and 1 into the stage
+  // read last in step - 1. Scheduling groups pin the interleaving (LDS reads
+  // first, then MFMA / VMEM / VALU alternating).
   bf16x8_t af[8], an[8];
   uint4 bq[NTW], bn[NTW];
-  auto mma_step = [&](const uint8_t* As, auto next_c) {
-    constexpr bool next = decltype(next_c)::value;
+  auto read_a = [&](bf16x8_t (&dst)[8], const uint8_t* As, int q) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = *(const bf16x8_t*)(As + swz_a(i * 32 + li, 4 * g + q));
+  };
+  auto mma_step = [&](int step, auto has_next_c, auto dma_c) {
+    constexpr bool has_next = decltype(has_next_c)::value;
+    constexpr bool dma = decltype(dma_c)::value;
+    const uint8_t* As = stage(step);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      int nvm = 0;
+      if (dma && q < 2) {
+        dma_part(step + 2, q);
+        nvm = q == 0 ? NDMA - 4 : 4;
+      }
       if (q < 3) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) an[i] = *(const bf16x8_t*)(As + swz_a(i * 32 + li, 4 * g + q + 1));
+        read_a(an, As, q + 1);
 #pragma unroll
         for (int j = 0; j < NTW; ++j) bn[j] = decoded(j, q + 1);
-      } else if constexpr (next) {
-        tables_next();
+      } else if constexpr (has_next) {
+        const uint8_t* nx = stage(step + 1);
+        read_a(an, nx, 0);
+        tables(nx);
 #pragma unroll
         for (int j = 0; j < NTW; ++j) bn[j] = decoded(j, 0);
       }
@@ -307,51 +403,60 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], as_bf16x8(bq[j]), acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(bq[j]), af[i], acc[i][j], 0, 0, 0);
       if (q < 3) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      else if (has_next) __builtin_amdgcn_sched_group_barrier(0x100, 8 + NTW + 1, 0);
 #pragma unroll
       for (int k = 0; k < 8 * NTW; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (k < nvm) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (q < 3) {
+      if (q < 3 || has_next) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) af[i] = an[i];
-      }
-      if (q < 3 || next) {
 #pragma unroll
         for (int j = 0; j < NTW; ++j) bq[j] = bn[j];
+      }
+      if (q == 2 && has_next) {
+        // only step + 2's DMAs (the last NDMA issued) may still be in flight
+        __builtin_amdgcn_s_waitcnt(dma ? vm_lgkm_wait(NDMA) : vm_lgkm_wait(0));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
-  // prologue: K-step 0 into stage 0, its tables and first operands ready
-  issue(0, smem);
-  __builtin_amdgcn_s_waitcnt(0);
-  tables_next();
+  // prologue: steps 0 and 1 in flight; step 0's operands ready
+  dma_part(0, 0);
+  dma_part(0, 1);
+  if (KT > 1) {
+    dma_part(1, 0);
+    dma_part(1, 1);
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(NDMA));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+  }
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  read_a(af, stage(0), 0);
+  tables(stage(0));
 #pragma unroll
   for (int j = 0; j < NTW; ++j) bq[j] = decoded(j, 0);
-  __syncthreads();
-  for (int step = 0; step + 1 < KT; ++step) {
-    const uint8_t* As = smem + (step & 1) * A_TILE;
-    uint8_t* An = smem + ((step + 1) & 1) * A_TILE;
-    issue(step + 1, An);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) af[i] = *(const bf16x8_t*)(As + swz_a(i * 32 + li, 4 * g));
-    mma_step(As, std::true_type{});
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA into the other stage has landed
-    __syncthreads();
+  int step = 0;
+  for (; step + 2 < KT; ++step) mma_step(step, std::true_type{}, std::true_type{});
+  if (step + 1 < KT) {
+    mma_step(step, std::true_type{}, std::false_type{});
+    ++step;
   }
-  {  // last weight step; the LoRA step's A tile (U) goes to the other stage
-    const uint8_t* As = smem + ((KT - 1) & 1) * A_TILE;
-    uint8_t* An = smem + (KT & 1) * A_TILE;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) af[i] = *(const bf16x8_t*)(As + swz_a(i * 32 + li, 4 * g));
-    mma_step(As, std::false_type{});
+  {  // last weight step; the LoRA step's A tile (U) goes to the next stage,
+     // last read two steps ago (before the barrier of the previous step)
+    mma_step(step, std::false_type{}, std::false_type{});
     uint4 ar[8];
     load_a_rank(ar, S.U, a.r, M, m0, t);
-    store_a(An, ar, t);
+    store_a(stage(step + 1), ar, t);
     __syncthreads();
   }
   // LoRA step: [U | 0] [s B | 0]^T
@@ -364,7 +469,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
       for (int q = 0; q < 4; ++q)
         lb[j][q] = n < N ? lora_row8(S.B + n * a.r, 32 * g + 8 * q, a.r, a.s) : make_uint4(0, 0, 0, 0);
     }
-    const uint8_t* As = smem + (KT & 1) * A_TILE;
+    const uint8_t* As = stage(step + 1);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       bf16x8_t a8[8];
@@ -374,30 +479,40 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8[i], as_bf16x8(lb[j][q]), acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lb[j][q]), a8[i], acc[i][j], 0, 0, 0);
     }
   }
 
+  // Epilogue. The products above are C = W X^T (the weight operand first), so
+  // lane (li, g) of accumulator [i][j] holds output row m = m0 + 32 i + li and,
+  // in entries 4 v .. 4 v + 3, the four consecutive columns
+  // n = n0 + w WN + 32 j + 8 v + 4 g + (0..3): one 8-byte bf16 store (16-byte
+  // float32) per group. N % 16 == 0, so a group is wholly inside or outside.
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 8; ++i) {
+    const int64_t m = m0 + 32 * i + li;
+    if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int64_t n = n0 + w * WN + 32 * j + li;
-      if (n >= N) continue;
+    for (int j = 0; j < NTW; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-        if (m < M) {
-          const int64_t o = m * S.ldo + S.col0 + n;
-          float val = acc[i][j][v];
-          if (S.resid) val += bf16_to_f32(S.resid[o]);
-          if (a.out_f32)
-            ((float*)S.out)[o] = val;
-          else
-            ((uint16_t*)S.out)[o] = f32_to_bf16(val);
+      for (int v = 0; v < 4; ++v) {
+        const int64_t n = n0 + w * WN + 32 * j + 8 * v + 4 * g;
+        if (n >= N) continue;
+        const int64_t o = m * S.ldo + S.col0 + n;
+        float f[4] = {acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]};
+        if (S.resid) {
+          const uint2 rv = *(const uint2*)(S.resid + o);
+          f[0] += __builtin_bit_cast(float, rv.x << 16);
+          f[1] += __builtin_bit_cast(float, rv.x & 0xffff0000u);
+          f[2] += __builtin_bit_cast(float, rv.y << 16);
+          f[3] += __builtin_bit_cast(float, rv.y & 0xffff0000u);
         }
+        if (a.out_f32)
+          *(float4*)((float*)S.out + o) = make_float4(f[0], f[1], f[2], f[3]);
+        else
+          *(uint2*)((uint16_t*)S.out + o) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
       }
-    }
+  }
 }
 
 // =============================================================== backward dX
@@ -595,7 +710,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
     if (rc_ != QL_OK) return rc_; \
   } while (0)
 
-constexpr int FWD_LDS = 2 * A_TILE;
+template <int BN>
+constexpr int fwd_lds() { return FWD_STAGES * fwd_stage_bytes<BN>(); }
 template <int BN>
 constexpr int bwd_lds() { return 2 * (A_TILE + 64 * BN * 2); }
 
@@ -605,8 +721,8 @@ ql_status ensure_attrs() {
   int dev = 0;
   QL_HIP_CHECK(hipGetDevice(&dev));
   if (dev >= 0 && dev < 64 && !g_attr_set[dev]) {
-    QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_fwd<64>, hipFuncAttributeMaxDynamicSharedMemorySize, FWD_LDS));
-    QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_fwd<32>, hipFuncAttributeMaxDynamicSharedMemorySize, FWD_LDS));
+    QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_fwd<64>, hipFuncAttributeMaxDynamicSharedMemorySize, fwd_lds<256>()));
+    QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_fwd<32>, hipFuncAttributeMaxDynamicSharedMemorySize, fwd_lds<128>()));
     QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_bwd<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      bwd_lds<256>()));
     QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_bwd<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -631,24 +747,17 @@ int cu_count() {
 
 }  // namespace
 
-// Tile width: the wide tile (256 columns) unless it leaves CUs idle in the
-// first wave of workgroups and the narrow one does not. The choice depends on
-// shapes only, so resident and streamed runs pick the same kernels.
-ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st) {
-  if (a.M == 0) return QL_OK;
-  QL_TRY_PROF(ensure_attrs());
+namespace {
+
+// One launch of the forward kernel over all segments of `a` with one tile width.
+ql_status launch_fwd_tiles(const FwdArgs& a, bool wide, hipStream_t st) {
   const int tiles_m = (int)((a.M + BM - 1) / BM);
-  auto count = [&](int bn, int* start) {
-    start[0] = 0;
-    for (int s = 0; s < kMaxSegs; ++s)
-      start[s + 1] = start[s] + (s < a.nseg ? tiles_m * (int)((a.seg[s].N + bn - 1) / bn) : 0);
-    return start[a.nseg];
-  };
-  int st256[kMaxSegs + 1], st128[kMaxSegs + 1];
-  const int t256 = count(256, st256), t128 = count(128, st128);
-  const bool wide = t256 >= cu_count() || t128 <= t256;
-  const int* start = wide ? st256 : st128;
-  const int total = wide ? t256 : t128;
+  const int bn = wide ? 256 : 128;
+  int start[kMaxSegs + 1];
+  start[0] = 0;
+  for (int s = 0; s < kMaxSegs; ++s)
+    start[s + 1] = start[s] + (s < a.nseg ? tiles_m * (int)((a.seg[s].N + bn - 1) / bn) : 0);
+  const int total = start[a.nseg];
   if (total == 0) return QL_OK;
   const int s1 = a.nseg > 1 ? start[1] : total + 1;
   const int s2 = a.nseg > 2 ? start[2] : total + 1;
@@ -656,9 +765,9 @@ ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st) {
   const bool prof = profiling_on();
   if (prof) QL_TRY_PROF(profile_begin(st, &tok));
   if (wide)
-    hipLaunchKernelGGL(k_gemm_fwd<64>, dim3(total), dim3(NT), FWD_LDS, st, a, tiles_m, total, s1, s2);
+    hipLaunchKernelGGL(k_gemm_fwd<64>, dim3(total), dim3(NT), fwd_lds<256>(), st, a, tiles_m, total, s1, s2);
   else
-    hipLaunchKernelGGL(k_gemm_fwd<32>, dim3(total), dim3(NT), FWD_LDS, st, a, tiles_m, total, s1, s2);
+    hipLaunchKernelGGL(k_gemm_fwd<32>, dim3(total), dim3(NT), fwd_lds<128>(), st, a, tiles_m, total, s1, s2);
   QL_HIP_CHECK(hipGetLastError());
   if (prof) {
     double flop = 0;
@@ -666,6 +775,70 @@ ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st) {
     QL_TRY_PROF(profile_end(st, tok, QL_KERNEL_GEMM_FWD, flop));
   }
   return QL_OK;
+}
+
+// Columns [c, N) of segment S as a segment of its own.
+FwdSeg seg_from(const FwdSeg& S, int64_t c, int64_t K, int r) {
+  FwdSeg o = S;
+  o.packed += c * (K / 2);
+  o.absmax += c * (K / 64);
+  o.B += c * r;
+  o.col0 += c;
+  o.N -= c;
+  return o;
+}
+
+}  // namespace
+
+// Launch geometry. Tiles are 256 x 256 (wide) or 256 x 128 (narrow); the chip
+// runs cu_count workgroups per round. One partial round: the wide tile unless
+// narrow tiles fill more CUs. Several rounds: the whole rounds take wide tiles
+// and the column blocks of the last, partial round are re-cut into narrow
+// tiles (twice as many, half the work each) in a second launch, so that round
+// fills the chip (for the 8B gate|up at M = 2048: 3 wide rounds + 1 narrow
+// instead of 4 wide rounds). The geometry depends on shapes only, so resident
+// and streamed runs pick the same kernels.
+ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st) {
+  if (a.M == 0) return QL_OK;
+  QL_TRY_PROF(ensure_attrs());
+  const int tiles_m = (int)((a.M + BM - 1) / BM);
+  const int C = cu_count();
+  int t256 = 0, t128 = 0;
+  for (int s = 0; s < a.nseg; ++s) {
+    t256 += tiles_m * (int)((a.seg[s].N + 255) / 256);
+    t128 += tiles_m * (int)((a.seg[s].N + 127) / 128);
+  }
+  if (t256 <= C) return launch_fwd_tiles(a, t256 == C || t128 <= t256, st);
+  const int full = (t256 / C) * C;
+  if (full == t256) return launch_fwd_tiles(a, true, st);
+  // split at the column block holding wide tile `full` (enumeration order:
+  // segment, column block, row block)
+  FwdArgs aw = a, an = a;
+  aw.nseg = 0;
+  an.nseg = 0;
+  int cum = 0;
+  for (int s = 0; s < a.nseg; ++s) {
+    const FwdSeg& S = a.seg[s];
+    const int blocks = (int)((S.N + 255) / 256);
+    if (an.nseg == 0 && cum + tiles_m * blocks <= full) {
+      aw.seg[aw.nseg++] = S;
+      cum += tiles_m * blocks;
+      continue;
+    }
+    if (an.nseg == 0) {
+      const int64_t kw = (int64_t)((full - cum) / tiles_m) * 256;  // columns left on wide tiles
+      if (kw > 0) {
+        aw.seg[aw.nseg] = S;
+        aw.seg[aw.nseg].N = kw;
+        ++aw.nseg;
+      }
+      an.seg[an.nseg++] = seg_from(S, kw, a.K, a.r);
+    } else {
+      an.seg[an.nseg++] = S;
+    }
+  }
+  if (aw.nseg > 0) QL_TRY_PROF(launch_fwd_tiles(aw, true, st));
+  return an.nseg > 0 ? launch_fwd_tiles(an, false, st) : QL_OK;
 }
 
 ql_status launch_gemm_bwd(const BwdArgs& a, hipStream_t st) {
