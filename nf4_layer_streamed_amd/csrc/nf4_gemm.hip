@@ -527,81 +527,145 @@ __device__ __forceinline__ int bt_off(int n, int k) {
   return n * (BN * 2) + ((chunk ^ swz_f(n)) << 4) + ((k & 4) << 1);
 }
 
-// WNB: output columns per wave (128 or 64); workgroup tile 256 x (2 WNB), waves 2 x 2.
-// Reduction order: for each segment its 64-row weight steps, then the LoRA
-// steps of all segments.
+// Raw weight data of one reduction step in LDS: the codes of 64 rows x BN
+// columns (BN / 2 bytes per row in 16-byte chunks; chunk c of row n sits in
+// slot n CPR + (c ^ ((n >> SH) mod CPR)), so 16 lanes reading one chunk of 16
+// consecutive rows hit distinct banks), then the absmax of 64 rows x 4 blocks.
+template <int BN>
+constexpr int bwd_raw_bytes() { return 64 * (BN / 2) + 1024; }
+template <int BN>
+constexpr int bwd_lds() { return 2 * A_TILE + 2 * bwd_raw_bytes<BN>() + 2 * (64 * BN * 2); }
+// By-value select among three uniform values (a ternary on lvalues would
+// select an address and keep the values in private memory).
+template <typename T>
+__device__ __forceinline__ T sel3(int s, T v0, T v1, T v2) {
+  T r = v2;
+  r = s == 1 ? v1 : r;
+  r = s == 0 ? v0 : r;
+  return r;
+}
+
+template <int BN>
+__device__ __forceinline__ int raw_slot(int n, int c) {
+  constexpr int CPR = BN / 32;
+  constexpr int SH = CPR == 8 ? 1 : 2;
+  return n * CPR + (c ^ ((n >> SH) & (CPR - 1)));
+}
+
+// WNB: output columns per wave (128 or 64); workgroup tile 256 x (2 WNB) at
+// columns k_base + (tile / tiles_m) BN; waves 2 x 2. Reduction order: for
+// each segment its 64-row weight steps, then the LoRA steps of all segments.
+//
+// Pipeline per reduction step s: the dY tile of step s + 1 (DMA, two stages)
+// and the raw codes and scales of step s + 2 (DMA, two stages) stream in
+// while step s's MFMAs run, and every thread decodes its share of step s + 1's
+// raw data into the other bf16 weight tile, interleaved with the MFMAs. One
+// barrier per step: each wave first waits for its own DMAs of the step.
 template <int WNB>
-__global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m, int tiles_total) {
+__global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m, int tiles_total, int k_base) {
   constexpr int BN = 2 * WNB;
   constexpr int NTW = WNB / 32;
-  constexpr int B_TILE = 64 * BN * 2;
-  constexpr int STAGE = A_TILE + B_TILE;
+  constexpr int CPR = BN / 32;
+  constexpr int SH = CPR == 8 ? 1 : 2;
+  constexpr int RAW = bwd_raw_bytes<BN>();
+  constexpr int DEC_BYTES = 64 * BN * 2;
+  constexpr int OFF_R = 2 * A_TILE, OFF_D = OFF_R + 2 * RAW;
+  constexpr int ABS = 64 * (BN / 2);
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1, g = lane >> 5, li = lane & 31;
+  const int t = threadIdx.x, lane = t & 63, g = lane >> 5, li = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w >> 1, wn = w & 1;
 
   const int tile = (int)xcd_remap(blockIdx.x, (uint32_t)tiles_total);
   const int64_t m0 = (int64_t)(tile % tiles_m) * BM;
-  const int64_t k0 = (int64_t)(tile / tiles_m) * BN;
+  const int64_t k0 = (int64_t)k_base + (int64_t)(tile / tiles_m) * BN;
   const int64_t K = a.K, kbn = K / 64, M = a.M;
   const int64_t xrows = M - m0 < BM ? M - m0 : BM;
+  const int nseg = a.nseg;
 
-  // weight steps per segment and their total
-  const int nw0 = (int)((a.seg[0].N + BK - 1) / BK);
-  const int nw1 = a.nseg > 1 ? (int)((a.seg[1].N + BK - 1) / BK) : 0;
-  const int nw2 = a.nseg > 2 ? (int)((a.seg[2].N + BK - 1) / BK) : 0;
-  const int WS = nw0 + nw1 + nw2;
-
-  // decode coordinates: one row (reduction index) and one 64-wide block of output columns
-  constexpr int UNITS = 64 * (BN / 64);
-  const bool dthread = t < UNITS;
-  const int drow = t & 63, dblk = (t >> 6) % (BN / 64);
-  const int64_t dk = k0 + 64 * dblk;
-  const bool dkval = dthread && dk < K;
-  const int xoff = ((t >> 3) * 0 + (t & 7) * 8) * 2;  // column part; the row part depends on the segment
-
-  uint4 ar[8];
-  uint4 bc0, bc1;
-  float bsc;
-
-  // per weight step: segment, first reduction row
-  auto seg_of = [&](int step, int& sg, int64_t& nb) {
-    if (step < nw0) { sg = 0; nb = (int64_t)step * BK; }
-    else if (step < nw0 + nw1) { sg = 1; nb = (int64_t)(step - nw0) * BK; }
-    else { sg = 2; nb = (int64_t)(step - nw0 - nw1) * BK; }
+  // per-segment descriptors (uniform; selected, never indexed)
+  auto seg_n = [&](int s) -> int64_t { return s < nseg ? a.seg[s].N : 0; };
+  const int64_t N0 = seg_n(0), N1 = seg_n(1), N2 = seg_n(2);
+  auto ydesc = [&](int s, int64_t N) {
+    return rsrc(s < nseg ? (const void*)(a.seg[s].dY + m0 * N) : nullptr, s < nseg ? xrows * N * 2 : 0);
   };
-  auto issue = [&](int step) {
-    int sg;
-    int64_t nb;
-    seg_of(step, sg, nb);
-    const BwdSeg& S = a.seg[sg];
-    const int ldy = (int)S.N;
-    const __amdgpu_buffer_rsrc_t yr = rsrc(S.dY + m0 * S.N, xrows * S.N * 2);
-    const int kmax = (int)(S.N - nb);  // columns of dY left in this segment
+  auto cdesc = [&](int s, int64_t N) {
+    return rsrc(s < nseg ? (const void*)(a.seg[s].packed + k0 / 2) : nullptr, s < nseg ? N * (K / 2) - k0 / 2 : 0);
+  };
+  auto sdesc = [&](int s, int64_t N) {
+    return rsrc(s < nseg ? (const void*)(a.seg[s].absmax + k0 / 64) : nullptr, s < nseg ? (N * kbn - k0 / 64) * 4 : 0);
+  };
+  const __amdgpu_buffer_rsrc_t yr0 = ydesc(0, N0), yr1 = ydesc(1, N1), yr2 = ydesc(2, N2);
+  const __amdgpu_buffer_rsrc_t cr0 = cdesc(0, N0), cr1 = cdesc(1, N1), cr2 = cdesc(2, N2);
+  const __amdgpu_buffer_rsrc_t sr0 = sdesc(0, N0), sr1 = sdesc(1, N1), sr2 = sdesc(2, N2);
+  const int WS = (int)((N0 + BK - 1) / BK + (N1 + BK - 1) / BK + (N2 + BK - 1) / BK);
+
+  // DMA cursors (segment, first reduction row) of the next dY tile and the
+  // next raw step; both walk the weight steps in order.
+  int sgA = 0, nbA = 0, sgR = 0, nbR = 0;
+  auto advance = [&](int& sg, int& nb) {
+    const int64_t N = sel3(sg, N0, N1, N2);
+    nb += BK;
+    const bool wrap = nb >= N;
+    nb = wrap ? 0 : nb;
+    sg += wrap ? 1 : 0;
+  };
+
+  // dY tile (256 rows x 64 columns of segment sgA from nbA) into an A stage;
+  // columns past the segment's N read as zeros (offset past the buffer).
+  const int arow = 8 * w + (lane >> 3), alc = (lane & 7) ^ (lane >> 3);
+  auto dma_a = [&](uint8_t* As) {
+    const int64_t N = sel3(sgA, N0, N1, N2);
+    const __amdgpu_buffer_rsrc_t yr = sel3(sgA, yr0, yr1, yr2);
+    const int ldy = __builtin_amdgcn_readfirstlane((int)N);
+    const int ylim = __builtin_amdgcn_readfirstlane((int)(xrows * N * 2));
+    // all-ones where the lane's 8 columns lie past N (branch-free select)
+    const int past = -(int)(nbA + 8 * alc >= N);
+    const int so = __builtin_amdgcn_readfirstlane(nbA * 2);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int row = (t >> 3) + 32 * i;
-      const uint4 v = bload16(yr, (row * ldy) * 2 + xoff, (int)nb * 2);
-      ar[i] = ((t & 7) * 8 < kmax) ? v : make_uint4(0, 0, 0, 0);
+      const int vo = (((arow + 32 * i) * ldy * 2 + alc * 16) & ~past) | (ylim & past);
+      dma16(yr, As + (4 * i + w) * 1024, vo, so);
     }
-    const int64_t nrows = S.N - nb < BK ? S.N - nb : BK;
-    const __amdgpu_buffer_rsrc_t cr = rsrc(S.packed + nb * (K / 2), nrows * (K / 2));
-    const __amdgpu_buffer_rsrc_t sr = rsrc(S.absmax + nb * kbn, nrows * kbn * 4);
-    const int co = drow * (int)(K / 2) + (int)(dk / 2);
-    bc0 = bload16(cr, co, 0);
-    bc1 = bload16(cr, co + 16, 0);
-    bsc = bload4f(sr, (drow * (int)kbn + (int)(dk / 64)) * 4, 0);
-    if (!dkval) {
-      bc0 = bc1 = make_uint4(0, 0, 0, 0);
-      bsc = 0.f;
-    }
+    advance(sgA, nbA);
   };
-  auto store_b = [&](uint8_t* Bs) {
-    const Lut lut = make_lut(bsc);
-    const uint32_t p[8] = {bc0.x, bc0.y, bc0.z, bc0.w, bc1.x, bc1.y, bc1.z, bc1.w};
-    if (dthread) {
+  // raw codes and scales of the step at (sgR, nbR) into a raw stage
+  auto dma_raw = [&](uint8_t* R) {
+    const __amdgpu_buffer_rsrc_t cr = sel3(sgR, cr0, cr1, cr2);
+    const __amdgpu_buffer_rsrc_t sr = sel3(sgR, sr0, sr1, sr2);
+    const int kh = (int)(K / 2);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) *(uint4*)(Bs + bt_off<BN>(drow, 64 * dblk + 8 * c)) = decode8(p[c], lut);
+    for (int cc = 0; cc < CPR / 4; ++cc) {
+      const int ci = w + 4 * cc;
+      const int slot = ci * 64 + lane;
+      const int n = slot / CPR, pc = slot % CPR;
+      const int c = pc ^ ((n >> SH) & (CPR - 1));
+      dma16(cr, R + ci * 1024, n * kh + c * 16, __builtin_amdgcn_readfirstlane(nbR * kh));
     }
+    dma4(sr, R + ABS + 256 * w, ((16 * w + (lane >> 2)) * (int)kbn + (lane & 3)) * 4,
+         __builtin_amdgcn_readfirstlane(nbR * (int)kbn * 4));
+    advance(sgR, nbR);
+  };
+
+  // decode share of a thread: row dn, 64-column block dc (wide) or half dh of it (narrow)
+  constexpr int NCH = BN == 256 ? 2 : 1;  // 16-byte code chunks per thread
+  const int dn = t & 63, dc = (t >> 6) & (BN / 64 - 1), dh = BN == 256 ? 0 : (t >> 7);
+  uint32_t dcode[4 * NCH];
+  Lut dlut;
+  auto dec_load = [&](const uint8_t* R) {
+#pragma unroll
+    for (int h = 0; h < NCH; ++h) {
+      const u32x4_t v = *(const u32x4_t*)(R + raw_slot<BN>(dn, 2 * dc + dh + h) * 16);
+      dcode[4 * h] = v[0];
+      dcode[4 * h + 1] = v[1];
+      dcode[4 * h + 2] = v[2];
+      dcode[4 * h + 3] = v[3];
+    }
+    dlut = make_lut(*(const float*)(R + ABS + (dn * 4 + dc) * 4));
+  };
+  // word e of the thread's codes -> 8 bf16 at columns 64 dc + 32 dh + 8 e
+  auto dec_word = [&](uint8_t* Bd, int e) {
+    const uint4 v = decode8(dcode[e], dlut);
+    *(u32x4_t*)(Bd + bt_off<BN>(dn, 64 * dc + 32 * dh + 8 * e)) = u32x4_t{v.x, v.y, v.z, v.w};
   };
 
   f32x16_t acc[4][NTW];
@@ -612,57 +676,105 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
 
   // transposed-read coordinates: within each group of 16 lanes, lane 4 ra + cbq
   // addresses row ra (of four) and the 4-column piece cbq (of four)
-  const int h = lane >> 4, s16 = lane & 15, ra = s16 >> 2, cbq = s16 & 3;
-  auto mma_step = [&](const uint8_t* st) {
-    const uint8_t* As = st;
-    const uint8_t* Bs = st + A_TILE;
+  const int h16 = lane >> 4, s16 = lane & 15, ra = s16 >> 2, cbq = s16 & 3;
+  bf16x8_t af[4], an[4], bfr[4][NTW];
+  auto read_a = [&](bf16x8_t (&fa)[4], const uint8_t* As, int q) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bf16x8_t af[4], bf[NTW];
+    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8_t*)(As + swz_a(wm * 128 + i * 32 + li, 2 * q + g));
+  };
+  // Weight fragments of sub-step q, read transposed. The transposing LDS read
+  // carries no type information, and the compiler then waits for every LDS
+  // DMA in flight before it; all of a step's transposed reads are therefore
+  // issued before the step's DMAs.
+  auto read_b = [&](bf16x8_t (&fb)[NTW], const uint8_t* Bs, int q) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8_t*)(As + swz_a(wm * 128 + i * 32 + li, 2 * q + g));
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        // lanes 32 g + c (c < 32) need column c and reduction rows 16 q + 8 g .. + 8
-        const int col = wn * WNB + 32 * j + 16 * (h & 1) + 4 * cbq;
-        const int row = 16 * q + 8 * (h >> 1) + ra;
-        const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(Bs + bt_off<BN>(row, col)));
-        const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(Bs + bt_off<BN>(row + 4, col)));
-        const i16x8_t v = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        bf[j] = __builtin_bit_cast(bf16x8_t, v);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NTW; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < NTW; ++j) {
+      // lanes 32 g + c (c < 32) need column c and reduction rows 16 q + 8 g .. + 8
+      const int col = wn * WNB + 32 * j + 16 * (h16 & 1) + 4 * cbq;
+      const int row = 16 * q + 8 * (h16 >> 1) + ra;
+      const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(Bs + bt_off<BN>(row, col)));
+      const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(Bs + bt_off<BN>(row + 4, col)));
+      const i16x8_t v = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      fb[j] = __builtin_bit_cast(bf16x8_t, v);
     }
   };
+  auto mfmas = [&](int q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[q][j], af[i], acc[i][j], 0, 0, 0);
+  };
+  auto barrier_all = [&]() {
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
 
-  // weight steps: stage s & 1 holds step s; step s + 1 is in registers while s computes
-  issue(0);
-  store_a(smem, ar, t);
-  store_b(smem + A_TILE);
-  if (WS > 1) issue(1);
-  __syncthreads();
-  for (int step = 0; step < WS; ++step) {
-    uint8_t* nx = smem + ((step + 1) & 1) * STAGE;
-    mma_step(smem + (step & 1) * STAGE);
-    if (step + 1 < WS) {
-      store_a(nx, ar, t);
-      store_b(nx + A_TILE);
-      if (step + 2 < WS) issue(step + 2);
+  // one reduction step on A stage / weight tile s & 1; DO_A: DMA the next dY
+  // tile; DO_R: DMA the raw data two steps ahead; DO_DEC: decode the next step
+  auto step_body = [&](int s, auto da_c, auto dr_c, auto dec_c) {
+    constexpr bool DO_A = decltype(da_c)::value, DO_R = decltype(dr_c)::value, DO_DEC = decltype(dec_c)::value;
+    const uint8_t* As = smem + (s & 1) * A_TILE;
+    const uint8_t* Bs = smem + OFF_D + (s & 1) * DEC_BYTES;
+    uint8_t* Bd = smem + OFF_D + ((s + 1) & 1) * DEC_BYTES;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) read_b(bfr[q], Bs, q);
+    read_a(af, As, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (DO_A) dma_a(smem + ((s + 1) & 1) * A_TILE);
+    if (DO_R) dma_raw(smem + OFF_R + (s & 1) * RAW);
+    if (DO_DEC) dec_load(smem + OFF_R + ((s + 1) & 1) * RAW);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q < 3) read_a(an, As, q + 1);
+      if (DO_DEC) {
+#pragma unroll
+        for (int e = 0; e < NCH; ++e) dec_word(Bd, NCH * q + e);
+      }
+      mfmas(q);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q < 3) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = an[i];
+      }
     }
-    __syncthreads();
+    barrier_all();
+  };
+
+  if (WS > 0) {
+    // prologue: dY tile 0 and raw steps 0 and 1 in flight; step 0 decoded
+    dma_a(smem);
+    dma_raw(smem + OFF_R);
+    if (WS > 1) dma_raw(smem + OFF_R + RAW);
+    barrier_all();
+    dec_load(smem + OFF_R);
+#pragma unroll
+    for (int e = 0; e < 4 * NCH; ++e) dec_word(smem + OFF_D, e);
+    barrier_all();
+    int st = 0;
+    for (; st + 2 < WS; ++st) step_body(st, std::true_type{}, std::true_type{}, std::true_type{});
+    if (st + 1 < WS) {
+      step_body(st, std::true_type{}, std::false_type{}, std::true_type{});
+      ++st;
+    }
+    step_body(st, std::false_type{}, std::false_type{}, std::false_type{});
   }
+
   // LoRA steps: A = G_s, B rows j < r = s A_s[j][k0 ..], zero past r
-  for (int sg = 0; sg < a.nseg; ++sg) {
+  constexpr int UNITS = 64 * (BN / 64);
+  const bool dthread = t < UNITS;
+  const int drow = t & 63, dblk = (t >> 6) % (BN / 64);
+  const int64_t dk = k0 + 64 * dblk;
+  for (int sg = 0; sg < nseg; ++sg) {
     const BwdSeg& S = a.seg[sg];
-    uint8_t* st = smem + ((WS + sg) & 1) * STAGE;
+    uint8_t* As = smem + (sg & 1) * A_TILE;
+    uint8_t* Bs = smem + OFF_D + (sg & 1) * DEC_BYTES;
+    uint4 ar[8];
     load_a_rank(ar, S.G, a.r, M, m0, t);
-    store_a(st, ar, t);
+    store_a(As, ar, t);
     if (dthread) {
       const bool live = drow < a.r && dk < K;
       const uint4* src = (const uint4*)(S.A + (int64_t)drow * K + dk);
@@ -675,33 +787,49 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
         for (int e = 0; e < 4; ++e)
           o[e] = pack_bf16x2(a.s * __builtin_bit_cast(float, wv[e] << 16),
                              a.s * __builtin_bit_cast(float, wv[e] & 0xffff0000u));
-        *(uint4*)(st + A_TILE + bt_off<BN>(drow, 64 * dblk + 8 * c)) = make_uint4(o[0], o[1], o[2], o[3]);
+        *(uint4*)(Bs + bt_off<BN>(drow, 64 * dblk + 8 * c)) = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
     __syncthreads();
-    mma_step(st);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) read_b(bfr[q], Bs, q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      read_a(af, As, q);
+      mfmas(q);
+    }
   }
 
+  // Epilogue. The products are C = W^T dY^T (weight operand first), so lane
+  // (li, g) of accumulator [i][j] holds output row m = m0 + 128 wm + 32 i + li
+  // and, in entries 4 v .. 4 v + 3, the four consecutive columns
+  // k = k0 + WNB wn + 32 j + 8 v + 4 g + (0..3). K % 64 == 0, so a group is
+  // wholly inside or outside.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + wm * 128 + 32 * i + li;
+    if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int64_t k = k0 + wn * WNB + 32 * j + li;
-      if (k >= K) continue;
+    for (int j = 0; j < NTW; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-        if (m < M) {
-          const int64_t o = m * K + k;
-          float val = acc[i][j][v];
-          if (a.resid) val += bf16_to_f32(a.resid[o]);
-          if (a.out_f32)
-            ((float*)a.out)[o] = val;
-          else
-            ((uint16_t*)a.out)[o] = f32_to_bf16(val);
+      for (int v = 0; v < 4; ++v) {
+        const int64_t k = k0 + wn * WNB + 32 * j + 8 * v + 4 * g;
+        if (k >= K) continue;
+        const int64_t o = m * K + k;
+        float f[4] = {acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]};
+        if (a.resid) {
+          const uint2 rv = *(const uint2*)(a.resid + o);
+          f[0] += __builtin_bit_cast(float, rv.x << 16);
+          f[1] += __builtin_bit_cast(float, rv.x & 0xffff0000u);
+          f[2] += __builtin_bit_cast(float, rv.y << 16);
+          f[3] += __builtin_bit_cast(float, rv.y & 0xffff0000u);
         }
+        if (a.out_f32)
+          *(float4*)((float*)a.out + o) = make_float4(f[0], f[1], f[2], f[3]);
+        else
+          *(uint2*)((uint16_t*)a.out + o) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
       }
-    }
+  }
 }
 
 #define QL_TRY_PROF(expr)         \
@@ -712,8 +840,6 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
 
 template <int BN>
 constexpr int fwd_lds() { return FWD_STAGES * fwd_stage_bytes<BN>(); }
-template <int BN>
-constexpr int bwd_lds() { return 2 * (A_TILE + 64 * BN * 2); }
 
 bool g_attr_set[64] = {};
 
@@ -841,29 +967,47 @@ ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st) {
   return an.nseg > 0 ? launch_fwd_tiles(an, false, st) : QL_OK;
 }
 
-ql_status launch_gemm_bwd(const BwdArgs& a, hipStream_t st) {
-  if (a.M == 0) return QL_OK;
-  QL_TRY_PROF(ensure_attrs());
+namespace {
+
+// One launch of the dX kernel over output columns [k_base, k_base + k_cols).
+ql_status launch_bwd_tiles(const BwdArgs& a, bool wide, int64_t k_base, int64_t k_cols, hipStream_t st) {
   const int tiles_m = (int)((a.M + BM - 1) / BM);
-  const int t256 = tiles_m * (int)((a.K + 255) / 256);
-  const int t128 = tiles_m * (int)((a.K + 127) / 128);
-  const bool wide = t256 >= cu_count() || t128 <= t256;
-  const int total = wide ? t256 : t128;
+  const int bn = wide ? 256 : 128;
+  const int total = tiles_m * (int)((k_cols + bn - 1) / bn);
   if (total == 0) return QL_OK;
   void* tok = nullptr;
   const bool prof = profiling_on();
   if (prof) QL_TRY_PROF(profile_begin(st, &tok));
   if (wide)
-    hipLaunchKernelGGL(k_gemm_bwd<128>, dim3(total), dim3(NT), bwd_lds<256>(), st, a, tiles_m, total);
+    hipLaunchKernelGGL(k_gemm_bwd<128>, dim3(total), dim3(NT), bwd_lds<256>(), st, a, tiles_m, total, (int)k_base);
   else
-    hipLaunchKernelGGL(k_gemm_bwd<64>, dim3(total), dim3(NT), bwd_lds<128>(), st, a, tiles_m, total);
+    hipLaunchKernelGGL(k_gemm_bwd<64>, dim3(total), dim3(NT), bwd_lds<128>(), st, a, tiles_m, total, (int)k_base);
   QL_HIP_CHECK(hipGetLastError());
   if (prof) {
     double flop = 0;
-    for (int s = 0; s < a.nseg; ++s) flop += 2.0 * (double)a.M * (double)a.K * (double)(a.seg[s].N + a.r);
+    for (int s = 0; s < a.nseg; ++s) flop += 2.0 * (double)a.M * (double)k_cols * (double)(a.seg[s].N + a.r);
     QL_TRY_PROF(profile_end(st, tok, QL_KERNEL_GEMM_BWD, flop));
   }
   return QL_OK;
+}
+
+}  // namespace
+
+// Same geometry rule as the forward: whole rounds on wide tiles, the column
+// blocks of a last partial round on narrow tiles in a second launch.
+ql_status launch_gemm_bwd(const BwdArgs& a, hipStream_t st) {
+  if (a.M == 0) return QL_OK;
+  QL_TRY_PROF(ensure_attrs());
+  const int tiles_m = (int)((a.M + BM - 1) / BM);
+  const int C = cu_count();
+  const int t256 = tiles_m * (int)((a.K + 255) / 256);
+  const int t128 = tiles_m * (int)((a.K + 127) / 128);
+  if (t256 <= C) return launch_bwd_tiles(a, t256 == C || t128 <= t256, 0, a.K, st);
+  const int full = (t256 / C) * C;
+  if (full == t256) return launch_bwd_tiles(a, true, 0, a.K, st);
+  const int64_t kw = (int64_t)(full / tiles_m) * 256;
+  if (kw > 0) QL_TRY_PROF(launch_bwd_tiles(a, true, 0, kw, st));
+  return launch_bwd_tiles(a, false, kw, a.K - kw, st);
 }
 
 }  // namespace ql
