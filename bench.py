@@ -13,10 +13,12 @@ from pinned host memory into two device slots, 2L - 2 layer copies per step,
 the last two layers reused at the turnaround). `value` is tokens per second of
 the whole step (M tokens per step). The JSON line also carries:
 
-* roofline - the dominant kernel (the fused NF4-dequant MFMA GEMM with the
-  larger summed time), its algorithmic FLOPs over its launch durations measured
-  with HIP events on its own stream during the timed steps, against the bf16
-  dense MFMA peak (2.5166 PFLOP/s).
+* roofline - the dominant kernel (the fused NF4-dequant MFMA GEMM build, by
+  kernel symbol, with the largest summed time), its algorithmic FLOPs over its
+  launch durations measured with HIP events on its own stream during the timed
+  steps, against the bf16 dense MFMA peak (2.5166 PFLOP/s); `traffic` is its
+  HBM bytes per launch from the committed counter summary (null if the kernel
+  sources changed since). gemm_all: all fused-GEMM launches together.
 * pcie - H2D bytes per step over the step time, against 64 GB/s (PCIe Gen5
   x16 per direction) and a same-session pinned-copy ceiling.
 * resident - the same step with the store resident in HBM (no copies).
@@ -37,8 +39,38 @@ HBM_PEAK_GBS = 8000.0
 PCIE_PEAK_GBS = 64.0
 
 
+CALIB_COPY_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_llama8b_stack_m2048.json")
+KERNEL_SOURCES = ("nf4_layer_streamed_amd/csrc/nf4_gemm.hip", "nf4_layer_streamed_amd/csrc/ql_internal.h")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's reading for a
+    plain device copy of known size), or None when there is no summary for it
+    or the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
 
 
 def build_inputs(ql, synth, torch, w, dev):
@@ -71,26 +103,31 @@ def build_inputs(ql, synth, torch, w, dev):
     return cfg, store, offs, lora, x, dy
 
 
-def cpu_baseline(rows=2048):
-    """The oracle on a bounded sample: layer 0 of the 8B stack with all 2048
-    tokens (or `rows` of them), forward + backward in bf16-faithful mode; tok/s
-    for the whole 32-layer step extrapolated as rows / (32 t), since every layer
-    has the same shapes and work."""
+def cpu_baseline(rows=2048, layers=3):
+    """The oracle on a bounded sample: the first `layers` layers of the 8B
+    stack with all 2048 tokens (or `rows` of them), forward + backward in
+    bf16-faithful mode, one layer at a time; tok/s for the whole 32-layer step
+    extrapolated as rows / (32 t / layers), since every layer has the same
+    shapes and work."""
     import numpy as np
     import synth
     from oracle import stack as ostack
     w = synth.WORKLOADS["llama8b_stack"]
     H, I, KV, d, r, alpha = w["H"], w["I"], w["KV"], w["head_dim"], w["r"], w["alpha"]
-    inp = synth.stack_inputs(1, rows, H, I, KV, r, ("llama8b_stack_cpu",))
-    ld = inp["layers"][0]
-    weights = {p: (ld[p]["packed"].numpy(), ld[p]["absmax"].numpy()) for p in ostack.PROJ}
-    lora = {p: (synth.as_f64(ld[p]["A"]), synth.as_f64(ld[p]["B"])) for p in ostack.PROJ}
-    layer = ostack.Layer(H, I, KV, d, alpha, weights, lora)
+    inp = synth.stack_inputs(layers, rows, H, I, KV, r, ("llama8b_stack_cpu",))
     x, dy = synth.as_f64(inp["x"]), synth.as_f64(inp["dy"])
-    t0 = time.perf_counter()
-    h, sv = layer.fwd(x)
-    layer.bwd(dy, sv)
-    t = time.perf_counter() - t0
+    t = 0.0
+    for li in range(layers):
+        ld = inp["layers"][li]
+        weights = {p: (ld[p]["packed"].numpy(), ld[p]["absmax"].numpy()) for p in ostack.PROJ}
+        lora = {p: (synth.as_f64(ld[p]["A"]), synth.as_f64(ld[p]["B"])) for p in ostack.PROJ}
+        layer = ostack.Layer(H, I, KV, d, alpha, weights, lora)
+        t0 = time.perf_counter()
+        h, sv = layer.fwd(x)
+        layer.bwd(dy, sv)
+        t += time.perf_counter() - t0
+        layer.drop_cache()
+        del layer, sv
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -103,9 +140,10 @@ def cpu_baseline(rows=2048):
             threads = max(i.get("num_threads", 0) for i in info) or cores
     except Exception:
         pass
-    return dict(value=rows / (w["L"] * t), unit="tok/s", cores=threads, kind="oracle",
-                sample=f"layer 0 of {w['L']}, {rows} of {w['M']} tokens, fwd+bwd bf16-faithful NumPy float64, "
-                       f"{t:.1f} s; tok/s = {rows} / ({w['L']} x t)", seconds=round(t, 2), host_cores=cores)
+    return dict(value=rows * layers / (w["L"] * t), unit="tok/s", cores=threads, kind="oracle",
+                sample=f"layers 0..{layers - 1} of {w['L']}, {rows} of {w['M']} tokens, fwd+bwd bf16-faithful "
+                       f"NumPy float64, {t:.1f} s; tok/s = {rows} / ({w['L']} x t / {layers})",
+                seconds=round(t, 2), host_cores=cores)
 
 
 def main():
@@ -166,7 +204,7 @@ def main():
         prof = None
         if profile:
             ql.ql_profile_enable(0)
-            prof = {k: ql.ql_profile_read(k) for k in (ql.QL_KERNEL_GEMM_FWD, ql.QL_KERNEL_GEMM_BWD)}
+            prof = {k: ql.ql_profile_read(k) for k in ql.KERNEL_SYMBOLS}
         return t, status, prof
 
     log(f"bench: warmup {args.warmup}, timing {args.steps} streamed steps")
@@ -186,16 +224,31 @@ def main():
     step_flop = L * (flop_fwd + flop_bwd)
     h2d_bytes = (2 * L - 2) * rec
     kern = {}
-    for k, name in ((ql.QL_KERNEL_GEMM_FWD, "k_gemm_fwd"), (ql.QL_KERNEL_GEMM_BWD, "k_gemm_bwd")):
+    for k, name in ql.KERNEL_SYMBOLS.items():
         n, kms, kfl = prof[k]
-        kern[name] = dict(launches=n, total_ms=kms, avg_us=1000.0 * kms / max(n, 1),
+        if n == 0:
+            continue
+        kern[name] = dict(launches=n, total_ms=kms, avg_us=1000.0 * kms / n,
                           tflops=kfl / (kms * 1e-3) / 1e12 if kms > 0 else 0.0, flop=kfl)
     dom = max(kern, key=lambda k: kern[k]["total_ms"])
     dk = kern[dom]
+    traffic = measured_traffic(dom)
     roofline = dict(bound="mfma", kernel=dom, achieved=round(dk["tflops"], 1), peak=MFMA_BF16_PEAK_TFLOPS,
-                    unit="TFLOP/s", frac=round(dk["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None,
+                    unit="TFLOP/s", frac=round(dk["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                    traffic=traffic, flop_per_launch=dk["flop"] / dk["launches"],
                     avg_launch_us=round(dk["avg_us"], 2), launches=dk["launches"])
     gemm_ms_per_step = sum(v["total_ms"] for v in kern.values()) / args.steps
+    gemm_flop = sum(v["flop"] for v in kern.values())
+    gemm_all = dict(tflops=round(gemm_flop / (sum(v["total_ms"] for v in kern.values()) * 1e-3) / 1e12, 1))
+    gemm_all["frac"] = round(gemm_all["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+
+    # a plain device copy of known size, outside the timed region: the
+    # reference point that scales the HBM byte counters of a counter run
+    calib = torch.empty(CALIB_COPY_BYTES, dtype=torch.uint8, device=dev)
+    calib_dst = torch.empty_like(calib)
+    calib_dst.copy_(calib)
+    torch.cuda.synchronize()
+    del calib, calib_dst
 
     # same-session PCIe ceiling: one 1 GiB pinned host-to-device copy
     nb = 1 << 30
@@ -252,6 +305,7 @@ def main():
         "tflops_step": round(step_flop / (ms * 1e-3) / 1e12, 1),
         "step_flop": step_flop,
         "gemm_ms_per_step": round(gemm_ms_per_step, 3),
+        "gemm_all": gemm_all,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kern.items()},
         "roofline": roofline,

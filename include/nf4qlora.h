@@ -233,15 +233,23 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
 
 /* ----------------------------------------------------------- measurement
  * Kernel timing for roofline measurement. While enabled, every launch of the
- * two fused NF4 GEMM kernels is bracketed by two hipEvents recorded on the
- * stream it runs on, together with its algorithmic FLOP count
- * (2 M N (K + r) for the forward, 2 M K (N + r) per reduction segment for dX).
+ * fused NF4 GEMM kernels is bracketed by two hipEvents recorded on the stream
+ * it runs on, together with its algorithmic FLOP count (2 M N (K + r) for the
+ * forward, 2 M K (N + r) per reduction segment for dX, over the columns the
+ * launch covers). Each kernel comes in a wide-tile (256 x 256 outputs per
+ * workgroup) and a narrow-tile (256 x 128) build, timed separately.
  * ql_profile_enable(1) starts a fresh record, ql_profile_enable(0) stops
  * recording. ql_profile_read waits for the recorded events and returns, for
  * one kernel, the number of launches, their summed duration (ms) and summed
  * FLOPs. Results are unaffected by profiling. Not thread-safe against
  * concurrent calls on other threads. */
-enum { QL_KERNEL_GEMM_FWD = 0, QL_KERNEL_GEMM_BWD = 1, QL_KERNEL_COUNT = 2 };
+enum {
+  QL_KERNEL_GEMM_FWD = 0,        /* forward, wide tiles */
+  QL_KERNEL_GEMM_BWD = 1,        /* dX, wide tiles */
+  QL_KERNEL_GEMM_FWD_NARROW = 2, /* forward, narrow tiles */
+  QL_KERNEL_GEMM_BWD_NARROW = 3, /* dX, narrow tiles */
+  QL_KERNEL_COUNT = 4
+};
 ql_status ql_profile_enable(int32_t on);
 ql_status ql_profile_read(int32_t kernel, int64_t* launches, double* ms, double* flop);
 

@@ -30,7 +30,9 @@ EXPORTS = (
     "stream_layer_stack_layout", "stream_layer_stack_workspace", "stream_layer_stack_saved_layout",
     "stream_layer_stack_fwd", "stream_layer_stack_bwd", "ql_profile_enable", "ql_profile_read",
 )
-QL_KERNEL_GEMM_FWD, QL_KERNEL_GEMM_BWD = 0, 1
+QL_KERNEL_GEMM_FWD, QL_KERNEL_GEMM_BWD, QL_KERNEL_GEMM_FWD_NARROW, QL_KERNEL_GEMM_BWD_NARROW = 0, 1, 2, 3
+# kernel symbol of each profiling id (the names rocprofv3 reports)
+KERNEL_SYMBOLS = {0: "k_gemm_fwd<64>", 1: "k_gemm_bwd<128>", 2: "k_gemm_fwd<32>", 3: "k_gemm_bwd<64>"}
 
 
 class QlError(RuntimeError):

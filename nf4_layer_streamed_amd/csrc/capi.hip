@@ -507,28 +507,20 @@ static std::vector<ProfRec> g_prof;
 
 bool profiling_on() { return g_prof_on; }
 
-ql_status profile_begin(hipStream_t st, void** token) {
-  ProfRec* r = new ProfRec{};
-  hipError_t e = hipEventCreate(&r->a);
-  if (e == hipSuccess) e = hipEventCreate(&r->b);
-  if (e == hipSuccess) e = hipEventRecord(r->a, st);
-  if (e != hipSuccess) {
-    delete r;
-    return set_error(QL_ERR_HIP, "profiling event: %s", hipGetErrorString(e));
-  }
-  *token = r;
+// The two events are handed to hipExtLaunchKernelGGL, which stamps them at
+// the start and end of the kernel's own dispatch (no separate stream markers).
+// They skip the system-scope fence a default event performs when it
+// completes, which would write back the L2 after every timed kernel.
+ql_status profile_begin(hipEvent_t* start, hipEvent_t* stop) {
+  hipError_t e = hipEventCreateWithFlags(start, hipEventDisableSystemFence);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(stop, hipEventDisableSystemFence);
+  if (e != hipSuccess) return set_error(QL_ERR_HIP, "profiling event: %s", hipGetErrorString(e));
   return QL_OK;
 }
 
-ql_status profile_end(hipStream_t st, void* token, int kernel, double flop) {
-  ProfRec* r = (ProfRec*)token;
-  r->kernel = kernel;
-  r->flop = flop;
-  hipError_t e = hipEventRecord(r->b, st);
+ql_status profile_end(hipEvent_t start, hipEvent_t stop, int kernel, double flop) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof.push_back(*r);
-  delete r;
-  if (e != hipSuccess) return set_error(QL_ERR_HIP, "profiling event: %s", hipGetErrorString(e));
+  g_prof.push_back(ProfRec{start, stop, kernel, flop});
   return QL_OK;
 }
 

@@ -41,6 +41,8 @@
 // Workgroups are mapped XCD-aware: the hardware deals workgroups round-robin
 // to the 8 XCDs, so consecutive logical tiles (the M-tiles of one W tile) are
 // made to land on one XCD and share its L2.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "ql_internal.h"
@@ -887,18 +889,20 @@ ql_status launch_fwd_tiles(const FwdArgs& a, bool wide, hipStream_t st) {
   if (total == 0) return QL_OK;
   const int s1 = a.nseg > 1 ? start[1] : total + 1;
   const int s2 = a.nseg > 2 ? start[2] : total + 1;
-  void* tok = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
   const bool prof = profiling_on();
-  if (prof) QL_TRY_PROF(profile_begin(st, &tok));
+  if (prof) QL_TRY_PROF(profile_begin(&e0, &e1));
   if (wide)
-    hipLaunchKernelGGL(k_gemm_fwd<64>, dim3(total), dim3(NT), fwd_lds<256>(), st, a, tiles_m, total, s1, s2);
+    hipExtLaunchKernelGGL(k_gemm_fwd<64>, dim3(total), dim3(NT), fwd_lds<256>(), st, e0, e1, 0, a, tiles_m, total,
+                          s1, s2);
   else
-    hipLaunchKernelGGL(k_gemm_fwd<32>, dim3(total), dim3(NT), fwd_lds<128>(), st, a, tiles_m, total, s1, s2);
+    hipExtLaunchKernelGGL(k_gemm_fwd<32>, dim3(total), dim3(NT), fwd_lds<128>(), st, e0, e1, 0, a, tiles_m, total,
+                          s1, s2);
   QL_HIP_CHECK(hipGetLastError());
   if (prof) {
     double flop = 0;
     for (int s = 0; s < a.nseg; ++s) flop += 2.0 * (double)a.M * (double)a.seg[s].N * (double)(a.K + a.r);
-    QL_TRY_PROF(profile_end(st, tok, QL_KERNEL_GEMM_FWD, flop));
+    QL_TRY_PROF(profile_end(e0, e1, wide ? QL_KERNEL_GEMM_FWD : QL_KERNEL_GEMM_FWD_NARROW, flop));
   }
   return QL_OK;
 }
@@ -975,18 +979,20 @@ ql_status launch_bwd_tiles(const BwdArgs& a, bool wide, int64_t k_base, int64_t 
   const int bn = wide ? 256 : 128;
   const int total = tiles_m * (int)((k_cols + bn - 1) / bn);
   if (total == 0) return QL_OK;
-  void* tok = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
   const bool prof = profiling_on();
-  if (prof) QL_TRY_PROF(profile_begin(st, &tok));
+  if (prof) QL_TRY_PROF(profile_begin(&e0, &e1));
   if (wide)
-    hipLaunchKernelGGL(k_gemm_bwd<128>, dim3(total), dim3(NT), bwd_lds<256>(), st, a, tiles_m, total, (int)k_base);
+    hipExtLaunchKernelGGL(k_gemm_bwd<128>, dim3(total), dim3(NT), bwd_lds<256>(), st, e0, e1, 0, a, tiles_m, total,
+                          (int)k_base);
   else
-    hipLaunchKernelGGL(k_gemm_bwd<64>, dim3(total), dim3(NT), bwd_lds<128>(), st, a, tiles_m, total, (int)k_base);
+    hipExtLaunchKernelGGL(k_gemm_bwd<64>, dim3(total), dim3(NT), bwd_lds<128>(), st, e0, e1, 0, a, tiles_m, total,
+                          (int)k_base);
   QL_HIP_CHECK(hipGetLastError());
   if (prof) {
     double flop = 0;
     for (int s = 0; s < a.nseg; ++s) flop += 2.0 * (double)a.M * (double)k_cols * (double)(a.seg[s].N + a.r);
-    QL_TRY_PROF(profile_end(st, tok, QL_KERNEL_GEMM_BWD, flop));
+    QL_TRY_PROF(profile_end(e0, e1, wide ? QL_KERNEL_GEMM_BWD : QL_KERNEL_GEMM_BWD_NARROW, flop));
   }
   return QL_OK;
 }

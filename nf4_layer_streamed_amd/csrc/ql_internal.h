@@ -115,8 +115,8 @@ ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st);
 
 // Kernel timing (ql_profile_enable): brackets a launch with events when on.
 bool profiling_on();
-ql_status profile_begin(hipStream_t st, void** token);
-ql_status profile_end(hipStream_t st, void* token, int kernel, double flop);
+ql_status profile_begin(hipEvent_t* start, hipEvent_t* stop);
+ql_status profile_end(hipEvent_t start, hipEvent_t stop, int kernel, double flop);
 ql_status launch_gemm_bwd(const BwdArgs& a, hipStream_t st);
 
 // Skinny NT product with split-K: out_j[m][0..r) = bf16(sum_k X[m][k] * Bt_j[.][k]).
