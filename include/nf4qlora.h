@@ -176,6 +176,11 @@ ql_status qlora_linear_bwd(const void* dy, const void* x, const void* u_saved, i
  * A pageable host store still works, but its copies cannot overlap compute;
  * the call then returns QL_WARN_PAGEABLE_HOST (docs "Layer Streaming":
  * pageable fallback with its cost reported).
+ * Slot ordering: layer l always uses slot l % 2. A streamed call's first copy
+ * waits for all work enqueued before the call on the compute stream (which
+ * may still read the slots), so successive calls may share the slots when
+ * they use the same compute stream; with different compute streams the
+ * caller orders the streams.
  */
 typedef struct {
   int32_t n_layers, hidden, inter, kv_dim, head_dim, r;
@@ -211,11 +216,18 @@ ql_status stream_layer_stack_saved_layout(const ql_stack_cfg* cfg, int64_t M, in
 
 /* Forward over all layers: y (bf16 [M x H]) = stack(x0). lora is a HOST array
  * of n_layers * QL_NPROJ adapters (device A, B; r and alpha must equal cfg's),
- * indexed [layer * QL_NPROJ + proj]. */
+ * indexed [layer * QL_NPROJ + proj].
+ * reuse_bwd_slots != 0 skips the copies of layers 0 and 1, which a
+ * stream_layer_stack_bwd call with the same cfg, store and slots left in the
+ * slots (the training loop's turnaround from one step's backward to the next
+ * step's forward); it requires that nothing wrote the slots since and that
+ * the same compute stream is used (2L - 4 copies per training step with both
+ * reuse flags). Ignored in resident mode. */
 ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
                                  const ql_lora* lora, const void* x0, int64_t M, void* y,
-                                 void* saved, size_t saved_bytes, void* slots, size_t slots_bytes,
-                                 void* ws, size_t ws_bytes, ql_stream compute, ql_stream copy);
+                                 void* saved, size_t saved_bytes, int32_t reuse_bwd_slots,
+                                 void* slots, size_t slots_bytes, void* ws, size_t ws_bytes,
+                                 ql_stream compute, ql_stream copy);
 
 /* Backward over all layers, last to first, from dy (bf16 [M x H]) at the
  * output: dx0 (bf16 [M x H], may be NULL) and dA / dB (HOST arrays of
@@ -223,7 +235,8 @@ ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, siz
  * reuse_fwd_slots != 0 skips the copies of the last two layers, which a
  * stream_layer_stack_fwd call with the same cfg, store and slots left in the
  * slots; it requires that nothing wrote the slots since and that the same
- * compute stream is used (2L-2 copies per forward + backward instead of 2L). */
+ * compute stream is used (2L-2 copies per forward + backward instead of 2L).
+ * Ignored in resident mode. */
 ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
                                  const ql_lora* lora, const void* dy, int64_t M,
                                  const void* saved, size_t saved_bytes, void* dx0,
@@ -238,11 +251,13 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
  * forward, 2 M K (N + r) per reduction segment for dX, over the columns the
  * launch covers). Each kernel comes in a wide-tile (256 x 256 outputs per
  * workgroup) and a narrow-tile (256 x 128) build, timed separately.
- * ql_profile_enable(1) starts a fresh record, ql_profile_enable(0) stops
- * recording. ql_profile_read waits for the recorded events and returns, for
- * one kernel, the number of launches, their summed duration (ms) and summed
- * FLOPs. Results are unaffected by profiling. Not thread-safe against
- * concurrent calls on other threads. */
+ * ql_profile_enable(1) starts a fresh record and reserves a pool of events
+ * (reused across records, so timed launches create none), ql_profile_enable(0)
+ * stops recording. ql_profile_read waits for the recorded events and returns,
+ * for one kernel, the number of launches, their summed duration (ms) and
+ * summed FLOPs. Results are unaffected by profiling. The events belong to the
+ * device current at ql_profile_enable(1). Not thread-safe against concurrent
+ * calls on other threads. */
 enum {
   QL_KERNEL_GEMM_FWD = 0,        /* forward, wide tiles */
   QL_KERNEL_GEMM_BWD = 1,        /* dX, wide tiles */

@@ -82,7 +82,7 @@ def load(path=LIB_PATH):
         "stream_layer_stack_workspace": (I32, [ctypes.POINTER(ql_stack_cfg), I64, ctypes.POINTER(SZ),
                                                ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
         "stream_layer_stack_saved_layout": (I32, [ctypes.POINTER(ql_stack_cfg), I64, P, ctypes.POINTER(SZ)]),
-        "stream_layer_stack_fwd": (I32, [ctypes.POINTER(ql_stack_cfg), P, SZ, P, P, I64, P, P, SZ, P, SZ,
+        "stream_layer_stack_fwd": (I32, [ctypes.POINTER(ql_stack_cfg), P, SZ, P, P, I64, P, P, SZ, I32, P, SZ,
                                          P, SZ, P, P]),
         "stream_layer_stack_bwd": (I32, [ctypes.POINTER(ql_stack_cfg), P, SZ, P, P, I64, P, SZ, P, P, P,
                                          I32, I32, P, SZ, P, SZ, P, P]),
@@ -245,13 +245,14 @@ def _nbytes(t):
     return 0 if t is None else t.numel() * t.element_size()
 
 
-def stream_layer_stack_fwd(cfg, store, lora, x0, M, y, saved, slots, ws, compute=None, copy=None):
+def stream_layer_stack_fwd(cfg, store, lora, x0, M, y, saved, slots, ws, compute=None, copy=None,
+                           reuse_bwd_slots=0):
     """lora: list over layers of {proj: (A, B)} device bf16 tensors."""
     c = cfg.c()
     arr = _lora_array(cfg, lora)
     return _check(load().stream_layer_stack_fwd(
         ctypes.byref(c), _ptr(store), _nbytes(store), arr, _ptr(x0), M, _ptr(y), _ptr(saved), _nbytes(saved),
-        _ptr(slots), _nbytes(slots), _ptr(ws), _nbytes(ws), _stream(compute), _stream(copy)))
+        int(reuse_bwd_slots), _ptr(slots), _nbytes(slots), _ptr(ws), _nbytes(ws), _stream(compute), _stream(copy)))
 
 
 def stream_layer_stack_bwd(cfg, store, lora, dy, M, saved, dx0, dA, dB, accumulate, reuse_fwd_slots, slots, ws,

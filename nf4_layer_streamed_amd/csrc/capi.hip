@@ -416,19 +416,40 @@ static PtrKind pointer_kind(const void* p) {
   return PK_PAGEABLE;
 }
 
+// One layer record host -> device on the copy stream.
+static ql_status copy_record(void* dst, const void* src, size_t bytes, hipStream_t P) {
+  QL_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, P));
+  return QL_OK;
+}
+
 struct Events {
-  hipEvent_t ready[2] = {nullptr, nullptr}, free_[2] = {nullptr, nullptr};
+  hipEvent_t ready[2] = {nullptr, nullptr}, free_[2] = {nullptr, nullptr}, entry = nullptr;
   ~Events() {
     for (int i = 0; i < 2; ++i) {
       if (ready[i]) (void)hipEventDestroy(ready[i]);
       if (free_[i]) (void)hipEventDestroy(free_[i]);
     }
+    if (entry) (void)hipEventDestroy(entry);
   }
+  // `ready` (copy -> compute) keeps the default system-scope fence: the
+  // compute stream must observe bytes the copy engine wrote. `free_` and
+  // `entry` (compute -> copy) only order the copy engine's writes after the
+  // kernels' reads of a slot, so they skip it; with the fence, every layer
+  // boundary would also write back the L2's dirty lines.
   ql_status create() {
     for (int i = 0; i < 2; ++i) {
       QL_HIP_CHECK(hipEventCreateWithFlags(&ready[i], hipEventDisableTiming));
-      QL_HIP_CHECK(hipEventCreateWithFlags(&free_[i], hipEventDisableTiming));
+      QL_HIP_CHECK(hipEventCreateWithFlags(&free_[i], hipEventDisableTiming | hipEventDisableSystemFence));
     }
+    QL_HIP_CHECK(hipEventCreateWithFlags(&entry, hipEventDisableTiming | hipEventDisableSystemFence));
+    return QL_OK;
+  }
+  // The slots may still be read by work enqueued earlier on the compute
+  // stream (the previous streamed call): the copy stream waits for all of it
+  // before this call's first copy.
+  ql_status after_compute(hipStream_t C, hipStream_t P) {
+    QL_HIP_CHECK(hipEventRecord(entry, C));
+    QL_HIP_CHECK(hipStreamWaitEvent(P, entry, 0));
     return QL_OK;
   }
 };
@@ -504,6 +525,21 @@ struct ProfRec {
 static std::mutex g_prof_mu;
 static bool g_prof_on = false;
 static std::vector<ProfRec> g_prof;
+// Events are pooled and reused across recordings, and the pool is filled when
+// recording is switched on, so a timed launch creates nothing (creating events
+// inside a timed region perturbs the concurrent layer copies).
+static std::vector<hipEvent_t> g_pool;
+static size_t g_pool_next = 0;
+constexpr size_t kPoolReserve = 4096;
+
+static ql_status pool_grow(size_t n) {
+  while (g_pool.size() < n) {
+    hipEvent_t e;
+    QL_HIP_CHECK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
+    g_pool.push_back(e);
+  }
+  return QL_OK;
+}
 
 bool profiling_on() { return g_prof_on; }
 
@@ -512,9 +548,10 @@ bool profiling_on() { return g_prof_on; }
 // They skip the system-scope fence a default event performs when it
 // completes, which would write back the L2 after every timed kernel.
 ql_status profile_begin(hipEvent_t* start, hipEvent_t* stop) {
-  hipError_t e = hipEventCreateWithFlags(start, hipEventDisableSystemFence);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(stop, hipEventDisableSystemFence);
-  if (e != hipSuccess) return set_error(QL_ERR_HIP, "profiling event: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  QL_TRY(pool_grow(g_pool_next + 2));
+  *start = g_pool[g_pool_next++];
+  *stop = g_pool[g_pool_next++];
   return QL_OK;
 }
 
@@ -525,12 +562,9 @@ ql_status profile_end(hipEvent_t start, hipEvent_t stop, int kernel, double flop
 }
 
 static void profile_clear() {
-  for (auto& r : g_prof) {
-    (void)hipEventSynchronize(r.b);
-    (void)hipEventDestroy(r.a);
-    (void)hipEventDestroy(r.b);
-  }
+  for (auto& r : g_prof) (void)hipEventSynchronize(r.b);
   g_prof.clear();
+  g_pool_next = 0;
 }
 
 }  // namespace ql
@@ -544,7 +578,10 @@ const char* ql_last_error(void) { return g_err; }
 ql_status ql_profile_enable(int32_t on) {
   clear_error();
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (on) profile_clear();
+  if (on) {
+    profile_clear();
+    QL_TRY(pool_grow(kPoolReserve));
+  }
   g_prof_on = on != 0;
   return QL_OK;
 }
@@ -743,13 +780,15 @@ ql_status stream_layer_stack_saved_layout(const ql_stack_cfg* cfg, int64_t M, in
 
 ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
                                  const ql_lora* lora, const void* x0, int64_t M, void* y, void* saved,
-                                 size_t saved_bytes, void* slots, size_t slots_bytes, void* ws, size_t ws_bytes,
-                                 ql_stream compute, ql_stream copy) {
+                                 size_t saved_bytes, int32_t reuse_bwd_slots, void* slots, size_t slots_bytes,
+                                 void* ws, size_t ws_bytes, ql_stream compute, ql_stream copy) {
   clear_error();
   const char* fn = "stream_layer_stack_fwd";
   StackCall sc;
   QL_TRY(validate_stack(fn, cfg, store, store_bytes, lora, M, saved, saved_bytes, slots, slots_bytes, ws,
                         ws_bytes, sc));
+  if (reuse_bwd_slots != 0 && reuse_bwd_slots != 1)
+    return set_error(QL_ERR_ARG, "%s: reuse_bwd_slots must be 0 or 1", fn);
   if (M > 0) {
     QL_TRY(check_ptr(fn, "x0", x0, 16));
     QL_TRY(check_ptr(fn, "y", y, 16));
@@ -766,11 +805,18 @@ ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, siz
   // layer 0 input into the saved area (the backward reads it)
   QL_HIP_CHECK(hipMemcpyAsync(sv + sc.SV.off[QL_SAVED_H_IN], x0, (size_t)M * H * 2, hipMemcpyDeviceToDevice, C));
   Events ev;
+  // layer l uses slot l % 2; with reuse_bwd_slots the preceding backward left
+  // layers 1 and 0 in their slots
+  bool have_ready[2] = {false, false};
   if (!cfg->resident) {
     QL_TRY(ev.create());
-    for (int l = 0; l < 2 && l < L; ++l) {
-      QL_HIP_CHECK(hipMemcpyAsync(sl8 + l * rec, st8 + l * rec, rec, hipMemcpyHostToDevice, P));
-      QL_HIP_CHECK(hipEventRecord(ev.ready[l], P));
+    if (!reuse_bwd_slots) {
+      QL_TRY(ev.after_compute(C, P));
+      for (int l = 0; l < 2 && l < L; ++l) {
+        QL_TRY(copy_record(sl8 + l * rec, st8 + l * rec, rec, P));
+        QL_HIP_CHECK(hipEventRecord(ev.ready[l], P));
+        have_ready[l] = true;
+      }
     }
   }
   for (int l = 0; l < L; ++l) {
@@ -779,7 +825,7 @@ ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, siz
     if (cfg->resident) {
       base = st8 + l * rec;
     } else {
-      QL_HIP_CHECK(hipStreamWaitEvent(C, ev.ready[slot], 0));
+      if (have_ready[slot]) QL_HIP_CHECK(hipStreamWaitEvent(C, ev.ready[slot], 0));
       base = sl8 + slot * rec;
     }
     uint8_t* svl = sv + (size_t)l * sc.SV.per_layer;
@@ -790,8 +836,9 @@ ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, siz
     if (!cfg->resident && l + 2 < L) {
       QL_HIP_CHECK(hipEventRecord(ev.free_[slot], C));
       QL_HIP_CHECK(hipStreamWaitEvent(P, ev.free_[slot], 0));
-      QL_HIP_CHECK(hipMemcpyAsync(sl8 + slot * rec, st8 + (size_t)(l + 2) * rec, rec, hipMemcpyHostToDevice, P));
+      QL_TRY(copy_record(sl8 + slot * rec, st8 + (size_t)(l + 2) * rec, rec, P));
       QL_HIP_CHECK(hipEventRecord(ev.ready[slot], P));
+      have_ready[slot] = true;
     }
   }
   return sc.pageable ? QL_WARN_PAGEABLE_HOST : QL_OK;
@@ -842,10 +889,11 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
   bool have_ready[2] = {false, false};
   if (streamed) {
     QL_TRY(ev.create());
+    if (!reuse_fwd_slots) QL_TRY(ev.after_compute(C, P));
     for (int i = 0; i < 2 && i < L; ++i) {
       const int l = L - 1 - i;
       if (reuse_fwd_slots) continue;  // the forward left layers L-1 and L-2 in their slots
-      QL_HIP_CHECK(hipMemcpyAsync(sl8 + (l & 1) * rec, st8 + (size_t)l * rec, rec, hipMemcpyHostToDevice, P));
+      QL_TRY(copy_record(sl8 + (l & 1) * rec, st8 + (size_t)l * rec, rec, P));
       QL_HIP_CHECK(hipEventRecord(ev.ready[l & 1], P));
       have_ready[l & 1] = true;
     }
@@ -870,7 +918,7 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
     if (streamed && l - 2 >= 0) {
       QL_HIP_CHECK(hipEventRecord(ev.free_[slot], C));
       QL_HIP_CHECK(hipStreamWaitEvent(P, ev.free_[slot], 0));
-      QL_HIP_CHECK(hipMemcpyAsync(sl8 + slot * rec, st8 + (size_t)(l - 2) * rec, rec, hipMemcpyHostToDevice, P));
+      QL_TRY(copy_record(sl8 + slot * rec, st8 + (size_t)(l - 2) * rec, rec, P));
       QL_HIP_CHECK(hipEventRecord(ev.ready[slot], P));
       have_ready[slot] = true;
     }

@@ -79,39 +79,105 @@ __global__ void k_skinny_reduce(const SkinnyArgs a, const float* __restrict__ pa
 
 int64_t skinny_nsplit(int64_t K) { return (K + SK_SPLIT - 1) / SK_SPLIT; }
 
-// Column reduction: thread = one column c, 16 ranks per pass (blockIdx.z);
-// the chunk's V rows sit in LDS as float32.
-constexpr int CR_COLS = 256;
-constexpr int CR_MAXCHUNK = 256;
+// Column reduction out[j][c] = s * sum_m Z[m][c] V[m][j]. A workgroup owns
+// CR_COLS columns (two per lane: one 4-byte load per row) and one block of
+// rows, 16 ranks per pass (blockIdx.z). Its four waves take interleaved rows;
+// the block's V rows are staged in LDS as float32 (read by broadcast). The
+// waves' sums are combined in LDS in wave order. With one row block the
+// workgroup writes the result; with several, float32 partials go to the
+// workspace and a second pass adds them in block order.
+constexpr int CR_COLS = 128;
+constexpr int CR_SUB = 256;  // V rows staged per LDS round
 
-__global__ __launch_bounds__(256) void k_colred_partial(const ColRedArgs a, int64_t chunk,
+__global__ __launch_bounds__(256) void k_colred_partial(const ColRedArgs a, int64_t rows_per_block, int nblk,
                                                         float* __restrict__ part) {
-  __shared__ float vs[CR_MAXCHUNK][16];
-  const int t = threadIdx.x;
-  const int64_t c = (int64_t)blockIdx.x * CR_COLS + t;
-  const int64_t mb = (int64_t)blockIdx.y * chunk;
-  const int64_t me = mb + chunk < a.M ? mb + chunk : a.M;
+  __shared__ float vs[CR_SUB][16];
+  __shared__ float red[3][CR_COLS][17];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int64_t c = (int64_t)blockIdx.x * CR_COLS + 2 * lane;
+  const int64_t mb = (int64_t)blockIdx.y * rows_per_block;
+  const int64_t me = mb + rows_per_block < a.M ? mb + rows_per_block : a.M;
   const int j0 = blockIdx.z * 16;
-  for (int64_t i = t; i < (me - mb) * 16; i += 256) {
-    const int64_t mi = i >> 4;
-    const int jj = (int)(i & 15);
-    vs[mi][jj] = (j0 + jj < a.r) ? bf16_to_f32(a.V[(mb + mi) * a.r + j0 + jj]) : 0.f;
+  const bool live = c < a.C;
+  // columns c, c + 1 stay inside one head under the repeat_kv remap (C, head_dim even)
+  const int64_t pc = live ? remap_col(c, a.head_dim, a.n_rep) : 0;
+  const uint32_t* zp = (const uint32_t*)(a.Z + pc);
+  const int64_t ldw = a.ldz / 2;
+  float acc0[16], acc1[16];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) acc0[jj] = acc1[jj] = 0.f;
+  for (int64_t sb = mb; sb < me; sb += CR_SUB) {
+    const int64_t se = sb + CR_SUB < me ? sb + CR_SUB : me;
+    __syncthreads();
+    for (int64_t i = t; i < (se - sb) * 16; i += 256) {
+      const int64_t mi = i >> 4;
+      const int jj = (int)(i & 15);
+      vs[mi][jj] = (j0 + jj < a.r) ? bf16_to_f32(a.V[(sb + mi) * a.r + j0 + jj]) : 0.f;
+    }
+    __syncthreads();
+    if (live) {
+      int64_t m = sb + w;
+      for (; m + 12 < se; m += 16) {  // four rows of this wave in flight
+        uint32_t zz[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) zz[u] = zp[(m + 4 * u) * ldw];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float z0 = __builtin_bit_cast(float, zz[u] << 16);
+          const float z1 = __builtin_bit_cast(float, zz[u] & 0xffff0000u);
+          const float* vr = vs[m + 4 * u - sb];
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            acc0[jj] += z0 * vr[jj];
+            acc1[jj] += z1 * vr[jj];
+          }
+        }
+      }
+      for (; m < se; m += 4) {
+        const uint32_t zz = zp[m * ldw];
+        const float z0 = __builtin_bit_cast(float, zz << 16);
+        const float z1 = __builtin_bit_cast(float, zz & 0xffff0000u);
+        const float* vr = vs[m - sb];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          acc0[jj] += z0 * vr[jj];
+          acc1[jj] += z1 * vr[jj];
+        }
+      }
+    }
+  }
+  // waves 1..3 hand their sums to wave 0, which adds them in wave order
+  if (w > 0) {
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      red[w - 1][2 * lane][jj] = acc0[jj];
+      red[w - 1][2 * lane + 1][jj] = acc1[jj];
+    }
   }
   __syncthreads();
-  float acc[16];
+  if (w > 0 || !live) return;
 #pragma unroll
-  for (int jj = 0; jj < 16; ++jj) acc[jj] = 0.f;
-  if (c < a.C) {
-    const int64_t pc = remap_col(c, a.head_dim, a.n_rep);
-    for (int64_t m = mb; m < me; ++m) {
-      const float z = bf16_to_f32(a.Z[m * a.ldz + pc]);
-      const float* vr = vs[m - mb];
+  for (int q = 0; q < 3; ++q)
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) acc[jj] += z * vr[jj];
+    for (int jj = 0; jj < 16; ++jj) {
+      acc0[jj] += red[q][2 * lane][jj];
+      acc1[jj] += red[q][2 * lane + 1][jj];
     }
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj)
-      if (j0 + jj < a.r) part[((int64_t)blockIdx.y * a.r + j0 + jj) * a.C + c] = acc[jj];
+  for (int jj = 0; jj < 16; ++jj) {
+    const int j = j0 + jj;
+    if (j >= a.r) break;
+    if (nblk == 1) {
+      const float v0 = a.s * acc0[jj], v1 = a.s * acc1[jj];
+      const int64_t o0 = a.transpose_out ? c * a.r + j : j * a.C + c;
+      const int64_t o1 = a.transpose_out ? (c + 1) * a.r + j : j * a.C + c + 1;
+      a.out[o0] = a.accumulate ? a.out[o0] + v0 : v0;
+      a.out[o1] = a.accumulate ? a.out[o1] + v1 : v1;
+    } else {
+      float* pp = part + ((int64_t)blockIdx.y * a.r + j) * a.C + c;
+      pp[0] = acc0[jj];
+      pp[1] = acc1[jj];
+    }
   }
 }
 
@@ -126,17 +192,15 @@ __global__ void k_colred_reduce(const ColRedArgs a, const float* __restrict__ pa
   a.out[o] = a.accumulate ? a.out[o] + s : s;
 }
 
-int64_t colred_chunk(int64_t M, int64_t C, int32_t r) {
-  // enough chunks to give ~2048 workgroups, chunks of at most CR_MAXCHUNK rows
-  const int64_t ctiles = (C + CR_COLS - 1) / CR_COLS;
-  const int64_t passes = (r + 15) / 16;
-  int64_t want = 2048 / (ctiles * passes);
-  if (want < 1) want = 1;
-  int64_t chunk = (M + want - 1) / want;
-  chunk = (chunk + 15) / 16 * 16;
-  if (chunk > CR_MAXCHUNK) chunk = CR_MAXCHUNK;
-  if (chunk < 16) chunk = 16;
-  return chunk;
+// Row blocks of a column reduction: enough for about 512 workgroups, at
+// least 64 rows each.
+int colred_blocks(int64_t M, int64_t C, int32_t r) {
+  const int64_t tiles = ((C + CR_COLS - 1) / CR_COLS) * ((r + 15) / 16);
+  int64_t nb = 512 / (tiles > 0 ? tiles : 1);
+  const int64_t maxb = M / 64 > 1 ? M / 64 : 1;
+  if (nb > maxb) nb = maxb;
+  if (nb < 1) nb = 1;
+  return (int)nb;
 }
 
 __global__ void k_transpose_bf16(const uint16_t* __restrict__ in, int64_t rows, int64_t cols,
@@ -181,9 +245,8 @@ ql_status launch_skinny(const SkinnyArgs& a, void* ws, hipStream_t st) {
 }
 
 size_t colred_ws_bytes(int64_t M, int64_t C, int32_t r) {
-  const int64_t chunk = colred_chunk(M, C, r);
-  const int64_t nchunk = (M + chunk - 1) / chunk;
-  return (size_t)nchunk * (size_t)r * (size_t)C * sizeof(float);
+  const int nb = colred_blocks(M, C, r);
+  return nb > 1 ? (size_t)nb * (size_t)r * (size_t)C * sizeof(float) : 0;
 }
 
 ql_status launch_colred(const ColRedArgs& a, void* ws, hipStream_t st) {
@@ -192,15 +255,18 @@ ql_status launch_colred(const ColRedArgs& a, void* ws, hipStream_t st) {
     if (!a.accumulate && n > 0) return launch_zero_f32(a.out, n, st);
     return QL_OK;
   }
-  const int64_t chunk = colred_chunk(a.M, a.C, a.r);
-  const int64_t nchunk = (a.M + chunk - 1) / chunk;
-  dim3 grid((unsigned)((a.C + CR_COLS - 1) / CR_COLS), (unsigned)nchunk, (unsigned)((a.r + 15) / 16));
+  if ((a.C & 1) || (a.ldz & 1) || (a.n_rep > 0 && (a.head_dim & 1)))
+    return set_error(QL_ERR_SHAPE, "colred: column count and row stride must be even");
+  const int nb = colred_blocks(a.M, a.C, a.r);
+  const int64_t rows = (a.M + nb - 1) / nb;
+  dim3 grid((unsigned)((a.C + CR_COLS - 1) / CR_COLS), (unsigned)nb, (unsigned)((a.r + 15) / 16));
   float* part = (float*)ws;
-  hipLaunchKernelGGL(k_colred_partial, grid, dim3(256), 0, st, a, chunk, part);
+  hipLaunchKernelGGL(k_colred_partial, grid, dim3(256), 0, st, a, rows, nb, part);
   QL_HIP_CHECK(hipGetLastError());
-  hipLaunchKernelGGL(k_colred_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, part,
-                     (int)nchunk);
-  QL_HIP_CHECK(hipGetLastError());
+  if (nb > 1) {
+    hipLaunchKernelGGL(k_colred_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, part, nb);
+    QL_HIP_CHECK(hipGetLastError());
+  }
   return QL_OK;
 }
 

@@ -44,11 +44,12 @@ class GpuStack:
         c = ql.StackCfg(**{**self.cfg.__dict__, "resident": int(resident)})
         return c
 
-    def fwd(self, resident=False, store=None):
+    def fwd(self, resident=False, store=None, reuse=False):
         cfg = self.cfg_mode(resident)
         st = store if store is not None else (self.store_dev if resident else self.store)
         return ql.stream_layer_stack_fwd(cfg, st, self.lora, self.x, self.M, self.y, self.saved,
-                                         None if resident else self.slots, self.ws, self.compute, self.copy)
+                                         None if resident else self.slots, self.ws, self.compute, self.copy,
+                                         reuse_bwd_slots=reuse)
 
     def bwd(self, resident=False, reuse=False, store=None, accumulate=False):
         cfg = self.cfg_mode(resident)
@@ -61,6 +62,10 @@ class GpuStack:
         a = self.fwd(resident)
         b = self.bwd(resident, reuse=reuse and not resident)
         return max(a, b)
+
+    def layer_stores(self):
+        """Per-layer {proj: (packed, absmax)} host tensors of this stack's store."""
+        return [{p: (d[p]["packed"], d[p]["absmax"]) for p in ql.PROJ} for d in self.inp["layers"]]
 
     def results(self):
         self.compute.synchronize()

@@ -125,6 +125,40 @@ def test_slot_reuse_at_turnaround_matches_full_copies(smol):
     assert identical(a, b)
 
 
+def test_training_loop_reuses_slots_both_ways(smol):
+    # fwd, then (bwd, fwd) pairs that each skip the two copies the other left
+    # in the slots; the last step must equal the resident step bitwise
+    smol.fwd()
+    for _ in range(2):
+        smol.bwd(reuse=True)
+        smol.fwd(reuse=True)
+    smol.bwd(reuse=True)
+    streamed = smol.results()
+    smol.step(resident=True)
+    assert identical(streamed, smol.results())
+
+
+def test_two_stores_share_slots_without_sync(smol):
+    # a second store (the layers in reverse order) through the same slots right
+    # after the first, with no host synchronisation in between: the second
+    # call's first copies must wait for the first call's compute
+    other = ql.build_store(smol.cfg, smol.layer_stores()[::-1], pinned=True)
+    other_dev = other.to(DEV)
+    smol.fwd(store=smol.store_dev, resident=True)
+    torch.cuda.synchronize()
+    y_first_resident = smol.y.clone()
+    smol.fwd(store=other_dev, resident=True)
+    torch.cuda.synchronize()
+    y_other_resident = smol.y.clone()
+    smol.fwd()
+    with torch.cuda.stream(smol.compute):
+        y_first = smol.y.clone()
+    smol.fwd(store=other)
+    torch.cuda.synchronize()
+    assert torch.equal(y_first.view(torch.uint8), y_first_resident.view(torch.uint8))
+    assert torch.equal(smol.y.view(torch.uint8), y_other_resident.view(torch.uint8))
+
+
 def test_pageable_store_warns_and_matches(smol):
     smol.step(resident=False, reuse=True)
     pinned = smol.results()
