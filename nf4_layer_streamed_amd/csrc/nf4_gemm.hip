@@ -26,8 +26,8 @@
 // rows 8 i + 4 g + j for accumulator 4 i + j.
 //
 // Forward layout: 256 x BN outputs per workgroup of 4 waves side by side along
-// N (each wave 256 x BN/4). X tiles (256 rows x 64) go through LDS (two stages,
-// rows of 128 B with the 16-B chunks XOR-swizzled by row); each wave decodes
+// N (each wave 256 x BN/4). X tiles (256 rows x 64) go through LDS (rows of
+// 128 B with the 16-B chunks XOR-swizzled by row); each wave decodes
 // its own W rows straight into MFMA B registers, so W never touches LDS and
 // each weight is decoded once per workgroup.
 //
@@ -60,7 +60,17 @@ constexpr int BM = 256;
 constexpr int BK = 64;
 constexpr int A_TILE = BM * BK * 2;  // 32 KB: 256 rows x 128 B
 
-__device__ __forceinline__ int swz_a(int row, int chunk) { return (row << 7) + ((chunk ^ (row & 7)) << 4); }
+// A tile rows are 128 B (8 chunks of 16 B); chunk c of row r is stored at
+// chunk c ^ f(r). The forward GEMM uses f(r) = (r ^ (r >> 3)) mod 8: its
+// fragment reads (32 consecutive rows, one chunk per lane half) then run at
+// about twice the LDS throughput of f(r) = r mod 8 in isolation, and the
+// kernel gains a few percent. The backward GEMM keeps f(r) = r mod 8, which
+// times a few percent faster there (its reads interleave with the decode's
+// LDS traffic differently).
+template <bool XS>
+__device__ __forceinline__ int swz_row(int row) { return (XS ? row ^ (row >> 3) : row) & 7; }
+template <bool XS>
+__device__ __forceinline__ int swz_a(int row, int chunk) { return (row << 7) + ((chunk ^ swz_row<XS>(row)) << 4); }
 
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t n) {
   const uint32_t q = n >> 3, rem = n & 7;
@@ -169,15 +179,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int v
 
 // A tile (256 rows x 64 bf16) by DMA: wave w moves 1-KB blocks b = 4 i + w
 // (rows 8 b .. 8 b + 7); lane l fills row 8 b + l / 8 at physical chunk l % 8,
-// which holds logical chunk (l % 8) ^ (l / 8) under the row swizzle.
-__device__ __forceinline__ int dma_voff(int lane, int w, int ldx) {
-  const int row = 8 * w + (lane >> 3);
-  const int lc = (lane & 7) ^ (lane >> 3);
-  return row * ldx * 2 + lc * 16;
-}
-__device__ __forceinline__ void dma_a_tile(__amdgpu_buffer_rsrc_t r, uint8_t* As, int voff0, int ldx, int w, int soff) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) dma16(r, As + (4 * i + w) * 1024, voff0 + i * 32 * ldx * 2, soff);
+// which holds logical chunk (l % 8) ^ swz_row(8 b + l / 8): (l % 8) ^ (l / 8)
+// for f(r) = r mod 8; with the XOR of r >> 3 also ^ (b mod 8), where b mod 8
+// is w for even i and w + 4 for odd i.
+template <bool XS>
+__device__ __forceinline__ int dma_chunk(int lane, int w, int odd) {
+  return (lane & 7) ^ (lane >> 3) ^ (XS ? w + 4 * odd : 0);
 }
 
 // A tile of the LoRA step: rows of a [M x r] bf16 matrix, zero past r (outside the main loop).
@@ -208,11 +215,12 @@ __device__ __forceinline__ void load_a_rank(uint4 (&ar)[8], const uint16_t* U, i
 
 // Thread t moves chunks c = t + 256 i (i < 8) of a 256 x 64 A tile: row
 // (t >> 3) + 32 i, 16-byte chunk t & 7.
+template <bool XS>
 __device__ __forceinline__ void store_a(uint8_t* As, const uint4 (&ar)[8], int t) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = t + NT * i;
-    *(uint4*)(As + swz_a(c >> 3, c & 7)) = ar[i];
+    *(uint4*)(As + swz_a<XS>(c >> 3, c & 7)) = ar[i];
   }
 }
 
@@ -278,7 +286,10 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
   const __amdgpu_buffer_rsrc_t cr = rsrc(S.packed + n0 * (K / 2), wrows * (K / 2));
   const __amdgpu_buffer_rsrc_t sr = rsrc(S.absmax + n0 * kb, wrows * kb * 4);
   const int ldx = __builtin_amdgcn_readfirstlane((int)a.ldx);
-  const int xvoff = dma_voff(lane, w, ldx);
+  // lane's source offset for even / odd DMA blocks (the logical chunk differs)
+  const int xrow = 8 * w + (lane >> 3);
+  const int xvoff0 = xrow * ldx * 2 + dma_chunk<true>(lane, w, 0) * 16;
+  const int xvoff1 = xrow * ldx * 2 + dma_chunk<true>(lane, w, 1) * 16;
   // codes: DMA instruction c moves rows 32 c .. 32 c + 31 (lane l: row 32 c + l / 2,
   // bytes 16 (l % 2) ..), landing contiguously at CODES + 1024 c
   const int cvoff = (lane >> 1) * (int)(K / 2) + 16 * (lane & 1);
@@ -314,7 +325,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
     uint8_t* st = stage(step);
     if (h == 0) sc = xcol_next();
 #pragma unroll
-    for (int i = 4 * h; i < 4 * h + 4; ++i) dma16(xr, st + (4 * i + w) * 1024, xvoff + i * 32 * ldx * 2, sc);
+    for (int i = 4 * h; i < 4 * h + 4; ++i)
+      dma16(xr, st + (4 * i + w) * 1024, ((i & 1) ? xvoff1 : xvoff0) + i * 32 * ldx * 2, sc);
     if (h == 0) {
 #pragma unroll
       for (int cc = 0; cc < BN / 128; ++cc) {
@@ -377,7 +389,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
   uint4 bq[NTW], bn[NTW];
   auto read_a = [&](bf16x8_t (&dst)[8], const uint8_t* As, int q) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = *(const bf16x8_t*)(As + swz_a(i * 32 + li, 4 * g + q));
+    for (int i = 0; i < 8; ++i) dst[i] = *(const bf16x8_t*)(As + swz_a<true>(i * 32 + li, 4 * g + q));
   };
   auto mma_step = [&](int step, auto has_next_c, auto dma_c) {
     constexpr bool has_next = decltype(has_next_c)::value;
@@ -458,7 +470,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
     mma_step(step, std::false_type{}, std::false_type{});
     uint4 ar[8];
     load_a_rank(ar, S.U, a.r, M, m0, t);
-    store_a(stage(step + 1), ar, t);
+    store_a<true>(stage(step + 1), ar, t);
     __syncthreads();
   }
   // LoRA step: [U | 0] [s B | 0]^T
@@ -476,7 +488,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
     for (int q = 0; q < 4; ++q) {
       bf16x8_t a8[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a8[i] = *(const bf16x8_t*)(As + swz_a(i * 32 + li, 4 * g + q));
+      for (int i = 0; i < 8; ++i) a8[i] = *(const bf16x8_t*)(As + swz_a<true>(i * 32 + li, 4 * g + q));
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -614,17 +626,18 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
 
   // dY tile (256 rows x 64 columns of segment sgA from nbA) into an A stage;
   // columns past the segment's N read as zeros (offset past the buffer).
-  const int arow = 8 * w + (lane >> 3), alc = (lane & 7) ^ (lane >> 3);
+  const int arow = 8 * w + (lane >> 3), alc0 = dma_chunk<false>(lane, w, 0), alc1 = dma_chunk<false>(lane, w, 1);
   auto dma_a = [&](uint8_t* As) {
     const int64_t N = sel3(sgA, N0, N1, N2);
     const __amdgpu_buffer_rsrc_t yr = sel3(sgA, yr0, yr1, yr2);
     const int ldy = __builtin_amdgcn_readfirstlane((int)N);
     const int ylim = __builtin_amdgcn_readfirstlane((int)(xrows * N * 2));
     // all-ones where the lane's 8 columns lie past N (branch-free select)
-    const int past = -(int)(nbA + 8 * alc >= N);
+    const int past0 = -(int)(nbA + 8 * alc0 >= N), past1 = -(int)(nbA + 8 * alc1 >= N);
     const int so = __builtin_amdgcn_readfirstlane(nbA * 2);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      const int alc = (i & 1) ? alc1 : alc0, past = (i & 1) ? past1 : past0;
       const int vo = (((arow + 32 * i) * ldy * 2 + alc * 16) & ~past) | (ylim & past);
       dma16(yr, As + (4 * i + w) * 1024, vo, so);
     }
@@ -682,7 +695,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
   bf16x8_t af[4], an[4], bfr[4][NTW];
   auto read_a = [&](bf16x8_t (&fa)[4], const uint8_t* As, int q) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8_t*)(As + swz_a(wm * 128 + i * 32 + li, 2 * q + g));
+    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8_t*)(As + swz_a<false>(wm * 128 + i * 32 + li, 2 * q + g));
   };
   // Weight fragments of sub-step q, read transposed. The transposing LDS read
   // carries no type information, and the compiler then waits for every LDS
@@ -776,7 +789,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
     uint8_t* Bs = smem + OFF_D + (sg & 1) * DEC_BYTES;
     uint4 ar[8];
     load_a_rank(ar, S.G, a.r, M, m0, t);
-    store_a(As, ar, t);
+    store_a<false>(As, ar, t);
     if (dthread) {
       const bool live = drow < a.r && dk < K;
       const uint4* src = (const uint4*)(S.A + (int64_t)drow * K + dk);
