@@ -241,9 +241,13 @@ constexpr int vm_lgkm_wait(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3)
 constexpr int FWD_STAGES = 3;
 // One forward LDS stage: the X tile (256 rows x 128 B, swizzled), the codes of
 // the workgroup's BN weight rows for one K-step (BN rows x 32 B) and their
-// absmax (256 floats; rows past BN are loaded as zeros and never read).
+// absmax (256 floats; rows past BN are loaded as zeros and never read). The
+// three X tiles come first, then the three code + scale blocks, so that the
+// fragment reads of stages 0 and 1 fit the 16-bit LDS offset field.
 template <int BN>
-constexpr int fwd_stage_bytes() { return A_TILE + BN * 32 + 1024; }
+constexpr int fwd_cs_bytes() { return BN * 32 + 1024; }
+template <int BN>
+constexpr int fwd_stage_bytes() { return A_TILE + fwd_cs_bytes<BN>(); }
 
 // DMA of 4-byte elements: lane l's word lands at lds + 4 * l.
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
@@ -252,18 +256,20 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, int vo
 
 // WN: columns per wave (64 or 32); workgroup tile 256 x (4 WN).
 // Every global read of the K-loop is a buffer-to-LDS DMA issued two K-steps
-// ahead into a three-stage ring: while step s computes from stage s mod 3,
-// step s + 2's X tile, codes and scales stream into stage (s + 2) mod 3. A
-// barrier between sub-steps 2 and 3 of step s certifies step s + 1's data
-// (each wave first waits for its own DMAs of it) and that no wave still reads
-// stage s mod 3's neighbour that is refilled next.
+// ahead into a three-stage ring: while step s computes from stage
+// (s - r) mod 3, step s + 2's X tile, codes and scales stream into the stage
+// after the next. A barrier between sub-steps 2 and 3 of step s certifies step
+// s + 1's data (each wave first waits for its own DMAs of it) and that no wave
+// still reads the stage that is refilled next. The offset r = (KT - 2) mod 3
+// aligns the stages so that the K-loop unrolls by three with every stage
+// offset a compile-time constant and the last two steps use stages 0 and 1.
 template <int WN>
 __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m, int tiles_total,
                                                     int seg_tile0_1, int seg_tile0_2) {
   constexpr int NTW = WN / 32;
   constexpr int BN = 4 * WN;
-  constexpr int STAGE = fwd_stage_bytes<BN>();
-  constexpr int CODES = A_TILE, SCALES = A_TILE + BN * 32;
+  constexpr int CSB = fwd_cs_bytes<BN>();
+  constexpr int SCALES = BN * 32;  // within a code + scale block
   // DMA instructions per wave per K-step: 8 for X, BN / 128 for codes, 1 for scales
   constexpr int NDMA = 8 + BN / 128 + 1;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -291,7 +297,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
   const int xvoff0 = xrow * ldx * 2 + dma_chunk<true>(lane, w, 0) * 16;
   const int xvoff1 = xrow * ldx * 2 + dma_chunk<true>(lane, w, 1) * 16;
   // codes: DMA instruction c moves rows 32 c .. 32 c + 31 (lane l: row 32 c + l / 2,
-  // bytes 16 (l % 2) ..), landing contiguously at CODES + 1024 c
+  // bytes 16 (l % 2) ..), landing contiguously at 1024 c of the code block
   const int cvoff = (lane >> 1) * (int)(K / 2) + 16 * (lane & 1);
   // scales: wave w moves rows 64 w + lane, landing at SCALES + 256 w
   const int svoff = (64 * w + lane) * (int)kb * 4;
@@ -315,15 +321,21 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
     hq += wrap2 ? 1 : 0;
     return c;
   };
-  auto stage = [&](int s) -> uint8_t* { return smem + (s % FWD_STAGES) * STAGE; };
+  // stage si: X tile at A_of(si), codes and scales at CS_of(si)
+  auto A_of = [&](int si) -> uint8_t* { return smem + si * A_TILE; };
+  auto CS_of = [&](int si) -> uint8_t* { return smem + FWD_STAGES * A_TILE + si * CSB; };
+  const int KT2 = KT - 2;
+  const int roff = (KT2 % 3 + 3) % 3;
+  auto stage_of = [&](int s) { return (s - roff + 3) % 3; };
 
-  // DMA part h (0 or 1) of K-step `step` into its stage: half of the X tile
+  // DMA part h (0 or 1) of K-step `step` into stage si: half of the X tile
   // (1-KB blocks 4 i + w, i in [4 h, 4 h + 4)); part 0 also moves the codes
   // and scales. Steps are DMAed in order.
   int sc = 0;
-  auto dma_part = [&](int step, int h) {
-    uint8_t* st = stage(step);
-    if (h == 0) sc = xcol_next();
+  auto dma_part = [&](int step, int h, int si) {
+    uint8_t* st = A_of(si);
+    uint8_t* cs = CS_of(si);
+    if (h == 0) sc = __builtin_amdgcn_readfirstlane(xcol_next());
 #pragma unroll
     for (int i = 4 * h; i < 4 * h + 4; ++i)
       dma16(xr, st + (4 * i + w) * 1024, ((i & 1) ? xvoff1 : xvoff0) + i * 32 * ldx * 2, sc);
@@ -331,9 +343,9 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
 #pragma unroll
       for (int cc = 0; cc < BN / 128; ++cc) {
         const int c = w + 4 * cc;
-        dma16(cr, st + CODES + 1024 * c, cvoff + 32 * c * (int)(K / 2), step * 32);
+        dma16(cr, cs + 1024 * c, cvoff + 32 * c * (int)(K / 2), step * 32);
       }
-      dma4(sr, st + SCALES + 256 * w, svoff, step * 4);
+      dma4(sr, cs + SCALES + 256 * w, svoff, step * 4);
     }
   };
 
@@ -345,23 +357,23 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
 
   uint4 bcur[NTW];
   Lut lut[NTW];
-  const int code_lane = CODES + (w * WN + li) * 32 + 16 * g;
+  const int code_lane = (w * WN + li) * 32 + 16 * g;
   auto decoded = [&](int j, int q) { return decode8(word(bcur[j], q), lut[j]); };
-  // Codes and block tables of the K-step in stage st. (All LDS reads of the
+  // Codes and block tables of the K-step whose code block is cs. (All LDS reads of the
   // K-loop are typed loads; ordering against the DMAs is carried by the
   // explicit waits before each barrier.) Lane (li, g) takes the
   // 16 code bytes 16 g.. of rows w WN + 32 j + li. With two row groups the
   // lanes g = 0 and 1 hold the same rows, so each builds the table of one
   // (row group g) and the halves swap them (v_permlane32_swap: lanes 32..63 of
   // the first operand trade places with lanes 0..31 of the second).
-  auto tables = [&](const uint8_t* st) {
+  auto tables = [&](const uint8_t* cs) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
-      const u32x4_t v = *(const u32x4_t*)(st + code_lane + 1024 * j);
+      const u32x4_t v = *(const u32x4_t*)(cs + code_lane + 1024 * j);
       bcur[j] = make_uint4(v[0], v[1], v[2], v[3]);
     }
     if constexpr (NTW == 2) {
-      const float sc_own = *(const float*)(st + SCALES + 4 * (w * WN + 32 * g + li));
+      const float sc_own = *(const float*)(cs + SCALES + 4 * (w * WN + 32 * g + li));
       const Lut own = make_lut(sc_own);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -373,33 +385,35 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
         lut[1].hi[e] = xh[1];
       }
     } else {
-      lut[0] = make_lut(*(const float*)(st + SCALES + 4 * (w * WN + li)));
+      lut[0] = make_lut(*(const float*)(cs + SCALES + 4 * (w * WN + li)));
     }
   };
 
-  // One K-step of MFMAs on the stage of `step`. Sub-step q's MFMAs overlap the
-  // LDS reads and B decode of sub-step q + 1. HAS_NEXT: between sub-steps 2
-  // and 3 the workgroup meets at a barrier (every wave's reads of this stage
-  // done, its DMAs of step + 1 landed), after which sub-step 3 prefetches step
-  // + 1's first A fragments, codes and tables, so the next step starts without
-  // waiting. DMA: step + 2's data is issued in sub-steps 0 and 1 into the stage
-  // read last in step - 1. Scheduling groups pin the interleaving (LDS reads
-  // first, then MFMA / VMEM / VALU alternating).
+  // One K-step of MFMAs on stage SI (a compile-time constant). Sub-step q's
+  // MFMAs overlap the LDS reads and B decode of sub-step q + 1. HAS_NEXT:
+  // between sub-steps 2 and 3 the workgroup meets at a barrier (every wave's
+  // reads of this stage done, its DMAs of step + 1 landed), after which
+  // sub-step 3 prefetches step + 1's first A fragments, codes and tables from
+  // stage SI + 1, so the next step starts without waiting. DMA: step + 2's
+  // data is issued in sub-steps 0 and 1 into stage SI + 2, read last in step
+  // - 1. Scheduling groups pin the interleaving (LDS reads first, then MFMA /
+  // VMEM / VALU alternating).
   bf16x8_t af[8], an[8];
   uint4 bq[NTW], bn[NTW];
   auto read_a = [&](bf16x8_t (&dst)[8], const uint8_t* As, int q) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) dst[i] = *(const bf16x8_t*)(As + swz_a<true>(i * 32 + li, 4 * g + q));
   };
-  auto mma_step = [&](int step, auto has_next_c, auto dma_c) {
+  auto mma_step = [&](int step, auto si_c, auto has_next_c, auto dma_c) {
+    constexpr int SI = decltype(si_c)::value;
     constexpr bool has_next = decltype(has_next_c)::value;
     constexpr bool dma = decltype(dma_c)::value;
-    const uint8_t* As = stage(step);
+    const uint8_t* As = A_of(SI);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       int nvm = 0;
       if (dma && q < 2) {
-        dma_part(step + 2, q);
+        dma_part(step + 2, q, (SI + 2) % 3);
         nvm = q == 0 ? NDMA - 4 : 4;
       }
       if (q < 3) {
@@ -407,9 +421,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
 #pragma unroll
         for (int j = 0; j < NTW; ++j) bn[j] = decoded(j, q + 1);
       } else if constexpr (has_next) {
-        const uint8_t* nx = stage(step + 1);
-        read_a(an, nx, 0);
-        tables(nx);
+        read_a(an, A_of((SI + 1) % 3), 0);
+        tables(CS_of((SI + 1) % 3));
 #pragma unroll
         for (int j = 0; j < NTW; ++j) bn[j] = decoded(j, 0);
       }
@@ -444,33 +457,52 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
   };
 
   // prologue: steps 0 and 1 in flight; step 0's operands ready
-  dma_part(0, 0);
-  dma_part(0, 1);
+  dma_part(0, 0, stage_of(0));
+  dma_part(0, 1, stage_of(0));
   if (KT > 1) {
-    dma_part(1, 0);
-    dma_part(1, 1);
+    dma_part(1, 0, stage_of(1));
+    dma_part(1, 1, stage_of(1));
     __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(NDMA));
   } else {
     __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
   }
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  read_a(af, stage(0), 0);
-  tables(stage(0));
+  read_a(af, A_of(stage_of(0)), 0);
+  tables(CS_of(stage_of(0)));
 #pragma unroll
   for (int j = 0; j < NTW; ++j) bq[j] = decoded(j, 0);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // steps 0 .. KT - 3 issue DMAs; the first roff of them bring the rest to a
+  // multiple of three
   int step = 0;
-  for (; step + 2 < KT; ++step) mma_step(step, std::true_type{}, std::true_type{});
-  if (step + 1 < KT) {
-    mma_step(step, std::true_type{}, std::false_type{});
+  if (roff == 1 && KT2 >= 1) {
+    mma_step(0, S2{}, T_{}, T_{});
+    step = 1;
+  } else if (roff == 2 && KT2 >= 2) {
+    mma_step(0, S1{}, T_{}, T_{});
+    mma_step(1, S2{}, T_{}, T_{});
+    step = 2;
+  }
+  for (; step < KT2; step += 3) {
+    mma_step(step, S0{}, T_{}, T_{});
+    mma_step(step + 1, S1{}, T_{}, T_{});
+    mma_step(step + 2, S2{}, T_{}, T_{});
+  }
+  if (KT > 1) {  // step KT - 2, stage 0
+    mma_step(step, S0{}, T_{}, F_{});
     ++step;
   }
-  {  // last weight step; the LoRA step's A tile (U) goes to the next stage,
+  {  // last weight step (stage 1); the LoRA step's A tile (U) goes to stage 2,
      // last read two steps ago (before the barrier of the previous step)
-    mma_step(step, std::false_type{}, std::false_type{});
+    mma_step(step, S1{}, F_{}, F_{});
     uint4 ar[8];
     load_a_rank(ar, S.U, a.r, M, m0, t);
-    store_a<true>(stage(step + 1), ar, t);
+    store_a<true>(A_of(2), ar, t);
     __syncthreads();
   }
   // LoRA step: [U | 0] [s B | 0]^T
@@ -483,7 +515,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
       for (int q = 0; q < 4; ++q)
         lb[j][q] = n < N ? lora_row8(S.B + n * a.r, 32 * g + 8 * q, a.r, a.s) : make_uint4(0, 0, 0, 0);
     }
-    const uint8_t* As = stage(step + 1);
+    const uint8_t* As = A_of(2);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       bf16x8_t a8[8];
