@@ -22,8 +22,13 @@ the whole step (M tokens per step). The JSON line also carries:
   (2.5166 PFLOP/s); `traffic` is its
   HBM bytes per launch from the committed counter summary (null if the kernel
   sources changed since). gemm_all: all fused-GEMM launches together.
+* dense_bf16_gemm - same-session practical ceiling: torch's dense bf16 GEMM
+  (hipBLASLt) on pre-dequantised weights at the stack's forward and dX
+  shapes; gemm_all.vs_dense_bf16 is the fused NF4 GEMMs' rate over it.
 * pcie - H2D bytes per step over the step time, against 64 GB/s (PCIe Gen5
   x16 per direction) and a same-session pinned-copy ceiling.
+* ring8 - the same streamed step with 8 device slots instead of 2 (each
+  turnaround then reuses 8 layers: 2 (L - 8) copies per step).
 * resident - the same step with the store resident in HBM (no copies).
 * cpu_baseline - the CPU oracle timed on a bounded sample.
 """
@@ -106,6 +111,42 @@ def build_inputs(ql, synth, torch, w, dev):
     return cfg, store, offs, lora, x, dy
 
 
+def dense_gemm_ceiling(torch, dev, M, w, reps=10):
+    """Same-session practical ceiling for the fused NF4 GEMMs: torch's dense
+    bf16 GEMM (hipBLASLt) on weights that are already bf16 in HBM, over the
+    stack's forward shapes (y = x W^T: q|k|v, o, gate|up, down) and dX shapes
+    (dX = dY W: v, o, gate|up, down), FLOP-weighted like one step's mix."""
+    H, I, KV = w["H"], w["I"], w["KV"]
+    fwd = [(H + 2 * KV, H), (H, H), (2 * I, H), (H, I)]     # (N, K)
+    bwd = [(KV, H), (H, H), (2 * I, H), (H, I)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    ops = []
+    for N, K in fwd:
+        x = torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16)
+        wt = torch.randn(K, N, device=dev, generator=g).to(torch.bfloat16)   # W^T, contiguous
+        ops.append((x, wt, 2.0 * M * N * K))
+    for N, K in bwd:
+        dy = torch.randn(M, N, device=dev, generator=g).to(torch.bfloat16)
+        wn = torch.randn(N, K, device=dev, generator=g).to(torch.bfloat16)   # W, contiguous
+        ops.append((dy, wn, 2.0 * M * N * K))
+    for a_, b_, _ in ops:
+        torch.mm(a_, b_)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for a_, b_, _ in ops:
+            torch.mm(a_, b_)
+    e1.record()
+    torch.cuda.synchronize()
+    flop = reps * sum(f for _, _, f in ops)
+    tf = flop / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del ops
+    return dict(tflops=round(tf, 1), frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                what="torch.mm bf16 (hipBLASLt), weights pre-dequantised in HBM, stack fwd+dX shapes at M=%d" % M)
+
+
 def cpu_baseline(rows=2048, layers=3):
     """The oracle on a bounded sample: the first `layers` layers of the 8B
     stack with all 2048 tokens (or `rows` of them), forward + backward in
@@ -186,9 +227,9 @@ def main():
     copy = torch.cuda.Stream(dev)
 
     def step(c, st, turnaround):
-        # a training step: the forward reuses the two layers the previous
-        # step's backward left in the slots (turnaround), the backward the two
-        # the forward left
+        # a training step: the forward reuses the layers the previous step's
+        # backward left in the slots (turnaround), the backward those the
+        # forward left
         streamed = not c.resident
         s1 = ql.stream_layer_stack_fwd(c, st, lora, x, M, y, saved, slots if streamed else None, ws,
                                        compute, copy, reuse_bwd_slots=int(streamed and turnaround))
@@ -281,6 +322,23 @@ def main():
                 same_session_h2d_GBs=round(h2d_ceiling, 2), bytes_per_step=h2d_bytes,
                 copies_per_step=copies, record_bytes=rec)
 
+    # the same step with a deeper slot ring (the docs' stream_buffers up to 8):
+    # each turnaround reuses 8 layers, so 2 (L - 8) copies per step
+    log(f"bench: 8-slot ring, {args.steps} streamed steps")
+    cfg8 = ql.StackCfg(**{**cfg.__dict__, "n_buffers": 8})
+    slots8 = torch.empty(ql.stream_layer_stack_workspace(cfg8, M)[0], dtype=torch.uint8, device=dev)
+    slots_main = slots
+    slots = slots8
+    t8, _, _ = timed(cfg8, store, args.steps, args.warmup, False)
+    slots = slots_main
+    del slots8
+    ms8 = 1000.0 * t8 / args.steps
+    ring8 = dict(n_buffers=8, value=round(M * args.steps / t8, 1), unit="tok/s", ms_per_step=round(ms8, 3),
+                 copies_per_step=2 * (w["L"] - 8), pcie_GBs=round(2 * (w["L"] - 8) * rec / (ms8 * 1e-3) / 1e9, 2))
+
+    dense = dense_gemm_ceiling(torch, dev, M, w)
+    gemm_all["vs_dense_bf16"] = round(gemm_all["tflops"] / dense["tflops"], 4)
+
     resident = None
     if not args.no_resident:
         log("bench: resident ablation (store in HBM, no copies)")
@@ -321,7 +379,9 @@ def main():
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kern.items()},
         "roofline": roofline,
+        "dense_bf16_gemm": dense,
         "pcie": pcie,
+        "ring8": ring8,
         "resident": resident,
         "cpu_baseline": cpu,
     }

@@ -176,16 +176,26 @@ ql_status qlora_linear_bwd(const void* dy, const void* x, const void* u_saved, i
  * A pageable host store still works, but its copies cannot overlap compute;
  * the call then returns QL_WARN_PAGEABLE_HOST (docs "Layer Streaming":
  * pageable fallback with its cost reported).
- * Slot ordering: layer l always uses slot l % 2. A streamed call's first copy
+ * Slots: n_buffers device records (2..QL_MAX_BUFFERS; the docs' buffer count
+ * for layer streaming, "Layer Streaming" section of performance-and-
+ * quantization, whose default is double buffering). Layer l always uses slot
+ * l % n_buffers; after computing layer l the forward refills its slot with
+ * layer l + n_buffers and the backward with layer l - n_buffers, so up to
+ * n_buffers - 1 copies run ahead of the compute stream. Reusing the slots at
+ * a turnaround (reuse_bwd_slots / reuse_fwd_slots) skips n_buffers copies, so
+ * a steady-state fwd + bwd step makes 2 (n_layers - n_buffers) copies.
+ * Slot ordering: a streamed call's first copy
  * waits for all work enqueued before the call on the compute stream (which
  * may still read the slots), so successive calls may share the slots when
  * they use the same compute stream; with different compute streams the
  * caller orders the streams.
  */
+#define QL_MAX_BUFFERS 8
+
 typedef struct {
   int32_t n_layers, hidden, inter, kv_dim, head_dim, r;
   float alpha, rms_eps;
-  int32_t n_buffers;  /* device slots; must be 2 */
+  int32_t n_buffers;  /* device slots, 2..QL_MAX_BUFFERS (2: double buffering) */
   int32_t resident;   /* 0: host store, streamed; 1: device store, no copies */
 } ql_stack_cfg;
 
@@ -217,12 +227,12 @@ ql_status stream_layer_stack_saved_layout(const ql_stack_cfg* cfg, int64_t M, in
 /* Forward over all layers: y (bf16 [M x H]) = stack(x0). lora is a HOST array
  * of n_layers * QL_NPROJ adapters (device A, B; r and alpha must equal cfg's),
  * indexed [layer * QL_NPROJ + proj].
- * reuse_bwd_slots != 0 skips the copies of layers 0 and 1, which a
- * stream_layer_stack_bwd call with the same cfg, store and slots left in the
- * slots (the training loop's turnaround from one step's backward to the next
- * step's forward); it requires that nothing wrote the slots since and that
- * the same compute stream is used (2L - 4 copies per training step with both
- * reuse flags). Ignored in resident mode. */
+ * reuse_bwd_slots != 0 skips the copies of layers 0 .. n_buffers - 1, which
+ * a stream_layer_stack_bwd call with the same cfg, store and slots left in
+ * the slots (the training loop's turnaround from one step's backward to the
+ * next step's forward); it requires that nothing wrote the slots since and
+ * that the same compute stream is used (2 (L - n_buffers) copies per training
+ * step with both reuse flags). Ignored in resident mode. */
 ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
                                  const ql_lora* lora, const void* x0, int64_t M, void* y,
                                  void* saved, size_t saved_bytes, int32_t reuse_bwd_slots,
@@ -232,11 +242,10 @@ ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, siz
 /* Backward over all layers, last to first, from dy (bf16 [M x H]) at the
  * output: dx0 (bf16 [M x H], may be NULL) and dA / dB (HOST arrays of
  * n_layers * QL_NPROJ device float32 pointers, [r x K] and [N x r]).
- * reuse_fwd_slots != 0 skips the copies of the last two layers, which a
- * stream_layer_stack_fwd call with the same cfg, store and slots left in the
- * slots; it requires that nothing wrote the slots since and that the same
- * compute stream is used (2L-2 copies per forward + backward instead of 2L).
- * Ignored in resident mode. */
+ * reuse_fwd_slots != 0 skips the copies of the last n_buffers layers, which
+ * a stream_layer_stack_fwd call with the same cfg, store and slots left in
+ * the slots; it requires that nothing wrote the slots since and that the same
+ * compute stream is used. Ignored in resident mode. */
 ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
                                  const ql_lora* lora, const void* dy, int64_t M,
                                  const void* saved, size_t saved_bytes, void* dx0,

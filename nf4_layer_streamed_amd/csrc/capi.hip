@@ -116,8 +116,8 @@ static ql_status check_cfg(const char* fn, const ql_stack_cfg* c) {
                      "%s: kv_dim (%d) must be a multiple of head_dim (%d) that divides hidden (%d)", fn,
                      c->kv_dim, c->head_dim, c->hidden);
   if (c->r < 1 || c->r > 64) return set_error(QL_ERR_RANK, "%s: r (%d) must be in 1..64", fn, c->r);
-  if (c->n_buffers != 2)
-    return set_error(QL_ERR_UNSUPPORTED, "%s: n_buffers (%d) must be 2 (double buffering)", fn, c->n_buffers);
+  if (c->n_buffers < 2 || c->n_buffers > QL_MAX_BUFFERS)
+    return set_error(QL_ERR_UNSUPPORTED, "%s: n_buffers (%d) must be in 2..%d", fn, c->n_buffers, QL_MAX_BUFFERS);
   if (c->resident != 0 && c->resident != 1)
     return set_error(QL_ERR_ARG, "%s: resident (%d) must be 0 or 1", fn, c->resident);
   if (!(c->rms_eps > 0.f) || !(c->alpha == c->alpha))
@@ -423,9 +423,10 @@ static ql_status copy_record(void* dst, const void* src, size_t bytes, hipStream
 }
 
 struct Events {
-  hipEvent_t ready[2] = {nullptr, nullptr}, free_[2] = {nullptr, nullptr}, entry = nullptr;
+  hipEvent_t ready[QL_MAX_BUFFERS] = {}, free_[QL_MAX_BUFFERS] = {}, entry = nullptr;
+  int n = 0;
   ~Events() {
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < n; ++i) {
       if (ready[i]) (void)hipEventDestroy(ready[i]);
       if (free_[i]) (void)hipEventDestroy(free_[i]);
     }
@@ -436,8 +437,9 @@ struct Events {
   // `entry` (compute -> copy) only order the copy engine's writes after the
   // kernels' reads of a slot, so they skip it; with the fence, every layer
   // boundary would also write back the L2's dirty lines.
-  ql_status create() {
-    for (int i = 0; i < 2; ++i) {
+  ql_status create(int nbuf) {
+    n = nbuf;
+    for (int i = 0; i < n; ++i) {
       QL_HIP_CHECK(hipEventCreateWithFlags(&ready[i], hipEventDisableTiming));
       QL_HIP_CHECK(hipEventCreateWithFlags(&free_[i], hipEventDisableTiming | hipEventDisableSystemFence));
     }
@@ -472,7 +474,7 @@ static ql_status validate_stack(const char* fn, const ql_stack_cfg* cfg, const v
   sc.SV = saved_layout(cfg, M);
   sc.WS = stack_ws(cfg, M);
   sc.store_need = (size_t)sc.SL.rec * cfg->n_layers;
-  sc.slots_need = cfg->resident ? 0 : (size_t)sc.SL.rec * 2;
+  sc.slots_need = cfg->resident ? 0 : (size_t)sc.SL.rec * cfg->n_buffers;
   sc.saved_need = sc.SV.per_layer * cfg->n_layers;
   if (!store) return set_error(QL_ERR_ARG, "%s: store is NULL", fn);
   if (!aligned(store, 256)) return set_error(QL_ERR_ALIGN, "%s: store must be 256-byte aligned", fn);
@@ -488,8 +490,8 @@ static ql_status validate_stack(const char* fn, const ql_stack_cfg* cfg, const v
     if (!slots) return set_error(QL_ERR_ARG, "%s: slots is NULL", fn);
     if (!aligned(slots, 256)) return set_error(QL_ERR_ALIGN, "%s: slots must be 256-byte aligned", fn);
     if (slots_bytes < sc.slots_need)
-      return set_error(QL_ERR_WORKSPACE, "%s: slots_bytes (%zu) < 2 layer records (%zu)", fn, slots_bytes,
-                       sc.slots_need);
+      return set_error(QL_ERR_WORKSPACE, "%s: slots_bytes (%zu) < n_buffers (%d) layer records (%zu)", fn,
+                       slots_bytes, cfg->n_buffers, sc.slots_need);
   }
   if (M > 0) {
     if (!saved) return set_error(QL_ERR_ARG, "%s: saved is NULL", fn);
@@ -760,7 +762,7 @@ ql_status stream_layer_stack_workspace(const ql_stack_cfg* cfg, int64_t M, size_
   QL_TRY(check_cfg("stream_layer_stack_workspace", cfg));
   if (M < 0) return set_error(QL_ERR_SHAPE, "stream_layer_stack_workspace: M must be >= 0");
   StackLayout SL = stack_layout(cfg);
-  if (slots_bytes) *slots_bytes = cfg->resident ? 0 : (size_t)SL.rec * 2;
+  if (slots_bytes) *slots_bytes = cfg->resident ? 0 : (size_t)SL.rec * cfg->n_buffers;
   if (saved_bytes) *saved_bytes = saved_layout(cfg, M).per_layer * cfg->n_layers;
   if (ws_bytes) *ws_bytes = stack_ws(cfg, M).total;
   return QL_OK;
@@ -805,14 +807,15 @@ ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, siz
   // layer 0 input into the saved area (the backward reads it)
   QL_HIP_CHECK(hipMemcpyAsync(sv + sc.SV.off[QL_SAVED_H_IN], x0, (size_t)M * H * 2, hipMemcpyDeviceToDevice, C));
   Events ev;
-  // layer l uses slot l % 2; with reuse_bwd_slots the preceding backward left
-  // layers 1 and 0 in their slots
-  bool have_ready[2] = {false, false};
+  // layer l uses slot l % nb; with reuse_bwd_slots the preceding backward
+  // left layers nb - 1 .. 0 in their slots
+  const int nb = cfg->n_buffers;
+  bool have_ready[QL_MAX_BUFFERS] = {};
   if (!cfg->resident) {
-    QL_TRY(ev.create());
+    QL_TRY(ev.create(nb));
     if (!reuse_bwd_slots) {
       QL_TRY(ev.after_compute(C, P));
-      for (int l = 0; l < 2 && l < L; ++l) {
+      for (int l = 0; l < nb && l < L; ++l) {
         QL_TRY(copy_record(sl8 + l * rec, st8 + l * rec, rec, P));
         QL_HIP_CHECK(hipEventRecord(ev.ready[l], P));
         have_ready[l] = true;
@@ -820,7 +823,7 @@ ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, siz
     }
   }
   for (int l = 0; l < L; ++l) {
-    const int slot = l & 1;
+    const int slot = l % nb;
     const uint8_t* base;
     if (cfg->resident) {
       base = st8 + l * rec;
@@ -833,10 +836,10 @@ ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, siz
                                   : (uint16_t*)y;
     QL_TRY(layer_fwd(cfg, sc.SL, layer_weights(sc.SL, base), lora + l * QL_NPROJ, M, sc.SV, svl, h_out, w8,
                      sc.WS, C));
-    if (!cfg->resident && l + 2 < L) {
+    if (!cfg->resident && l + nb < L) {
       QL_HIP_CHECK(hipEventRecord(ev.free_[slot], C));
       QL_HIP_CHECK(hipStreamWaitEvent(P, ev.free_[slot], 0));
-      QL_TRY(copy_record(sl8 + slot * rec, st8 + (size_t)(l + 2) * rec, rec, P));
+      QL_TRY(copy_record(sl8 + slot * rec, st8 + (size_t)(l + nb) * rec, rec, P));
       QL_HIP_CHECK(hipEventRecord(ev.ready[slot], P));
       have_ready[slot] = true;
     }
@@ -885,24 +888,25 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
   const size_t rec = (size_t)sc.SL.rec;
   Events ev;
   const bool streamed = !cfg->resident;
-  // layers L-1, L-2, ... ; layer l uses slot l % 2 (the forward's mapping)
-  bool have_ready[2] = {false, false};
+  // layers L-1, L-2, ... ; layer l uses slot l % nb (the forward's mapping)
+  const int nb = cfg->n_buffers;
+  bool have_ready[QL_MAX_BUFFERS] = {};
   if (streamed) {
-    QL_TRY(ev.create());
+    QL_TRY(ev.create(nb));
     if (!reuse_fwd_slots) QL_TRY(ev.after_compute(C, P));
-    for (int i = 0; i < 2 && i < L; ++i) {
+    for (int i = 0; i < nb && i < L; ++i) {
       const int l = L - 1 - i;
-      if (reuse_fwd_slots) continue;  // the forward left layers L-1 and L-2 in their slots
-      QL_TRY(copy_record(sl8 + (l & 1) * rec, st8 + (size_t)l * rec, rec, P));
-      QL_HIP_CHECK(hipEventRecord(ev.ready[l & 1], P));
-      have_ready[l & 1] = true;
+      if (reuse_fwd_slots) continue;  // the forward left layers L-1 .. L-nb in their slots
+      QL_TRY(copy_record(sl8 + (l % nb) * rec, st8 + (size_t)l * rec, rec, P));
+      QL_HIP_CHECK(hipEventRecord(ev.ready[l % nb], P));
+      have_ready[l % nb] = true;
     }
   }
   uint16_t* dhA = (uint16_t*)(w8 + sc.WS.dhA);
   uint16_t* dhB = (uint16_t*)(w8 + sc.WS.dhB);
   const uint16_t* dh = (const uint16_t*)dy;
   for (int l = L - 1; l >= 0; --l) {
-    const int slot = l & 1;
+    const int slot = l % nb;
     const uint8_t* base;
     if (!streamed) {
       base = st8 + (size_t)l * rec;
@@ -915,10 +919,10 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
                      sv + (size_t)l * sc.SV.per_layer, dh, out, dA + l * QL_NPROJ, dB + l * QL_NPROJ,
                      accumulate, w8, sc.WS, C));
     dh = out;
-    if (streamed && l - 2 >= 0) {
+    if (streamed && l - nb >= 0) {
       QL_HIP_CHECK(hipEventRecord(ev.free_[slot], C));
       QL_HIP_CHECK(hipStreamWaitEvent(P, ev.free_[slot], 0));
-      QL_TRY(copy_record(sl8 + slot * rec, st8 + (size_t)(l - 2) * rec, rec, P));
+      QL_TRY(copy_record(sl8 + slot * rec, st8 + (size_t)(l - nb) * rec, rec, P));
       QL_HIP_CHECK(hipEventRecord(ev.ready[slot], P));
       have_ready[slot] = true;
     }

@@ -9,7 +9,7 @@ from gpu_util import DEV, f64, ql
 
 
 class GpuStack:
-    def __init__(self, name, L=None, M=None, gen_device="cpu", pinned=True, resident_copy=True):
+    def __init__(self, name, L=None, M=None, gen_device="cpu", pinned=True, resident_copy=True, n_buffers=2):
         w = dict(synth.WORKLOADS[name])
         if L is not None:
             w["L"] = L
@@ -18,7 +18,8 @@ class GpuStack:
         self.w = w
         self.name = name
         self.M = w["M"]
-        self.cfg = ql.StackCfg(w["L"], w["H"], w["I"], w["KV"], w["head_dim"], w["r"], w["alpha"])
+        self.cfg = ql.StackCfg(w["L"], w["H"], w["I"], w["KV"], w["head_dim"], w["r"], w["alpha"],
+                               n_buffers=n_buffers)
         inp = synth.stack_inputs(w["L"], w["M"], w["H"], w["I"], w["KV"], w["r"], (name,), device=gen_device)
         self.inp = inp
         stores = [{p: (d[p]["packed"], d[p]["absmax"]) for p in ql.PROJ} for d in inp["layers"]]
@@ -43,6 +44,12 @@ class GpuStack:
     def cfg_mode(self, resident):
         c = ql.StackCfg(**{**self.cfg.__dict__, "resident": int(resident)})
         return c
+
+    def set_buffers(self, n):
+        """Use n device slots from now on (the slot memory must hold n records)."""
+        offs, _, _ = ql.stream_layer_stack_layout(self.cfg)
+        assert n * offs[1] <= self.slots.numel()
+        self.cfg = ql.StackCfg(**{**self.cfg.__dict__, "n_buffers": n})
 
     def fwd(self, resident=False, store=None, reuse=False):
         cfg = self.cfg_mode(resident)

@@ -114,6 +114,9 @@ def test_stack_layout_sizes(name, L, H, I, KV, d, r):
     assert all(spans[i][1] <= spans[i + 1][0] for i in range(len(spans) - 1))
     slots, saved, ws = ql.stream_layer_stack_workspace(cfg, 512)
     assert slots == 2 * rec
+    for nb in (3, 8):   # n_buffers slots of one record each (docs: stream_buffers in [2, 8])
+        c = ql.StackCfg(**{**cfg.__dict__, "n_buffers": nb})
+        assert ql.stream_layer_stack_workspace(c, 512)[0] == nb * rec
     offs_s, per = ql.stream_layer_stack_saved_layout(cfg, 512)
     assert saved == per * L
 
@@ -122,8 +125,10 @@ def test_stack_cfg_validation():
     lib()
     bad = [ql.StackCfg(0, 576, 1536, 192, 64, 8, 16.0), ql.StackCfg(2, 577, 1536, 192, 64, 8, 16.0),
            ql.StackCfg(2, 576, 1536, 200, 64, 8, 16.0), ql.StackCfg(2, 576, 1536, 192, 64, 0, 16.0),
-           ql.StackCfg(2, 576, 1536, 192, 64, 8, 16.0, n_buffers=3)]
-    want = [ql.QL_ERR_SHAPE, ql.QL_ERR_SHAPE, ql.QL_ERR_SHAPE, ql.QL_ERR_RANK, ql.QL_ERR_UNSUPPORTED]
+           ql.StackCfg(2, 576, 1536, 192, 64, 8, 16.0, n_buffers=1),
+           ql.StackCfg(2, 576, 1536, 192, 64, 8, 16.0, n_buffers=9)]
+    want = [ql.QL_ERR_SHAPE, ql.QL_ERR_SHAPE, ql.QL_ERR_SHAPE, ql.QL_ERR_RANK, ql.QL_ERR_UNSUPPORTED,
+            ql.QL_ERR_UNSUPPORTED]
     for cfg, st in zip(bad, want):
         with pytest.raises(ql.QlError) as e:
             ql.stream_layer_stack_layout(cfg)

@@ -200,6 +200,60 @@ def test_slot_memory_is_two_layer_records(smol):
     assert smol.slots.numel() == 2 * offs[1]
 
 
+@pytest.fixture(scope="module")
+def smol8():
+    require_gpu()
+    return GpuStack("smollm2_stack", n_buffers=8)
+
+
+@pytest.mark.parametrize("nb", [3, 5, 8])
+def test_deeper_ring_training_loop_equals_resident(smol8, nb):
+    # the pages expose 2..8 stream buffers; with n slots layer l uses slot
+    # l % n, the prefetch runs n - 1 layers ahead and each turnaround reuses n
+    # layers: fwd, then (bwd, fwd) pairs reusing the slots, must equal the
+    # resident step bitwise
+    smol8.set_buffers(nb)
+    assert smol8.fwd() == ql.QL_OK
+    for _ in range(2):
+        assert smol8.bwd(reuse=True) == ql.QL_OK
+        assert smol8.fwd(reuse=True) == ql.QL_OK
+    assert smol8.bwd(reuse=True) == ql.QL_OK
+    streamed = smol8.results()
+    smol8.step(resident=True)
+    assert identical(streamed, smol8.results())
+    # and without reuse (every call copies its first n layers itself)
+    smol8.fwd()
+    smol8.bwd(reuse=False)
+    assert identical(streamed, smol8.results())
+
+
+def test_deeper_ring_slot_memory(smol8):
+    offs, _, _ = ql.stream_layer_stack_layout(smol8.cfg)
+    for nb in (2, 5, 8):
+        c = ql.StackCfg(**{**smol8.cfg.__dict__, "n_buffers": nb})
+        assert ql.stream_layer_stack_workspace(c, smol8.M)[0] == nb * offs[1]
+    # slot memory for fewer records than n_buffers is refused before anything runs
+    smol8.set_buffers(8)
+    with pytest.raises(ql.QlError) as e:
+        ql.stream_layer_stack_fwd(smol8.cfg, smol8.store, smol8.lora, smol8.x, smol8.M, smol8.y, smol8.saved,
+                                  smol8.slots[: 7 * offs[1]], smol8.ws, smol8.compute, smol8.copy)
+    assert e.value.status == ql.QL_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("L,nb", [(5, 8), (8, 8), (9, 4)])
+def test_ring_longer_than_or_equal_to_stack(L, nb):
+    # fewer layers than slots: every layer is copied once in the prologue
+    require_gpu()
+    s = GpuStack("smollm2_stack", L=L, M=64, n_buffers=nb)
+    assert s.fwd() == ql.QL_OK
+    assert s.bwd(reuse=True) == ql.QL_OK
+    assert s.fwd(reuse=True) == ql.QL_OK
+    assert s.bwd(reuse=True) == ql.QL_OK
+    got = s.results()
+    s.step(resident=True)
+    assert identical(got, s.results())
+
+
 @pytest.mark.parametrize("L,M", [(1, 77), (3, 1)])
 def test_small_stacks_ragged_rows(L, M):
     require_gpu()
