@@ -29,6 +29,9 @@ the whole step (M tokens per step). The JSON line also carries:
   x16 per direction) and a same-session pinned-copy ceiling.
 * ring8 - the same streamed step with 8 device slots instead of 2 (each
   turnaround then reuses 8 layers: 2 (L - 8) copies per step).
+* with_reference - a preference-training step: the policy forward and the
+  adapter-off reference forward in one pass over the streamed layers, then
+  the backward (no extra copies for the reference).
 * resident - the same step with the store resident in HBM (no copies).
 * cpu_baseline - the CPU oracle timed on a bounded sample.
 """
@@ -336,6 +339,31 @@ def main():
     ring8 = dict(n_buffers=8, value=round(M * args.steps / t8, 1), unit="tok/s", ms_per_step=round(ms8, 3),
                  copies_per_step=2 * (w["L"] - 8), pcie_GBs=round(2 * (w["L"] - 8) * rec / (ms8 * 1e-3) / 1e9, 2))
 
+    # preference-training step: policy + adapter-off reference forward in one
+    # pass over the streamed layers, then the backward (same copies per step)
+    log(f"bench: step with the reference forward, {args.steps} streamed steps")
+    _, per_layer = ql.stream_layer_stack_saved_layout(cfg, M)
+    ref_scratch = torch.empty(per_layer, dtype=torch.uint8, device=dev)
+    ref_y = torch.empty(M, w["H"], dtype=torch.bfloat16, device=dev)
+
+    def pref_step(turnaround):
+        s1 = ql.stream_layer_stack_fwd_ref(cfg, store, lora, x, M, y, saved, ref_y, ref_scratch, slots, ws,
+                                           compute, copy, reuse_bwd_slots=int(turnaround))
+        s2 = ql.stream_layer_stack_bwd(cfg, store, lora, dy, M, saved, dx, dA, dB, 0, 1, slots, ws, compute, copy)
+        return max(s1, s2)
+
+    for i in range(args.warmup):
+        pref_step(i > 0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        pref_step(True)
+    torch.cuda.synchronize()
+    tr = time.perf_counter() - t0
+    with_ref = dict(value=round(M * args.steps / tr, 1), unit="tok/s", ms_per_step=round(1000 * tr / args.steps, 3),
+                    copies_per_step=copies, note="policy + adapter-off reference forward share each layer copy")
+    del ref_scratch, ref_y
+
     dense = dense_gemm_ceiling(torch, dev, M, w)
     gemm_all["vs_dense_bf16"] = round(gemm_all["tflops"] / dense["tflops"], 4)
 
@@ -382,6 +410,7 @@ def main():
         "dense_bf16_gemm": dense,
         "pcie": pcie,
         "ring8": ring8,
+        "with_reference": with_ref,
         "resident": resident,
         "cpu_baseline": cpu,
     }

@@ -239,6 +239,28 @@ ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, siz
                                  void* slots, size_t slots_bytes, void* ws, size_t ws_bytes,
                                  ql_stream compute, ql_stream copy);
 
+/* Policy forward plus the adapter-off reference forward, in one pass over the
+ * layers. For preference losses the reference model is the same streamed
+ * frozen base with the adapters switched off, which on the pages costs extra
+ * layer reads (the aiany.app entry "Soup", section "How It Works"). Here each
+ * streamed layer, once in its slot, serves both forwards before the slot is
+ * refilled, so the reference adds compute but no host-to-device copies.
+ * y, saved: exactly those of stream_layer_stack_fwd with the same arguments
+ * (bitwise). ref_y (bf16 [M x H]): the stack's output with every LoRA term
+ * removed (y = x W^T per projection), on the same x0. ref_scratch: one
+ * layer's saved activations (per_layer_bytes of
+ * stream_layer_stack_saved_layout), overwritten; its contents afterwards are
+ * unspecified. lora == NULL: the reference alone (y and saved are then not
+ * used and may be NULL). reuse_bwd_slots and the slot ordering are as in
+ * stream_layer_stack_fwd, so a following stream_layer_stack_bwd may reuse the
+ * slots this call leaves. */
+ql_status stream_layer_stack_fwd_ref(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
+                                     const ql_lora* lora, const void* x0, int64_t M, void* y,
+                                     void* saved, size_t saved_bytes, void* ref_y, void* ref_scratch,
+                                     size_t ref_scratch_bytes, int32_t reuse_bwd_slots, void* slots,
+                                     size_t slots_bytes, void* ws, size_t ws_bytes,
+                                     ql_stream compute, ql_stream copy);
+
 /* Backward over all layers, last to first, from dy (bf16 [M x H]) at the
  * output: dx0 (bf16 [M x H], may be NULL) and dA / dB (HOST arrays of
  * n_layers * QL_NPROJ device float32 pointers, [r x K] and [N x r]).

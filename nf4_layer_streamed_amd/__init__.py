@@ -28,7 +28,8 @@ EXPORTS = (
     "ql_last_error", "ql_abi_version", "nf4_codebook", "nf4_quantize", "nf4_dequant",
     "qlora_linear_workspace", "qlora_linear_fwd", "qlora_linear_bwd",
     "stream_layer_stack_layout", "stream_layer_stack_workspace", "stream_layer_stack_saved_layout",
-    "stream_layer_stack_fwd", "stream_layer_stack_bwd", "ql_profile_enable", "ql_profile_read",
+    "stream_layer_stack_fwd", "stream_layer_stack_fwd_ref", "stream_layer_stack_bwd", "ql_profile_enable",
+    "ql_profile_read",
 )
 QL_KERNEL_GEMM_FWD, QL_KERNEL_GEMM_BWD, QL_KERNEL_GEMM_FWD_NARROW, QL_KERNEL_GEMM_BWD_NARROW = 0, 1, 2, 3
 # kernel symbol of each profiling id (the names rocprofv3 reports)
@@ -84,6 +85,8 @@ def load(path=LIB_PATH):
         "stream_layer_stack_saved_layout": (I32, [ctypes.POINTER(ql_stack_cfg), I64, P, ctypes.POINTER(SZ)]),
         "stream_layer_stack_fwd": (I32, [ctypes.POINTER(ql_stack_cfg), P, SZ, P, P, I64, P, P, SZ, I32, P, SZ,
                                          P, SZ, P, P]),
+        "stream_layer_stack_fwd_ref": (I32, [ctypes.POINTER(ql_stack_cfg), P, SZ, P, P, I64, P, P, SZ, P, P, SZ,
+                                             I32, P, SZ, P, SZ, P, P]),
         "stream_layer_stack_bwd": (I32, [ctypes.POINTER(ql_stack_cfg), P, SZ, P, P, I64, P, SZ, P, P, P,
                                          I32, I32, P, SZ, P, SZ, P, P]),
         "ql_profile_enable": (I32, [I32]),
@@ -253,6 +256,19 @@ def stream_layer_stack_fwd(cfg, store, lora, x0, M, y, saved, slots, ws, compute
     return _check(load().stream_layer_stack_fwd(
         ctypes.byref(c), _ptr(store), _nbytes(store), arr, _ptr(x0), M, _ptr(y), _ptr(saved), _nbytes(saved),
         int(reuse_bwd_slots), _ptr(slots), _nbytes(slots), _ptr(ws), _nbytes(ws), _stream(compute), _stream(copy)))
+
+
+def stream_layer_stack_fwd_ref(cfg, store, lora, x0, M, y, saved, ref_y, ref_scratch, slots, ws, compute=None,
+                               copy=None, reuse_bwd_slots=0):
+    """Policy forward (lora: as stream_layer_stack_fwd, or None for the
+    reference alone) and the adapter-off reference forward into ref_y, sharing
+    each layer's copy."""
+    c = cfg.c()
+    arr = _lora_array(cfg, lora) if lora is not None else None
+    return _check(load().stream_layer_stack_fwd_ref(
+        ctypes.byref(c), _ptr(store), _nbytes(store), arr, _ptr(x0), M, _ptr(y), _ptr(saved), _nbytes(saved),
+        _ptr(ref_y), _ptr(ref_scratch), _nbytes(ref_scratch), int(reuse_bwd_slots), _ptr(slots), _nbytes(slots),
+        _ptr(ws), _nbytes(ws), _stream(compute), _stream(copy)))
 
 
 def stream_layer_stack_bwd(cfg, store, lora, dy, M, saved, dx0, dA, dB, accumulate, reuse_fwd_slots, slots, ws,

@@ -219,18 +219,22 @@ static LayerW layer_weights(const StackLayout& L, const uint8_t* base) {
 static inline const uint16_t* u16(const void* p) { return (const uint16_t*)p; }
 static inline uint16_t* u16w(void* p) { return (uint16_t*)p; }
 
+// One layer's forward. lo == nullptr: the adapters are off (the base model,
+// x W^T only): no LoRA-down launches and no LoRA step in the GEMMs; the U
+// entries of sv are left untouched.
 static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const LayerW& W,
                            const ql_lora* lo, int64_t M, const SavedLayout& SV, uint8_t* sv,
                            uint16_t* h_out, uint8_t* ws, const StackWs& WS, hipStream_t st) {
   const int64_t H = c->hidden, I = c->inter, KV = c->kv_dim;
-  const int r = c->r;
-  const float s = c->alpha / (float)r;
+  const bool on = lo != nullptr;
+  const int r = on ? c->r : 0;
+  const float s = on ? c->alpha / (float)c->r : 0.f;
   auto S = [&](int i) { return (uint16_t*)(sv + SV.off[i]); };
   void* scratch = ws + WS.scratch;
   const uint16_t* h_in = S(QL_SAVED_H_IN);
 
   QL_TRY(launch_rmsnorm_fwd(h_in, M, H, c->rms_eps, S(QL_SAVED_N1), st));
-  {  // LoRA down of q, k, v (they share n1)
+  if (on) {  // LoRA down of q, k, v (they share n1)
     SkinnyArgs a{};
     a.X = S(QL_SAVED_N1); a.M = M; a.K = H; a.ldx = H; a.r = r; a.nseg = 3;
     for (int p = 0; p < 3; ++p) { a.Bt[p] = u16(lo[p].A); a.out[p] = S(QL_SAVED_U0 + p); }
@@ -242,7 +246,8 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     const int outs[3] = {QL_SAVED_Q, QL_SAVED_K, QL_SAVED_V};
     for (int p = 0; p < 3; ++p) {
       FwdSeg& g = a.seg[p];
-      g.packed = W.packed[p]; g.absmax = W.absmax[p]; g.U = S(QL_SAVED_U0 + p); g.B = u16(lo[p].B);
+      g.packed = W.packed[p]; g.absmax = W.absmax[p];
+      g.U = on ? S(QL_SAVED_U0 + p) : nullptr; g.B = on ? u16(lo[p].B) : nullptr;
       g.out = S(outs[p]); g.N = SL.N[p]; g.ldo = SL.N[p]; g.col0 = 0; g.resid = nullptr;
     }
     QL_TRY(launch_gemm_fwd(a, st));
@@ -251,30 +256,36 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
   {  // o: input a = repeat_kv(v) read through the column remap; residual h_in
     SkinnyArgs u{};
     u.X = S(QL_SAVED_V); u.M = M; u.K = H; u.ldx = KV; u.head_dim = c->head_dim; u.n_rep = n_rep;
-    u.r = r; u.nseg = 1; u.Bt[0] = u16(lo[QL_PROJ_O].A); u.out[0] = S(QL_SAVED_U0 + QL_PROJ_O);
-    QL_TRY(launch_skinny(u, scratch, st));
+    if (on) {
+      u.r = r; u.nseg = 1; u.Bt[0] = u16(lo[QL_PROJ_O].A); u.out[0] = S(QL_SAVED_U0 + QL_PROJ_O);
+      QL_TRY(launch_skinny(u, scratch, st));
+    }
     FwdArgs a{};
     a.X = S(QL_SAVED_V); a.M = M; a.K = H; a.ldx = KV; a.head_dim = c->head_dim; a.n_rep = n_rep;
     a.r = r; a.s = s; a.nseg = 1;
     FwdSeg& g = a.seg[0];
-    g.packed = W.packed[QL_PROJ_O]; g.absmax = W.absmax[QL_PROJ_O]; g.U = S(QL_SAVED_U0 + QL_PROJ_O);
-    g.B = u16(lo[QL_PROJ_O].B); g.out = S(QL_SAVED_H_MID); g.N = H; g.ldo = H; g.resid = h_in;
+    g.packed = W.packed[QL_PROJ_O]; g.absmax = W.absmax[QL_PROJ_O];
+    g.U = on ? S(QL_SAVED_U0 + QL_PROJ_O) : nullptr; g.B = on ? u16(lo[QL_PROJ_O].B) : nullptr;
+    g.out = S(QL_SAVED_H_MID); g.N = H; g.ldo = H; g.resid = h_in;
     QL_TRY(launch_gemm_fwd(a, st));
   }
   QL_TRY(launch_rmsnorm_fwd(S(QL_SAVED_H_MID), M, H, c->rms_eps, S(QL_SAVED_N2), st));
   {  // gate | up
     SkinnyArgs u{};
-    u.X = S(QL_SAVED_N2); u.M = M; u.K = H; u.ldx = H; u.r = r; u.nseg = 2;
-    u.Bt[0] = u16(lo[QL_PROJ_GATE].A); u.out[0] = S(QL_SAVED_U0 + QL_PROJ_GATE);
-    u.Bt[1] = u16(lo[QL_PROJ_UP].A); u.out[1] = S(QL_SAVED_U0 + QL_PROJ_UP);
-    QL_TRY(launch_skinny(u, scratch, st));
+    if (on) {
+      u.X = S(QL_SAVED_N2); u.M = M; u.K = H; u.ldx = H; u.r = r; u.nseg = 2;
+      u.Bt[0] = u16(lo[QL_PROJ_GATE].A); u.out[0] = S(QL_SAVED_U0 + QL_PROJ_GATE);
+      u.Bt[1] = u16(lo[QL_PROJ_UP].A); u.out[1] = S(QL_SAVED_U0 + QL_PROJ_UP);
+      QL_TRY(launch_skinny(u, scratch, st));
+    }
     FwdArgs a{};
     a.X = S(QL_SAVED_N2); a.M = M; a.K = H; a.ldx = H; a.r = r; a.s = s; a.nseg = 2;
     const int outs[2] = {QL_SAVED_GATE, QL_SAVED_UP};
     for (int q = 0; q < 2; ++q) {
       const int p = QL_PROJ_GATE + q;
       FwdSeg& g = a.seg[q];
-      g.packed = W.packed[p]; g.absmax = W.absmax[p]; g.U = S(QL_SAVED_U0 + p); g.B = u16(lo[p].B);
+      g.packed = W.packed[p]; g.absmax = W.absmax[p];
+      g.U = on ? S(QL_SAVED_U0 + p) : nullptr; g.B = on ? u16(lo[p].B) : nullptr;
       g.out = S(outs[q]); g.N = I; g.ldo = I; g.resid = nullptr;
     }
     QL_TRY(launch_gemm_fwd(a, st));
@@ -282,14 +293,16 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
   QL_TRY(launch_swiglu_fwd(S(QL_SAVED_GATE), S(QL_SAVED_UP), M * I, S(QL_SAVED_ACT), st));
   {  // down, residual h_mid
     SkinnyArgs u{};
-    u.X = S(QL_SAVED_ACT); u.M = M; u.K = I; u.ldx = I; u.r = r; u.nseg = 1;
-    u.Bt[0] = u16(lo[QL_PROJ_DOWN].A); u.out[0] = S(QL_SAVED_U0 + QL_PROJ_DOWN);
-    QL_TRY(launch_skinny(u, scratch, st));
+    if (on) {
+      u.X = S(QL_SAVED_ACT); u.M = M; u.K = I; u.ldx = I; u.r = r; u.nseg = 1;
+      u.Bt[0] = u16(lo[QL_PROJ_DOWN].A); u.out[0] = S(QL_SAVED_U0 + QL_PROJ_DOWN);
+      QL_TRY(launch_skinny(u, scratch, st));
+    }
     FwdArgs a{};
     a.X = S(QL_SAVED_ACT); a.M = M; a.K = I; a.ldx = I; a.r = r; a.s = s; a.nseg = 1;
     FwdSeg& g = a.seg[0];
     g.packed = W.packed[QL_PROJ_DOWN]; g.absmax = W.absmax[QL_PROJ_DOWN];
-    g.U = S(QL_SAVED_U0 + QL_PROJ_DOWN); g.B = u16(lo[QL_PROJ_DOWN].B);
+    g.U = on ? S(QL_SAVED_U0 + QL_PROJ_DOWN) : nullptr; g.B = on ? u16(lo[QL_PROJ_DOWN].B) : nullptr;
     g.out = h_out; g.N = H; g.ldo = H; g.resid = S(QL_SAVED_H_MID);
     QL_TRY(launch_gemm_fwd(a, st));
   }
@@ -464,10 +477,12 @@ struct StackCall {
   bool pageable = false;
 };
 
+// policy == false: no adapters and no saved activations are used (the
+// adapter-off forward alone); lora and saved are then not checked.
 static ql_status validate_stack(const char* fn, const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
                                 const ql_lora* lora, int64_t M, const void* saved, size_t saved_bytes,
                                 const void* slots, size_t slots_bytes, const void* ws, size_t ws_bytes,
-                                StackCall& sc) {
+                                StackCall& sc, bool policy = true) {
   QL_TRY(check_cfg(fn, cfg));
   if (M < 0) return set_error(QL_ERR_SHAPE, "%s: M (%lld) must be >= 0", fn, (long long)M);
   sc.SL = stack_layout(cfg);
@@ -494,16 +509,19 @@ static ql_status validate_stack(const char* fn, const ql_stack_cfg* cfg, const v
                        slots_bytes, cfg->n_buffers, sc.slots_need);
   }
   if (M > 0) {
-    if (!saved) return set_error(QL_ERR_ARG, "%s: saved is NULL", fn);
-    if (!aligned(saved, 256)) return set_error(QL_ERR_ALIGN, "%s: saved must be 256-byte aligned", fn);
-    if (saved_bytes < sc.saved_need)
-      return set_error(QL_ERR_WORKSPACE, "%s: saved_bytes (%zu) < required (%zu)", fn, saved_bytes,
-                       sc.saved_need);
+    if (policy) {
+      if (!saved) return set_error(QL_ERR_ARG, "%s: saved is NULL", fn);
+      if (!aligned(saved, 256)) return set_error(QL_ERR_ALIGN, "%s: saved must be 256-byte aligned", fn);
+      if (saved_bytes < sc.saved_need)
+        return set_error(QL_ERR_WORKSPACE, "%s: saved_bytes (%zu) < required (%zu)", fn, saved_bytes,
+                         sc.saved_need);
+    }
     if (!ws) return set_error(QL_ERR_ARG, "%s: ws is NULL", fn);
     if (!aligned(ws, 256)) return set_error(QL_ERR_ALIGN, "%s: ws must be 256-byte aligned", fn);
     if (ws_bytes < sc.WS.total)
       return set_error(QL_ERR_WORKSPACE, "%s: ws_bytes (%zu) < required (%zu)", fn, ws_bytes, sc.WS.total);
   }
+  if (!policy) return QL_OK;
   if (!lora) return set_error(QL_ERR_ARG, "%s: lora is NULL", fn);
   for (int l = 0; l < cfg->n_layers; ++l)
     for (int p = 0; p < QL_NPROJ; ++p) {
@@ -780,32 +798,31 @@ ql_status stream_layer_stack_saved_layout(const ql_stack_cfg* cfg, int64_t M, in
   return QL_OK;
 }
 
-ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
-                                 const ql_lora* lora, const void* x0, int64_t M, void* y, void* saved,
-                                 size_t saved_bytes, int32_t reuse_bwd_slots, void* slots, size_t slots_bytes,
-                                 void* ws, size_t ws_bytes, ql_stream compute, ql_stream copy) {
-  clear_error();
-  const char* fn = "stream_layer_stack_fwd";
-  StackCall sc;
-  QL_TRY(validate_stack(fn, cfg, store, store_bytes, lora, M, saved, saved_bytes, slots, slots_bytes, ws,
-                        ws_bytes, sc));
-  if (reuse_bwd_slots != 0 && reuse_bwd_slots != 1)
-    return set_error(QL_ERR_ARG, "%s: reuse_bwd_slots must be 0 or 1", fn);
-  if (M > 0) {
-    QL_TRY(check_ptr(fn, "x0", x0, 16));
-    QL_TRY(check_ptr(fn, "y", y, 16));
-  }
-  if (M == 0) return sc.pageable ? QL_WARN_PAGEABLE_HOST : QL_OK;
-  hipStream_t C = (hipStream_t)compute, P = (hipStream_t)copy;
+}  // extern "C"
+
+// Forward pass over the layers shared by the public entry points. Policy
+// (lora != nullptr): the adapted stack, activations saved for the backward,
+// output y. Reference (ref_y != nullptr): the adapter-off stack on the same
+// x0, activations of one layer at a time in ref_sv (the saved layout of one
+// layer; its h_in entry carries the running hidden state), output ref_y. With
+// both, each layer's slot serves the two passes before it is refilled, so the
+// reference adds no copies.
+static ql_status stack_fwd(const ql_stack_cfg* cfg, const StackCall& sc, const void* store, const ql_lora* lora,
+                           const void* x0, int64_t M, void* y, void* saved, void* ref_y, void* ref_sv,
+                           int32_t reuse_bwd_slots, void* slots, void* ws, hipStream_t C, hipStream_t P) {
   const int L = cfg->n_layers;
   const int64_t H = cfg->hidden;
   uint8_t* sv = (uint8_t*)saved;
+  uint8_t* rv = (uint8_t*)ref_sv;
   uint8_t* w8 = (uint8_t*)ws;
   const uint8_t* st8 = (const uint8_t*)store;
   uint8_t* sl8 = (uint8_t*)slots;
   const size_t rec = (size_t)sc.SL.rec;
   // layer 0 input into the saved area (the backward reads it)
-  QL_HIP_CHECK(hipMemcpyAsync(sv + sc.SV.off[QL_SAVED_H_IN], x0, (size_t)M * H * 2, hipMemcpyDeviceToDevice, C));
+  if (lora)
+    QL_HIP_CHECK(hipMemcpyAsync(sv + sc.SV.off[QL_SAVED_H_IN], x0, (size_t)M * H * 2, hipMemcpyDeviceToDevice, C));
+  if (ref_y)
+    QL_HIP_CHECK(hipMemcpyAsync(rv + sc.SV.off[QL_SAVED_H_IN], x0, (size_t)M * H * 2, hipMemcpyDeviceToDevice, C));
   Events ev;
   // layer l uses slot l % nb; with reuse_bwd_slots the preceding backward
   // left layers nb - 1 .. 0 in their slots
@@ -831,11 +848,18 @@ ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, siz
       if (have_ready[slot]) QL_HIP_CHECK(hipStreamWaitEvent(C, ev.ready[slot], 0));
       base = sl8 + slot * rec;
     }
-    uint8_t* svl = sv + (size_t)l * sc.SV.per_layer;
-    uint16_t* h_out = (l + 1 < L) ? (uint16_t*)(sv + (size_t)(l + 1) * sc.SV.per_layer + sc.SV.off[QL_SAVED_H_IN])
-                                  : (uint16_t*)y;
-    QL_TRY(layer_fwd(cfg, sc.SL, layer_weights(sc.SL, base), lora + l * QL_NPROJ, M, sc.SV, svl, h_out, w8,
-                     sc.WS, C));
+    const LayerW W = layer_weights(sc.SL, base);
+    if (lora) {
+      uint8_t* svl = sv + (size_t)l * sc.SV.per_layer;
+      uint16_t* h_out = (l + 1 < L) ? (uint16_t*)(sv + (size_t)(l + 1) * sc.SV.per_layer + sc.SV.off[QL_SAVED_H_IN])
+                                    : (uint16_t*)y;
+      QL_TRY(layer_fwd(cfg, sc.SL, W, lora + l * QL_NPROJ, M, sc.SV, svl, h_out, w8, sc.WS, C));
+    }
+    if (ref_y) {
+      // the layer's last kernel reads h_in no more, so its output may replace it
+      uint16_t* h_out = (l + 1 < L) ? (uint16_t*)(rv + sc.SV.off[QL_SAVED_H_IN]) : (uint16_t*)ref_y;
+      QL_TRY(layer_fwd(cfg, sc.SL, W, nullptr, M, sc.SV, rv, h_out, w8, sc.WS, C));
+    }
     if (!cfg->resident && l + nb < L) {
       QL_HIP_CHECK(hipEventRecord(ev.free_[slot], C));
       QL_HIP_CHECK(hipStreamWaitEvent(P, ev.free_[slot], 0));
@@ -845,6 +869,55 @@ ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, siz
     }
   }
   return sc.pageable ? QL_WARN_PAGEABLE_HOST : QL_OK;
+}
+
+extern "C" {
+
+ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
+                                 const ql_lora* lora, const void* x0, int64_t M, void* y, void* saved,
+                                 size_t saved_bytes, int32_t reuse_bwd_slots, void* slots, size_t slots_bytes,
+                                 void* ws, size_t ws_bytes, ql_stream compute, ql_stream copy) {
+  clear_error();
+  const char* fn = "stream_layer_stack_fwd";
+  StackCall sc;
+  QL_TRY(validate_stack(fn, cfg, store, store_bytes, lora, M, saved, saved_bytes, slots, slots_bytes, ws,
+                        ws_bytes, sc));
+  if (reuse_bwd_slots != 0 && reuse_bwd_slots != 1)
+    return set_error(QL_ERR_ARG, "%s: reuse_bwd_slots must be 0 or 1", fn);
+  if (M > 0) {
+    QL_TRY(check_ptr(fn, "x0", x0, 16));
+    QL_TRY(check_ptr(fn, "y", y, 16));
+  }
+  if (M == 0) return sc.pageable ? QL_WARN_PAGEABLE_HOST : QL_OK;
+  return stack_fwd(cfg, sc, store, lora, x0, M, y, saved, nullptr, nullptr, reuse_bwd_slots, slots, ws,
+                   (hipStream_t)compute, (hipStream_t)copy);
+}
+
+ql_status stream_layer_stack_fwd_ref(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
+                                     const ql_lora* lora, const void* x0, int64_t M, void* y, void* saved,
+                                     size_t saved_bytes, void* ref_y, void* ref_scratch, size_t ref_scratch_bytes,
+                                     int32_t reuse_bwd_slots, void* slots, size_t slots_bytes, void* ws,
+                                     size_t ws_bytes, ql_stream compute, ql_stream copy) {
+  clear_error();
+  const char* fn = "stream_layer_stack_fwd_ref";
+  StackCall sc;
+  QL_TRY(validate_stack(fn, cfg, store, store_bytes, lora, M, saved, saved_bytes, slots, slots_bytes, ws,
+                        ws_bytes, sc, lora != nullptr));
+  if (reuse_bwd_slots != 0 && reuse_bwd_slots != 1)
+    return set_error(QL_ERR_ARG, "%s: reuse_bwd_slots must be 0 or 1", fn);
+  if (M > 0) {
+    QL_TRY(check_ptr(fn, "x0", x0, 16));
+    if (lora) QL_TRY(check_ptr(fn, "y", y, 16));
+    QL_TRY(check_ptr(fn, "ref_y", ref_y, 16));
+    if (!ref_scratch) return set_error(QL_ERR_ARG, "%s: ref_scratch is NULL", fn);
+    if (!aligned(ref_scratch, 256)) return set_error(QL_ERR_ALIGN, "%s: ref_scratch must be 256-byte aligned", fn);
+    if (ref_scratch_bytes < sc.SV.per_layer)
+      return set_error(QL_ERR_WORKSPACE, "%s: ref_scratch_bytes (%zu) < one layer of saved activations (%zu)",
+                       fn, ref_scratch_bytes, (size_t)sc.SV.per_layer);
+  }
+  if (M == 0) return sc.pageable ? QL_WARN_PAGEABLE_HOST : QL_OK;
+  return stack_fwd(cfg, sc, store, lora, x0, M, y, lora ? saved : nullptr, ref_y, ref_scratch, reuse_bwd_slots,
+                   slots, ws, (hipStream_t)compute, (hipStream_t)copy);
 }
 
 ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,

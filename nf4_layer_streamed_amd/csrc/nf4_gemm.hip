@@ -500,13 +500,15 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
   {  // last weight step (stage 1); the LoRA step's A tile (U) goes to stage 2,
      // last read two steps ago (before the barrier of the previous step)
     mma_step(step, S1{}, F_{}, F_{});
-    uint4 ar[8];
-    load_a_rank(ar, S.U, a.r, M, m0, t);
-    store_a<true>(A_of(2), ar, t);
-    __syncthreads();
+    if (a.r > 0) {
+      uint4 ar[8];
+      load_a_rank(ar, S.U, a.r, M, m0, t);
+      store_a<true>(A_of(2), ar, t);
+      __syncthreads();
+    }
   }
-  // LoRA step: [U | 0] [s B | 0]^T
-  {
+  // LoRA step: [U | 0] [s B | 0]^T (none with r = 0: the adapter is off)
+  if (a.r > 0) {
     uint4 lb[NTW][4];
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {

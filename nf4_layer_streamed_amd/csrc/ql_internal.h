@@ -82,7 +82,7 @@ constexpr int kMaxSegs = 3;
 struct FwdArgs {
   const uint16_t* X;  // bf16 [M x ldx], logical columns 0..K-1 (optionally remapped)
   int64_t M, K, ldx;
-  int32_t r;
+  int32_t r;  // 0: adapter off (no LoRA step; U and B unused)
   float s;
   int32_t head_dim, n_rep;  // repeat_kv remap of X's columns (n_rep 0 = none)
   int32_t out_f32;
