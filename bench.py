@@ -32,6 +32,8 @@ the whole step (M tokens per step). The JSON line also carries:
 * with_reference - a preference-training step: the policy forward and the
   adapter-off reference forward in one pass over the streamed layers, then
   the backward (no extra copies for the reference).
+* recompute - the same streamed step with per-layer activation recomputation
+  (only layer inputs saved; the backward recomputes each layer from its slot).
 * resident - the same step with the store resident in HBM (no copies).
 * cpu_baseline - the CPU oracle timed on a bounded sample.
 """
@@ -364,6 +366,21 @@ def main():
                     copies_per_step=copies, note="policy + adapter-off reference forward share each layer copy")
     del ref_scratch, ref_y
 
+    # the same streamed step with per-layer recomputation (gradient
+    # checkpointing): the forward keeps only layer inputs, the backward
+    # recomputes each layer from its slot
+    log(f"bench: recompute mode, {args.steps} streamed steps")
+    cfg_rc = ql.StackCfg(**{**cfg.__dict__, "recompute": 1})
+    _, saved_rc_b, ws_rc_b = ql.stream_layer_stack_workspace(cfg_rc, M)
+    saved_main, ws_main = saved, ws
+    saved = torch.empty(saved_rc_b, dtype=torch.uint8, device=dev)
+    ws = torch.empty(ws_rc_b, dtype=torch.uint8, device=dev)
+    trc, _, _ = timed(cfg_rc, store, args.steps, args.warmup, False)
+    saved, ws = saved_main, ws_main
+    recompute = dict(value=round(M * args.steps / trc, 1), unit="tok/s", ms_per_step=round(1000 * trc / args.steps, 3),
+                     saved_bytes=int(saved_rc_b), saved_bytes_without=int(saved.numel()),
+                     ws_bytes=int(ws_rc_b), ws_bytes_without=int(ws.numel()))
+
     dense = dense_gemm_ceiling(torch, dev, M, w)
     gemm_all["vs_dense_bf16"] = round(gemm_all["tflops"] / dense["tflops"], 4)
 
@@ -411,6 +428,7 @@ def main():
         "pcie": pcie,
         "ring8": ring8,
         "with_reference": with_ref,
+        "recompute": recompute,
         "resident": resident,
         "cpu_baseline": cpu,
     }

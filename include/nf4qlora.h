@@ -197,6 +197,7 @@ typedef struct {
   float alpha, rms_eps;
   int32_t n_buffers;  /* device slots, 2..QL_MAX_BUFFERS (2: double buffering) */
   int32_t resident;   /* 0: host store, streamed; 1: device store, no copies */
+  int32_t recompute;  /* 1: per-layer activation recomputation (gradient checkpointing) */
 } ql_stack_cfg;
 
 enum { QL_PROJ_Q = 0, QL_PROJ_K, QL_PROJ_V, QL_PROJ_O, QL_PROJ_GATE, QL_PROJ_UP, QL_PROJ_DOWN,
@@ -220,7 +221,14 @@ enum { QL_SAVED_H_IN = 0, QL_SAVED_N1, QL_SAVED_Q, QL_SAVED_K, QL_SAVED_V, QL_SA
 
 /* Byte offsets (host int64 [QL_SAVED_COUNT]) of each saved tensor within one
  * layer's part of `saved`, and that part's size; layer l starts at
- * l * per_layer_bytes. All saved tensors are bf16, row-major with M rows. */
+ * l * per_layer_bytes. All saved tensors are bf16, row-major with M rows.
+ * recompute = 1 (gradient checkpointing, handled per layer by the streamer as
+ * in the docs' "Layer Streaming" configuration): the forward keeps only each
+ * layer's input h_in (every other offset is -1) and the backward recomputes
+ * the layer's activations from it, with the weights already in the layer's
+ * slot, into a one-layer area of the workspace. No extra copies; the
+ * recomputed values are those the forward produced, so y, dx0, dA and dB are
+ * bitwise those of recompute = 0. */
 ql_status stream_layer_stack_saved_layout(const ql_stack_cfg* cfg, int64_t M, int64_t* offsets,
                                           size_t* per_layer_bytes);
 
@@ -248,9 +256,9 @@ ql_status stream_layer_stack_fwd(const ql_stack_cfg* cfg, const void* store, siz
  * y, saved: exactly those of stream_layer_stack_fwd with the same arguments
  * (bitwise). ref_y (bf16 [M x H]): the stack's output with every LoRA term
  * removed (y = x W^T per projection), on the same x0. ref_scratch: one
- * layer's saved activations (per_layer_bytes of
- * stream_layer_stack_saved_layout), overwritten; its contents afterwards are
- * unspecified. lora == NULL: the reference alone (y and saved are then not
+ * layer's activations (per_layer_bytes of stream_layer_stack_saved_layout
+ * for the same cfg with recompute = 0), overwritten; its contents afterwards
+ * are unspecified. lora == NULL: the reference alone (y and saved are then not
  * used and may be NULL). reuse_bwd_slots and the slot ordering are as in
  * stream_layer_stack_fwd, so a following stream_layer_stack_bwd may reuse the
  * slots this call leaves. */

@@ -55,7 +55,7 @@ class ql_stack_cfg(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("kv_dim", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("r", ctypes.c_int32),
                 ("alpha", ctypes.c_float), ("rms_eps", ctypes.c_float),
-                ("n_buffers", ctypes.c_int32), ("resident", ctypes.c_int32)]
+                ("n_buffers", ctypes.c_int32), ("resident", ctypes.c_int32), ("recompute", ctypes.c_int32)]
 
 
 _lib = None
@@ -196,10 +196,11 @@ class StackCfg:
     rms_eps: float = 1e-5
     n_buffers: int = 2
     resident: int = 0
+    recompute: int = 0
 
     def c(self):
         return ql_stack_cfg(self.n_layers, self.hidden, self.inter, self.kv_dim, self.head_dim, self.r,
-                            self.alpha, self.rms_eps, self.n_buffers, self.resident)
+                            self.alpha, self.rms_eps, self.n_buffers, self.resident, self.recompute)
 
     def proj_shape(self, p):
         H, I, KV = self.hidden, self.inter, self.kv_dim

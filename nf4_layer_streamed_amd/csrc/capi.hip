@@ -120,6 +120,8 @@ static ql_status check_cfg(const char* fn, const ql_stack_cfg* c) {
     return set_error(QL_ERR_UNSUPPORTED, "%s: n_buffers (%d) must be in 2..%d", fn, c->n_buffers, QL_MAX_BUFFERS);
   if (c->resident != 0 && c->resident != 1)
     return set_error(QL_ERR_ARG, "%s: resident (%d) must be 0 or 1", fn, c->resident);
+  if (c->recompute != 0 && c->recompute != 1)
+    return set_error(QL_ERR_ARG, "%s: recompute (%d) must be 0 or 1", fn, c->recompute);
   if (!(c->rms_eps > 0.f) || !(c->alpha == c->alpha))
     return set_error(QL_ERR_ARG, "%s: rms_eps must be > 0 and alpha finite", fn);
   return QL_OK;
@@ -150,7 +152,8 @@ struct SavedLayout {
   size_t per_layer;
 };
 
-static SavedLayout saved_layout(const ql_stack_cfg* c, int64_t M) {
+// Every activation of one layer (what the backward reads).
+static SavedLayout full_layout(const ql_stack_cfg* c, int64_t M) {
   SavedLayout s;
   const int64_t H = c->hidden, I = c->inter, KV = c->kv_dim, r = c->r;
   const int64_t cols[QL_SAVED_COUNT] = {H, H, H, KV, KV, H, H, I, I, I, r, r, r, r, r, r, r};
@@ -163,9 +166,21 @@ static SavedLayout saved_layout(const ql_stack_cfg* c, int64_t M) {
   return s;
 }
 
-// internal temporaries of the stack (offsets into ws)
+// What the forward keeps per layer: every activation, or with recompute only
+// the layer input h_in (the other offsets are -1).
+static SavedLayout saved_layout(const ql_stack_cfg* c, int64_t M) {
+  if (!c->recompute) return full_layout(c, M);
+  SavedLayout s;
+  for (int i = 0; i < QL_SAVED_COUNT; ++i) s.off[i] = -1;
+  s.off[QL_SAVED_H_IN] = 0;
+  s.per_layer = align256((size_t)(M * c->hidden * 2));
+  return s;
+}
+
+// internal temporaries of the stack (offsets into ws); with recompute also one
+// layer of activations (ck, full layout) and the recomputed layer output
 struct StackWs {
-  size_t dhA, dhB, dhmid, dact, dg, du, dn, da32, dv, bt, G[5], scratch, total;
+  size_t dhA, dhB, dhmid, dact, dg, du, dn, da32, dv, bt, G[5], scratch, ck, ck_out, total;
 };
 
 static StackWs stack_ws(const ql_stack_cfg* c, int64_t M) {
@@ -197,6 +212,11 @@ static StackWs stack_ws(const ql_stack_cfg* c, int64_t M) {
   mx(colred_ws_bytes(M, I, r));
   mx(colred_ws_bytes(M, KV, r));
   w.scratch = take(sc);
+  w.ck = w.ck_out = 0;
+  if (c->recompute) {
+    w.ck = take(full_layout(c, M).per_layer);
+    w.ck_out = take((size_t)(M * H * 2));
+  }
   w.total = off;
   return w;
 }
@@ -471,7 +491,7 @@ struct Events {
 
 struct StackCall {
   StackLayout SL;
-  SavedLayout SV;
+  SavedLayout SV, SVF;  // caller's saved layout; every activation of one layer
   StackWs WS;
   size_t store_need, slots_need, saved_need;
   bool pageable = false;
@@ -487,6 +507,7 @@ static ql_status validate_stack(const char* fn, const ql_stack_cfg* cfg, const v
   if (M < 0) return set_error(QL_ERR_SHAPE, "%s: M (%lld) must be >= 0", fn, (long long)M);
   sc.SL = stack_layout(cfg);
   sc.SV = saved_layout(cfg, M);
+  sc.SVF = full_layout(cfg, M);
   sc.WS = stack_ws(cfg, M);
   sc.store_need = (size_t)sc.SL.rec * cfg->n_layers;
   sc.slots_need = cfg->resident ? 0 : (size_t)sc.SL.rec * cfg->n_buffers;
@@ -822,7 +843,7 @@ static ql_status stack_fwd(const ql_stack_cfg* cfg, const StackCall& sc, const v
   if (lora)
     QL_HIP_CHECK(hipMemcpyAsync(sv + sc.SV.off[QL_SAVED_H_IN], x0, (size_t)M * H * 2, hipMemcpyDeviceToDevice, C));
   if (ref_y)
-    QL_HIP_CHECK(hipMemcpyAsync(rv + sc.SV.off[QL_SAVED_H_IN], x0, (size_t)M * H * 2, hipMemcpyDeviceToDevice, C));
+    QL_HIP_CHECK(hipMemcpyAsync(rv + sc.SVF.off[QL_SAVED_H_IN], x0, (size_t)M * H * 2, hipMemcpyDeviceToDevice, C));
   Events ev;
   // layer l uses slot l % nb; with reuse_bwd_slots the preceding backward
   // left layers nb - 1 .. 0 in their slots
@@ -853,12 +874,20 @@ static ql_status stack_fwd(const ql_stack_cfg* cfg, const StackCall& sc, const v
       uint8_t* svl = sv + (size_t)l * sc.SV.per_layer;
       uint16_t* h_out = (l + 1 < L) ? (uint16_t*)(sv + (size_t)(l + 1) * sc.SV.per_layer + sc.SV.off[QL_SAVED_H_IN])
                                     : (uint16_t*)y;
-      QL_TRY(layer_fwd(cfg, sc.SL, W, lora + l * QL_NPROJ, M, sc.SV, svl, h_out, w8, sc.WS, C));
+      if (cfg->recompute) {
+        // the layer runs on the one-layer area ck; only its input is kept
+        uint8_t* ck = w8 + sc.WS.ck;
+        QL_HIP_CHECK(hipMemcpyAsync(ck + sc.SVF.off[QL_SAVED_H_IN], svl + sc.SV.off[QL_SAVED_H_IN],
+                                    (size_t)M * H * 2, hipMemcpyDeviceToDevice, C));
+        QL_TRY(layer_fwd(cfg, sc.SL, W, lora + l * QL_NPROJ, M, sc.SVF, ck, h_out, w8, sc.WS, C));
+      } else {
+        QL_TRY(layer_fwd(cfg, sc.SL, W, lora + l * QL_NPROJ, M, sc.SVF, svl, h_out, w8, sc.WS, C));
+      }
     }
     if (ref_y) {
       // the layer's last kernel reads h_in no more, so its output may replace it
-      uint16_t* h_out = (l + 1 < L) ? (uint16_t*)(rv + sc.SV.off[QL_SAVED_H_IN]) : (uint16_t*)ref_y;
-      QL_TRY(layer_fwd(cfg, sc.SL, W, nullptr, M, sc.SV, rv, h_out, w8, sc.WS, C));
+      uint16_t* h_out = (l + 1 < L) ? (uint16_t*)(rv + sc.SVF.off[QL_SAVED_H_IN]) : (uint16_t*)ref_y;
+      QL_TRY(layer_fwd(cfg, sc.SL, W, nullptr, M, sc.SVF, rv, h_out, w8, sc.WS, C));
     }
     if (!cfg->resident && l + nb < L) {
       QL_HIP_CHECK(hipEventRecord(ev.free_[slot], C));
@@ -911,9 +940,9 @@ ql_status stream_layer_stack_fwd_ref(const ql_stack_cfg* cfg, const void* store,
     QL_TRY(check_ptr(fn, "ref_y", ref_y, 16));
     if (!ref_scratch) return set_error(QL_ERR_ARG, "%s: ref_scratch is NULL", fn);
     if (!aligned(ref_scratch, 256)) return set_error(QL_ERR_ALIGN, "%s: ref_scratch must be 256-byte aligned", fn);
-    if (ref_scratch_bytes < sc.SV.per_layer)
-      return set_error(QL_ERR_WORKSPACE, "%s: ref_scratch_bytes (%zu) < one layer of saved activations (%zu)",
-                       fn, ref_scratch_bytes, (size_t)sc.SV.per_layer);
+    if (ref_scratch_bytes < sc.SVF.per_layer)
+      return set_error(QL_ERR_WORKSPACE, "%s: ref_scratch_bytes (%zu) < one layer of activations (%zu)",
+                       fn, ref_scratch_bytes, (size_t)sc.SVF.per_layer);
   }
   if (M == 0) return sc.pageable ? QL_WARN_PAGEABLE_HOST : QL_OK;
   return stack_fwd(cfg, sc, store, lora, x0, M, y, lora ? saved : nullptr, ref_y, ref_scratch, reuse_bwd_slots,
@@ -988,9 +1017,21 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
       base = sl8 + slot * rec;
     }
     uint16_t* out = (l == 0 && dx0) ? (uint16_t*)dx0 : (((L - 1 - l) & 1) ? dhB : dhA);
-    QL_TRY(layer_bwd(cfg, sc.SL, layer_weights(sc.SL, base), lora + l * QL_NPROJ, M, sc.SV,
-                     sv + (size_t)l * sc.SV.per_layer, dh, out, dA + l * QL_NPROJ, dB + l * QL_NPROJ,
-                     accumulate, w8, sc.WS, C));
+    const LayerW W = layer_weights(sc.SL, base);
+    const uint8_t* svl = sv + (size_t)l * sc.SV.per_layer;
+    if (cfg->recompute) {
+      // recompute the layer's activations from its saved input, with the
+      // weights already in the slot (same kernels, same bytes: the same values
+      // the forward produced)
+      uint8_t* ck = w8 + sc.WS.ck;
+      QL_HIP_CHECK(hipMemcpyAsync(ck + sc.SVF.off[QL_SAVED_H_IN], svl + sc.SV.off[QL_SAVED_H_IN],
+                                  (size_t)M * cfg->hidden * 2, hipMemcpyDeviceToDevice, C));
+      QL_TRY(layer_fwd(cfg, sc.SL, W, lora + l * QL_NPROJ, M, sc.SVF, ck, (uint16_t*)(w8 + sc.WS.ck_out), w8,
+                       sc.WS, C));
+      svl = ck;
+    }
+    QL_TRY(layer_bwd(cfg, sc.SL, W, lora + l * QL_NPROJ, M, sc.SVF, svl, dh, out, dA + l * QL_NPROJ,
+                     dB + l * QL_NPROJ, accumulate, w8, sc.WS, C));
     dh = out;
     if (streamed && l - nb >= 0) {
       QL_HIP_CHECK(hipEventRecord(ev.free_[slot], C));

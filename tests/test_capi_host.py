@@ -119,6 +119,15 @@ def test_stack_layout_sizes(name, L, H, I, KV, d, r):
         assert ql.stream_layer_stack_workspace(c, 512)[0] == nb * rec
     offs_s, per = ql.stream_layer_stack_saved_layout(cfg, 512)
     assert saved == per * L
+    # recompute: only each layer's input is saved; the workspace gains one
+    # layer of activations and one layer output
+    rc = ql.StackCfg(**{**cfg.__dict__, "recompute": 1})
+    offs_r, per_r = ql.stream_layer_stack_saved_layout(rc, 512)
+    assert per_r == 512 * cfg.hidden * 2 and offs_r["h_in"] == 0
+    assert all(v == -1 for k, v in offs_r.items() if k != "h_in")
+    _, saved_r, ws_r = ql.stream_layer_stack_workspace(rc, 512)
+    assert saved_r == per_r * L
+    assert ws_r == ws + per + 512 * cfg.hidden * 2
 
 
 def test_stack_cfg_validation():
@@ -126,9 +135,10 @@ def test_stack_cfg_validation():
     bad = [ql.StackCfg(0, 576, 1536, 192, 64, 8, 16.0), ql.StackCfg(2, 577, 1536, 192, 64, 8, 16.0),
            ql.StackCfg(2, 576, 1536, 200, 64, 8, 16.0), ql.StackCfg(2, 576, 1536, 192, 64, 0, 16.0),
            ql.StackCfg(2, 576, 1536, 192, 64, 8, 16.0, n_buffers=1),
-           ql.StackCfg(2, 576, 1536, 192, 64, 8, 16.0, n_buffers=9)]
+           ql.StackCfg(2, 576, 1536, 192, 64, 8, 16.0, n_buffers=9),
+           ql.StackCfg(2, 576, 1536, 192, 64, 8, 16.0, recompute=2)]
     want = [ql.QL_ERR_SHAPE, ql.QL_ERR_SHAPE, ql.QL_ERR_SHAPE, ql.QL_ERR_RANK, ql.QL_ERR_UNSUPPORTED,
-            ql.QL_ERR_UNSUPPORTED]
+            ql.QL_ERR_UNSUPPORTED, ql.QL_ERR_ARG]
     for cfg, st in zip(bad, want):
         with pytest.raises(ql.QlError) as e:
             ql.stream_layer_stack_layout(cfg)
