@@ -87,8 +87,9 @@ ql_status nf4_codebook(float* out /* host [16] */);
  * gets code 7 (the zero level) and absmax 0. Codes are packed 8 to a 32-bit
  * little-endian word (elements 8w..8w+7 in bytes 4w..4w+3): byte j of word w
  * holds element 8w+j in its low nibble and element 8w+j+4 in its high nibble.
- * Quantisation is offline, done once per tensor (docs "NF4 streaming": "the
- * base is quantised once, offline, one tensor at a time").
+ * Quantisation is offline, done once per tensor (docs "Layer Streaming",
+ * "NF4 streaming": the base is quantised a tensor at a time, once, before
+ * training).
  *   packed: uint8 [n/2], absmax: float32 [n/64]; all 16-byte aligned.
  * Non-finite input is refused with QL_ERR_NONFINITE. To detect it the call
  * waits for the stream to finish the kernel (it is synchronous). On
@@ -104,6 +105,33 @@ ql_status nf4_quantize(const float* w, int64_t n, uint8_t* packed, float* absmax
  */
 ql_status nf4_dequant(const uint8_t* packed, const float* absmax, int64_t n,
                       int32_t out_dtype, void* out, ql_stream s);
+
+/* ------------------------------------------- double-quantised block scales
+ * The pages' NF4 stores (3.60 GB for Llama-3.1-8B with 113 MB layer buffers:
+ * Soup README, header figure caption; 1.43 GB for Qwen2.5-3B: CHANGELOG
+ * [0.72.2]) are about 0.516 bytes per weight, which is NF4 codes plus 8-bit
+ * block scales: the second-level quantisation of QLoRA section 3 ("Double
+ * Quantization"). Reading taken here:
+ *   mu = fl32(S / n), S the float64 sum of the n float32 absmax values taken
+ *     in a fixed order (runs of 256 left to right, then the run sums left to
+ *     right);
+ *   per run of 256: d = fl32(c - mu), s = fl32(max |d| / 448),
+ *     code = OCP FP8 E4M3 of fl32(d / s), round-to-nearest-even, saturated to
+ *     +-448 (s = 0: code 0);
+ *   expansion: c' = fl32(fl32(e4m3(code) * s) + mu).
+ * The NF4 codes are those of the float32 absmax; only the scale storage
+ * changes (c' replaces absmax in every use).
+ *
+ * nf4_dq_layout: the block for nblocks scales: codes (nblocks bytes) at 0, the
+ * run scales (float32, ceil(nblocks / 256)) at *scale_off, mu (float32) at
+ * *mean_off, *bytes in all (multiples of 256).
+ * nf4_double_quant: absmax (float32 [nblocks], finite, as nf4_quantize makes
+ * it) -> the block at dq (256-byte aligned, dq_bytes >= the block size).
+ * nf4_dq_expand: the block -> c' (float32 [nblocks]).
+ */
+ql_status nf4_dq_layout(int64_t nblocks, size_t* scale_off, size_t* mean_off, size_t* bytes);
+ql_status nf4_double_quant(const float* absmax, int64_t nblocks, void* dq, size_t dq_bytes, ql_stream s);
+ql_status nf4_dq_expand(const void* dq, int64_t nblocks, float* absmax, ql_stream s);
 
 /* ------------------------------------------------------- NF4 + LoRA linear */
 typedef struct {
@@ -165,10 +193,10 @@ ql_status qlora_linear_bwd(const void* dy, const void* x, const void* u_saved, i
  * The frozen NF4 weights live in one "store" of n_layers records (layout from
  * stream_layer_stack_layout). Streamed mode (resident == 0): the store is HOST
  * memory, ideally page-locked; each layer's record is copied with one
- * asynchronous host-to-device copy on the `copy` stream into one of two device
- * slots, while the `compute` stream works on the other slot; events order the
- * two (docs "Layer Streaming": "two pre-allocated VRAM buffers", "stream_buffers:
- * 2  # double-buffering"). Peak device memory for weights is the two slots.
+ * asynchronous host-to-device copy on the `copy` stream into one of n_buffers
+ * device slots, while the `compute` stream works on another; events order the
+ * two (docs "Layer Streaming": pre-allocated device buffers, two by default).
+ * Peak device memory for weights is the n_buffers slots.
  * Resident mode (resident == 1): the store is a DEVICE buffer, nothing is
  * copied and the same kernels run in the same order on the same bytes, so the
  * results are bit-identical to streamed mode (blog "Why the evidence is better
@@ -198,6 +226,9 @@ typedef struct {
   int32_t n_buffers;  /* device slots, 2..QL_MAX_BUFFERS (2: double buffering) */
   int32_t resident;   /* 0: host store, streamed; 1: device store, no copies */
   int32_t recompute;  /* 1: per-layer activation recomputation (gradient checkpointing) */
+  int32_t absmax_dq;  /* 1: each projection's absmax in the record is its nf4_double_quant
+                       * block; the layer's scales are expanded on the device before
+                       * its GEMMs (8% fewer bytes per copy) */
 } ql_stack_cfg;
 
 enum { QL_PROJ_Q = 0, QL_PROJ_K, QL_PROJ_V, QL_PROJ_O, QL_PROJ_GATE, QL_PROJ_UP, QL_PROJ_DOWN,

@@ -26,6 +26,7 @@ SAVED = ("h_in", "n1", "q", "k", "v", "h_mid", "n2", "gate", "up", "act") + tupl
 
 EXPORTS = (
     "ql_last_error", "ql_abi_version", "nf4_codebook", "nf4_quantize", "nf4_dequant",
+    "nf4_dq_layout", "nf4_double_quant", "nf4_dq_expand",
     "qlora_linear_workspace", "qlora_linear_fwd", "qlora_linear_bwd",
     "stream_layer_stack_layout", "stream_layer_stack_workspace", "stream_layer_stack_saved_layout",
     "stream_layer_stack_fwd", "stream_layer_stack_fwd_ref", "stream_layer_stack_bwd", "ql_profile_enable",
@@ -55,7 +56,8 @@ class ql_stack_cfg(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("kv_dim", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("r", ctypes.c_int32),
                 ("alpha", ctypes.c_float), ("rms_eps", ctypes.c_float),
-                ("n_buffers", ctypes.c_int32), ("resident", ctypes.c_int32), ("recompute", ctypes.c_int32)]
+                ("n_buffers", ctypes.c_int32), ("resident", ctypes.c_int32), ("recompute", ctypes.c_int32),
+                ("absmax_dq", ctypes.c_int32)]
 
 
 _lib = None
@@ -76,6 +78,9 @@ def load(path=LIB_PATH):
         "nf4_codebook": (I32, [P]),
         "nf4_quantize": (I32, [P, I64, P, P, P]),
         "nf4_dequant": (I32, [P, P, I64, I32, P, P]),
+        "nf4_dq_layout": (I32, [I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+        "nf4_double_quant": (I32, [P, I64, P, SZ, P]),
+        "nf4_dq_expand": (I32, [P, I64, P, P]),
         "qlora_linear_workspace": (I32, [I64, I64, I64, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
         "qlora_linear_fwd": (I32, [P, I64, ql_nf4_weight, ql_lora, P, P, P, SZ, P]),
         "qlora_linear_bwd": (I32, [P, P, P, I64, ql_nf4_weight, ql_lora, P, P, P, I32, P, SZ, P]),
@@ -145,6 +150,23 @@ def nf4_dequant(packed, absmax, n, out, stream=None):
     return _check(load().nf4_dequant(_ptr(packed), _ptr(absmax), n, dt, _ptr(out), _stream(stream)))
 
 
+def nf4_dq_layout(nblocks):
+    """-> (scale offset, mean offset, bytes) of the double-quantised block of nblocks scales."""
+    so, mo, nb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().nf4_dq_layout(nblocks, ctypes.byref(so), ctypes.byref(mo), ctypes.byref(nb)))
+    return so.value, mo.value, nb.value
+
+
+def nf4_double_quant(absmax, dq, stream=None):
+    """absmax (float32 device tensor of n scales) -> the block in dq (uint8 device tensor)."""
+    return _check(load().nf4_double_quant(_ptr(absmax), absmax.numel(), _ptr(dq), _nbytes(dq), _stream(stream)))
+
+
+def nf4_dq_expand(dq, nblocks, out, stream=None):
+    """The block in dq -> float32 scales in out (nblocks elements)."""
+    return _check(load().nf4_dq_expand(_ptr(dq), nblocks, _ptr(out), _stream(stream)))
+
+
 @dataclass
 class NF4Weight:
     packed: torch.Tensor
@@ -197,10 +219,12 @@ class StackCfg:
     n_buffers: int = 2
     resident: int = 0
     recompute: int = 0
+    absmax_dq: int = 0
 
     def c(self):
         return ql_stack_cfg(self.n_layers, self.hidden, self.inter, self.kv_dim, self.head_dim, self.r,
-                            self.alpha, self.rms_eps, self.n_buffers, self.resident, self.recompute)
+                            self.alpha, self.rms_eps, self.n_buffers, self.resident, self.recompute,
+                            self.absmax_dq)
 
     def proj_shape(self, p):
         H, I, KV = self.hidden, self.inter, self.kv_dim
@@ -303,7 +327,15 @@ def build_store(cfg, layers, pinned=True, device=None):
             packed, absmax = d[p]
             po, ao = proj[p]
             store[base + po: base + po + packed.numel()].copy_(packed.reshape(-1).view(torch.uint8))
-            ab = absmax.reshape(-1).view(torch.uint8)
+            if cfg.absmax_dq:
+                # the scale block is made on the GPU (nf4_double_quant)
+                dev = device if device is not None else "cuda"
+                a = absmax.reshape(-1).to(dev, torch.float32)
+                ab = torch.empty(nf4_dq_layout(a.numel())[2], dtype=torch.uint8, device=dev)
+                nf4_double_quant(a, ab)
+                torch.cuda.synchronize()
+            else:
+                ab = absmax.reshape(-1).view(torch.uint8)
             store[base + ao: base + ao + ab.numel()].copy_(ab)
     return store
 

@@ -24,7 +24,6 @@ ql_status set_error(ql_status st, const char* fmt, ...) {
 static void clear_error() { g_err[0] = 0; }
 
 static inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
-static inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 #define QL_TRY(expr)                 \
   do {                               \
@@ -122,6 +121,8 @@ static ql_status check_cfg(const char* fn, const ql_stack_cfg* c) {
     return set_error(QL_ERR_ARG, "%s: resident (%d) must be 0 or 1", fn, c->resident);
   if (c->recompute != 0 && c->recompute != 1)
     return set_error(QL_ERR_ARG, "%s: recompute (%d) must be 0 or 1", fn, c->recompute);
+  if (c->absmax_dq != 0 && c->absmax_dq != 1)
+    return set_error(QL_ERR_ARG, "%s: absmax_dq (%d) must be 0 or 1", fn, c->absmax_dq);
   if (!(c->rms_eps > 0.f) || !(c->alpha == c->alpha))
     return set_error(QL_ERR_ARG, "%s: rms_eps must be > 0 and alpha finite", fn);
   return QL_OK;
@@ -139,9 +140,11 @@ static StackLayout stack_layout(const ql_stack_cfg* c) {
     s.packed_off[p] = (int64_t)off;
     off += align256((size_t)(n[p] * k[p] / 2));
   }
+  // float32 absmax per 64 weights, or its double-quantised block
   for (int p = 0; p < QL_NPROJ; ++p) {
     s.absmax_off[p] = (int64_t)off;
-    off += align256((size_t)(n[p] * (k[p] / 64) * 4));
+    const int64_t nb = n[p] * (k[p] / 64);
+    off += c->absmax_dq ? dq_layout(nb).bytes : align256((size_t)(nb * 4));
   }
   s.rec = (int64_t)align256(off);
   return s;
@@ -180,7 +183,9 @@ static SavedLayout saved_layout(const ql_stack_cfg* c, int64_t M) {
 // internal temporaries of the stack (offsets into ws); with recompute also one
 // layer of activations (ck, full layout) and the recomputed layer output
 struct StackWs {
-  size_t dhA, dhB, dhmid, dact, dg, du, dn, da32, dv, bt, G[5], scratch, ck, ck_out, total;
+  size_t dhA, dhB, dhmid, dact, dg, du, dn, da32, dv, bt, G[5], scratch, ck, ck_out;
+  size_t absx[QL_NPROJ];  // absmax_dq: the layer's expanded float32 scales
+  size_t total;
 };
 
 static StackWs stack_ws(const ql_stack_cfg* c, int64_t M) {
@@ -212,6 +217,12 @@ static StackWs stack_ws(const ql_stack_cfg* c, int64_t M) {
   mx(colred_ws_bytes(M, I, r));
   mx(colred_ws_bytes(M, KV, r));
   w.scratch = take(sc);
+  for (int p = 0; p < QL_NPROJ; ++p) w.absx[p] = 0;
+  if (c->absmax_dq) {
+    const int64_t n[QL_NPROJ] = {H, KV, KV, H, I, I, H};
+    const int64_t k[QL_NPROJ] = {H, H, H, H, H, H, I};
+    for (int p = 0; p < QL_NPROJ; ++p) w.absx[p] = take((size_t)(n[p] * (k[p] / 64) * 4));
+  }
   w.ck = w.ck_out = 0;
   if (c->recompute) {
     w.ck = take(full_layout(c, M).per_layer);
@@ -234,6 +245,31 @@ static LayerW layer_weights(const StackLayout& L, const uint8_t* base) {
     w.absmax[p] = (const float*)(base + L.absmax_off[p]);
   }
   return w;
+}
+
+// The layer's weights in a slot (or the resident store). With double-quantised
+// scales, the seven blocks are first expanded into the workspace's float32
+// area (one launch, on the compute stream, after the layer's copy has landed)
+// and the GEMMs read the scales from there.
+static ql_status layer_weights_ready(const ql_stack_cfg* c, const StackLayout& L, const StackWs& WS,
+                                     const uint8_t* base, uint8_t* ws, hipStream_t st, LayerW& W) {
+  W = layer_weights(L, base);
+  if (!c->absmax_dq) return QL_OK;
+  DqExpandArgs a{};
+  a.nblk = QL_NPROJ;
+  int64_t cum = 0;
+  for (int p = 0; p < QL_NPROJ; ++p) {
+    const int64_t nb = L.N[p] * (L.K[p] / 64);
+    const DqLayout dl = dq_layout(nb);
+    a.src[p] = base + L.absmax_off[p];
+    a.scale_off[p] = dl.scale_off;
+    a.mean_off[p] = dl.mean_off;
+    a.dst[p] = (float*)(ws + WS.absx[p]);
+    cum += nb;
+    a.end[p] = cum;
+    W.absmax[p] = a.dst[p];
+  }
+  return launch_dq_expand(a, st);
 }
 
 static inline const uint16_t* u16(const void* p) { return (const uint16_t*)p; }
@@ -679,6 +715,47 @@ ql_status nf4_quantize(const float* w, int64_t n, uint8_t* packed, float* absmax
   return QL_OK;
 }
 
+ql_status nf4_dq_layout(int64_t nblocks, size_t* scale_off, size_t* mean_off, size_t* bytes) {
+  clear_error();
+  if (nblocks < 0) return set_error(QL_ERR_SHAPE, "nf4_dq_layout: nblocks (%lld) must be >= 0", (long long)nblocks);
+  const DqLayout l = dq_layout(nblocks);
+  if (scale_off) *scale_off = l.scale_off;
+  if (mean_off) *mean_off = l.mean_off;
+  if (bytes) *bytes = l.bytes;
+  return QL_OK;
+}
+
+ql_status nf4_double_quant(const float* absmax, int64_t nblocks, void* dq, size_t dq_bytes, ql_stream s) {
+  clear_error();
+  const char* fn = "nf4_double_quant";
+  if (nblocks < 0) return set_error(QL_ERR_SHAPE, "%s: nblocks (%lld) must be >= 0", fn, (long long)nblocks);
+  if (nblocks == 0) return QL_OK;
+  QL_TRY(check_ptr(fn, "absmax", absmax, 4));
+  QL_TRY(check_ptr(fn, "dq", dq, 256));
+  const DqLayout l = dq_layout(nblocks);
+  if (dq_bytes < l.bytes)
+    return set_error(QL_ERR_WORKSPACE, "%s: dq_bytes (%zu) < block size (%zu)", fn, dq_bytes, l.bytes);
+  return launch_dq_quant(absmax, nblocks, (uint8_t*)dq, (hipStream_t)s);
+}
+
+ql_status nf4_dq_expand(const void* dq, int64_t nblocks, float* absmax, ql_stream s) {
+  clear_error();
+  const char* fn = "nf4_dq_expand";
+  if (nblocks < 0) return set_error(QL_ERR_SHAPE, "%s: nblocks (%lld) must be >= 0", fn, (long long)nblocks);
+  if (nblocks == 0) return QL_OK;
+  QL_TRY(check_ptr(fn, "dq", dq, 256));
+  QL_TRY(check_ptr(fn, "absmax", absmax, 4));
+  const DqLayout l = dq_layout(nblocks);
+  DqExpandArgs a{};
+  a.nblk = 1;
+  a.src[0] = (const uint8_t*)dq;
+  a.scale_off[0] = l.scale_off;
+  a.mean_off[0] = l.mean_off;
+  a.dst[0] = absmax;
+  a.end[0] = nblocks;
+  return launch_dq_expand(a, (hipStream_t)s);
+}
+
 ql_status nf4_dequant(const uint8_t* packed, const float* absmax, int64_t n, int32_t out_dtype, void* out,
                       ql_stream s) {
   clear_error();
@@ -869,7 +946,8 @@ static ql_status stack_fwd(const ql_stack_cfg* cfg, const StackCall& sc, const v
       if (have_ready[slot]) QL_HIP_CHECK(hipStreamWaitEvent(C, ev.ready[slot], 0));
       base = sl8 + slot * rec;
     }
-    const LayerW W = layer_weights(sc.SL, base);
+    LayerW W;
+    QL_TRY(layer_weights_ready(cfg, sc.SL, sc.WS, base, w8, C, W));
     if (lora) {
       uint8_t* svl = sv + (size_t)l * sc.SV.per_layer;
       uint16_t* h_out = (l + 1 < L) ? (uint16_t*)(sv + (size_t)(l + 1) * sc.SV.per_layer + sc.SV.off[QL_SAVED_H_IN])
@@ -1017,7 +1095,8 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
       base = sl8 + slot * rec;
     }
     uint16_t* out = (l == 0 && dx0) ? (uint16_t*)dx0 : (((L - 1 - l) & 1) ? dhB : dhA);
-    const LayerW W = layer_weights(sc.SL, base);
+    LayerW W;
+    QL_TRY(layer_weights_ready(cfg, sc.SL, sc.WS, base, w8, C, W));
     const uint8_t* svl = sv + (size_t)l * sc.SV.per_layer;
     if (cfg->recompute) {
       // recompute the layer's activations from its saved input, with the

@@ -57,6 +57,8 @@ ql_status set_error(ql_status st, const char* fmt, ...);
   } while (0)
 
 // ---------------------------------------------------------------- launchers
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
 // All launchers enqueue on `st` and report launch errors through the status.
 
 ql_status launch_nf4_quantize(const float* w, int64_t n, uint8_t* packed, float* absmax,
@@ -64,6 +66,24 @@ ql_status launch_nf4_quantize(const float* w, int64_t n, uint8_t* packed, float*
 ql_status launch_clear_i32(int* p, int n, hipStream_t st);
 ql_status launch_nf4_dequant(const uint8_t* packed, const float* absmax, int64_t n, int out_f32,
                              void* out, hipStream_t st);
+
+// Double-quantised scales (nf4_dq.hip): stored block of n 8-bit scales.
+struct DqLayout {
+  size_t scale_off, mean_off, bytes;
+};
+DqLayout dq_layout(int64_t n);
+// block <- double quantisation of the n float32 scales c
+ql_status launch_dq_quant(const float* c, int64_t n, uint8_t* block, hipStream_t st);
+// Expansion of several blocks back to float32 scales, one launch.
+constexpr int kMaxDq = 8;
+struct DqExpandArgs {
+  const uint8_t* src[kMaxDq];
+  size_t scale_off[kMaxDq], mean_off[kMaxDq];
+  float* dst[kMaxDq];
+  int64_t end[kMaxDq];  // cumulative scale counts
+  int32_t nblk;
+};
+ql_status launch_dq_expand(const DqExpandArgs& a, hipStream_t st);
 
 // Segment of a fused NF4 GEMM: one frozen projection with its LoRA factors.
 struct FwdSeg {

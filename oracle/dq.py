@@ -119,8 +119,12 @@ def mean_scale(c) -> np.float32:
     return np.float32(total / n)
 
 
-def double_quant(c):
-    """float32 scales [n] -> (codes uint8 [n], run scales float32 [ceil(n/256)], mu float32)."""
+def double_quant(c, only_runs=None):
+    """float32 scales [n] -> (codes uint8 [n], run scales float32 [ceil(n/256)], mu float32).
+
+    only_runs: quantise just these runs (the others stay zero), for sampled
+    checks of large tensors; mu is always that of the whole tensor.
+    """
     c = np.asarray(c, np.float32).ravel()
     if not np.all(np.isfinite(c)):
         raise ValueError("non-finite scale")
@@ -129,7 +133,7 @@ def double_quant(c):
     d = (c - mu).astype(np.float32)                       # float32 subtraction
     codes = np.zeros(n, np.uint8)
     scales = np.zeros(runs(n), np.float32)
-    for b in range(runs(n)):
+    for b in (range(runs(n)) if only_runs is None else only_runs):
         db = d[b * RUN:(b + 1) * RUN]
         m = np.float32(np.max(np.abs(db)))
         s = np.float32(m / np.float32(E4M3_MAX))           # float32 division

@@ -10,7 +10,7 @@ from gpu_util import DEV, f64, ql
 
 class GpuStack:
     def __init__(self, name, L=None, M=None, gen_device="cpu", pinned=True, resident_copy=True, n_buffers=2,
-                 recompute=0):
+                 recompute=0, absmax_dq=0):
         w = dict(synth.WORKLOADS[name])
         if L is not None:
             w["L"] = L
@@ -20,7 +20,7 @@ class GpuStack:
         self.name = name
         self.M = w["M"]
         self.cfg = ql.StackCfg(w["L"], w["H"], w["I"], w["KV"], w["head_dim"], w["r"], w["alpha"],
-                               n_buffers=n_buffers, recompute=recompute)
+                               n_buffers=n_buffers, recompute=recompute, absmax_dq=absmax_dq)
         inp = synth.stack_inputs(w["L"], w["M"], w["H"], w["I"], w["KV"], w["r"], (name,), device=gen_device)
         self.inp = inp
         stores = [{p: (d[p]["packed"], d[p]["absmax"]) for p in ql.PROJ} for d in inp["layers"]]

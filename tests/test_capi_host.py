@@ -13,6 +13,7 @@ import torch
 from gpu_util import ROOT, lib, ql
 from oracle import nf4 as onf4
 from oracle import stack as ostack
+from oracle import dq as dq_oracle
 
 HEADER = os.path.join(ROOT, "include", "nf4qlora.h")
 
@@ -143,3 +144,18 @@ def test_stack_cfg_validation():
         with pytest.raises(ql.QlError) as e:
             ql.stream_layer_stack_layout(cfg)
         assert e.value.status == st, (cfg, ql.ql_last_error())
+
+
+def test_double_quantised_store_is_the_pages_size():
+    # with double-quantised scales the 8B stack's store is the pages' 3.60 GB
+    # with 113 MB layer records (README header figure), Qwen2.5-3B's 1.43 GB
+    lib()
+    c8 = ql.StackCfg(32, 4096, 14336, 1024, 128, 16, 32.0, absmax_dq=1)
+    offs, proj, total = ql.stream_layer_stack_layout(c8)
+    assert total == 3600474112 and offs[1] == 112514816
+    assert round(total / 1e9, 2) == 3.60 and round(offs[1] / 1e6) == 113
+    c3 = ql.StackCfg(36, 2048, 11008, 256, 128, 16, 32.0, absmax_dq=1)
+    assert round(ql.stream_layer_stack_layout(c3)[2] / 1e9, 2) == 1.43
+    # and the block layout matches the oracle's
+    for n in (1, 256, 1000, 917504):
+        assert ql.nf4_dq_layout(n) == dq_oracle.block_layout(n)
