@@ -36,6 +36,8 @@ the whole step (M tokens per step). The JSON line also carries:
   (only layer inputs saved; the backward recomputes each layer from its slot).
 * double_quant - the same streamed step from a store whose block scales are
   double-quantised (nf4_double_quant; the pages' 3.60 GB form of this store).
+* small_stack_graph - the launch-bound SmolLM2-shaped stack: eager steps
+  against the same step captured once into a HIP graph and replayed.
 * resident - the same step with the store resident in HBM (no copies).
 * cpu_baseline - the CPU oracle timed on a bounded sample.
 """
@@ -141,6 +143,52 @@ def build_dq_store(ql, torch, cfg, store, dev):
             dq_store[dst + aq: dst + aq + blk.numel()].copy_(blk)
     torch.cuda.synchronize()
     return cfg_dq, dq_store
+
+
+def small_stack_graph(ql, synth, torch, dev, steps=20, warmup=3):
+    """The SmolLM2-shaped streamed stack (30 layers, hidden 576, M = 512): a
+    step issues about 1,400 kernels, so launches bound it. tok/s of eager steps
+    and of the same step captured once and replayed (stream_layer_stack_step_capture)."""
+    w = synth.WORKLOADS["smollm2_stack"]
+    M = w["M"]
+    cfg, store, offs, lora, x, dy = build_inputs(ql, synth, torch, w, dev)
+    slots_b, saved_b, ws_b = ql.stream_layer_stack_workspace(cfg, M)
+    slots = torch.empty(slots_b, dtype=torch.uint8, device=dev)
+    saved = torch.empty(saved_b, dtype=torch.uint8, device=dev)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    y = torch.empty(M, w["H"], dtype=torch.bfloat16, device=dev)
+    dx = torch.empty_like(y)
+    dA = [{p: torch.empty(w["r"], cfg.proj_shape(p)[1], device=dev) for p in ql.PROJ} for _ in range(w["L"])]
+    dB = [{p: torch.empty(cfg.proj_shape(p)[0], w["r"], device=dev) for p in ql.PROJ} for _ in range(w["L"])]
+    compute, copy = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+
+    def eager(turnaround):
+        ql.stream_layer_stack_fwd(cfg, store, lora, x, M, y, saved, slots, ws, compute, copy,
+                                  reuse_bwd_slots=int(turnaround))
+        ql.stream_layer_stack_bwd(cfg, store, lora, dy, M, saved, dx, dA, dB, 0, 1, slots, ws, compute, copy)
+
+    for i in range(warmup):
+        eager(i > 0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        eager(True)
+    torch.cuda.synchronize()
+    te = (time.perf_counter() - t0) / steps
+    g = ql.stream_layer_stack_step_capture(cfg, store, lora, x, dy, M, y, saved, dx, dA, dB, 0, 1, slots, ws,
+                                           compute, copy)
+    for _ in range(warmup):
+        g.launch(compute)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.launch(compute)
+    torch.cuda.synchronize()
+    tg = (time.perf_counter() - t0) / steps
+    g.destroy()
+    return dict(workload="smollm2_stack: 30 layers, hidden 576, intermediate 1536, kv 192, r8, M=512, streamed",
+                eager=dict(value=round(M / te, 1), ms_per_step=round(1000 * te, 3)),
+                graph=dict(value=round(M / tg, 1), ms_per_step=round(1000 * tg, 3)), unit="tok/s")
 
 
 def dense_gemm_ceiling(torch, dev, M, w, reps=10):
@@ -426,6 +474,9 @@ def main():
                         pcie_GBs=round(copies * rec_dq / (msdq * 1e-3) / 1e9, 2), status=int(status_dq))
     del dq_store
 
+    log("bench: SmolLM2-shaped stack, eager and captured steps")
+    small = small_stack_graph(ql, synth, torch, dev)
+
     dense = dense_gemm_ceiling(torch, dev, M, w)
     gemm_all["vs_dense_bf16"] = round(gemm_all["tflops"] / dense["tflops"], 4)
 
@@ -475,6 +526,7 @@ def main():
         "with_reference": with_ref,
         "recompute": recompute,
         "double_quant": double_quant,
+        "small_stack_graph": small,
         "resident": resident,
         "cpu_baseline": cpu,
     }

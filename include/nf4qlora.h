@@ -314,6 +314,35 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
                                  int32_t reuse_fwd_slots, void* slots, size_t slots_bytes,
                                  void* ws, size_t ws_bytes, ql_stream compute, ql_stream copy);
 
+/* --------------------------------------------------------------- step graphs
+ * A whole training step (stream_layer_stack_fwd then stream_layer_stack_bwd
+ * with reuse_fwd_slots = 1) captured once into a HIP graph and replayed with
+ * one launch. A small model's layer loop is bound by per-launch cost, not by
+ * the GPU (the SmolLM2 shape issues about 1,400 kernels per step); the pages
+ * meet the same kind of limit when an H100 runs no faster than a laptop GPU
+ * at batch 1 (Soup README, "Citing Soup", v3 notes). All pointers are baked into the
+ * graph: between replays the caller rewrites the contents of x0 and dy (and
+ * of lora's factors), never their addresses. turnaround = 1: the forward
+ * reuses the layers the previous step's backward left in the slots (the
+ * first replay must then follow a step of this cfg on the same slots);
+ * turnaround = 0: every replay copies its first layers itself. The store must
+ * be page-locked host memory (or a device store in resident mode) and kernel
+ * timing must be off. The capture enqueues nothing that runs; a replay runs
+ * on `stream` like the two calls would on `compute` (the copies keep their own
+ * engine), and results are bitwise those of the uncaptured calls.
+ * Capturing code must not create hipMemsetAsync nodes; none is used here.
+ */
+typedef struct ql_step_graph_s* ql_step_graph;
+ql_status stream_layer_stack_step_capture(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
+                                          const ql_lora* lora, const void* x0, const void* dy, int64_t M,
+                                          void* y, void* saved, size_t saved_bytes, void* dx0,
+                                          float* const* dA, float* const* dB, int32_t accumulate,
+                                          int32_t turnaround, void* slots, size_t slots_bytes, void* ws,
+                                          size_t ws_bytes, ql_stream compute, ql_stream copy,
+                                          ql_step_graph* out);
+ql_status ql_step_graph_launch(ql_step_graph g, ql_stream stream);
+ql_status ql_step_graph_destroy(ql_step_graph g);
+
 /* ----------------------------------------------------------- measurement
  * Kernel timing for roofline measurement. While enabled, every launch of the
  * fused NF4 GEMM kernels is bracketed by two hipEvents recorded on the stream

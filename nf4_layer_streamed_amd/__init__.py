@@ -30,7 +30,7 @@ EXPORTS = (
     "qlora_linear_workspace", "qlora_linear_fwd", "qlora_linear_bwd",
     "stream_layer_stack_layout", "stream_layer_stack_workspace", "stream_layer_stack_saved_layout",
     "stream_layer_stack_fwd", "stream_layer_stack_fwd_ref", "stream_layer_stack_bwd", "ql_profile_enable",
-    "ql_profile_read",
+    "ql_profile_read", "stream_layer_stack_step_capture", "ql_step_graph_launch", "ql_step_graph_destroy",
 )
 QL_KERNEL_GEMM_FWD, QL_KERNEL_GEMM_BWD, QL_KERNEL_GEMM_FWD_NARROW, QL_KERNEL_GEMM_BWD_NARROW = 0, 1, 2, 3
 # kernel symbol of each profiling id (the names rocprofv3 reports)
@@ -92,6 +92,11 @@ def load(path=LIB_PATH):
                                          P, SZ, P, P]),
         "stream_layer_stack_fwd_ref": (I32, [ctypes.POINTER(ql_stack_cfg), P, SZ, P, P, I64, P, P, SZ, P, P, SZ,
                                              I32, P, SZ, P, SZ, P, P]),
+        "stream_layer_stack_step_capture": (I32, [ctypes.POINTER(ql_stack_cfg), P, SZ, P, P, P, I64, P, P, SZ, P,
+                                                  P, P, I32, I32, P, SZ, P, SZ, P, P,
+                                                  ctypes.POINTER(ctypes.c_void_p)]),
+        "ql_step_graph_launch": (I32, [P, P]),
+        "ql_step_graph_destroy": (I32, [P]),
         "stream_layer_stack_bwd": (I32, [ctypes.POINTER(ql_stack_cfg), P, SZ, P, P, I64, P, SZ, P, P, P,
                                          I32, I32, P, SZ, P, SZ, P, P]),
         "ql_profile_enable": (I32, [I32]),
@@ -308,6 +313,44 @@ def stream_layer_stack_bwd(cfg, store, lora, dy, M, saved, dx0, dA, dB, accumula
         ctypes.byref(c), _ptr(store), _nbytes(store), arr, _ptr(dy), M, _ptr(saved), _nbytes(saved), _ptr(dx0),
         pa, pb, int(accumulate), int(reuse_fwd_slots), _ptr(slots), _nbytes(slots), _ptr(ws), _nbytes(ws),
         _stream(compute), _stream(copy)))
+
+
+class StepGraph:
+    """A captured training step (stream_layer_stack_step_capture); launch() replays it."""
+
+    def __init__(self, handle, keep):
+        self._h = handle
+        self._keep = keep   # the tensors whose addresses the graph holds
+
+    def launch(self, stream=None):
+        return _check(load().ql_step_graph_launch(self._h, _stream(stream)))
+
+    def destroy(self):
+        if self._h:
+            load().ql_step_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def stream_layer_stack_step_capture(cfg, store, lora, x0, dy, M, y, saved, dx0, dA, dB, accumulate, turnaround,
+                                    slots, ws, compute, copy=None):
+    """Captures fwd + bwd (reuse_fwd_slots = 1) into a graph; see the header for the rules."""
+    c = cfg.c()
+    arr = _lora_array(cfg, lora)
+    n = cfg.n_layers * NPROJ
+    pa = (ctypes.c_void_p * n)(*[dA[l][p].data_ptr() for l in range(cfg.n_layers) for p in PROJ])
+    pb = (ctypes.c_void_p * n)(*[dB[l][p].data_ptr() for l in range(cfg.n_layers) for p in PROJ])
+    h = ctypes.c_void_p()
+    _check(load().stream_layer_stack_step_capture(
+        ctypes.byref(c), _ptr(store), _nbytes(store), arr, _ptr(x0), _ptr(dy), M, _ptr(y), _ptr(saved),
+        _nbytes(saved), _ptr(dx0), pa, pb, int(accumulate), int(turnaround), _ptr(slots), _nbytes(slots), _ptr(ws),
+        _nbytes(ws), _stream(compute), _stream(copy), ctypes.byref(h)))
+    return StepGraph(h, (store, x0, dy, y, saved, dx0, dA, dB, slots, ws, lora))
 
 
 def build_store(cfg, layers, pinned=True, device=None):

@@ -1123,4 +1123,77 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
   return sc.pageable ? QL_WARN_PAGEABLE_HOST : QL_OK;
 }
 
+
+// ------------------------------------------------------------- step graphs
+struct ql_step_graph_s {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+ql_status stream_layer_stack_step_capture(const ql_stack_cfg* cfg, const void* store, size_t store_bytes,
+                                          const ql_lora* lora, const void* x0, const void* dy, int64_t M, void* y,
+                                          void* saved, size_t saved_bytes, void* dx0, float* const* dA,
+                                          float* const* dB, int32_t accumulate, int32_t turnaround, void* slots,
+                                          size_t slots_bytes, void* ws, size_t ws_bytes, ql_stream compute,
+                                          ql_stream copy, ql_step_graph* out) {
+  clear_error();
+  const char* fn = "stream_layer_stack_step_capture";
+  if (!out) return set_error(QL_ERR_ARG, "%s: out is NULL", fn);
+  *out = nullptr;
+  StackCall sc;
+  QL_TRY(validate_stack(fn, cfg, store, store_bytes, lora, M, saved, saved_bytes, slots, slots_bytes, ws,
+                        ws_bytes, sc));
+  if (sc.pageable)
+    return set_error(QL_ERR_UNSUPPORTED, "%s: a pageable host store cannot be captured (copies need page-locked "
+                     "memory)", fn);
+  if (turnaround != 0 && turnaround != 1) return set_error(QL_ERR_ARG, "%s: turnaround must be 0 or 1", fn);
+  if (profiling_on()) return set_error(QL_ERR_UNSUPPORTED, "%s: kernel timing is on (ql_profile_enable)", fn);
+  if (!compute) return set_error(QL_ERR_ARG, "%s: capture needs an explicit compute stream", fn);
+  if (M == 0) return set_error(QL_ERR_SHAPE, "%s: M must be >= 1", fn);
+  hipStream_t C = (hipStream_t)compute;
+  QL_HIP_CHECK(hipStreamBeginCapture(C, hipStreamCaptureModeRelaxed));
+  ql_status st = stream_layer_stack_fwd(cfg, store, store_bytes, lora, x0, M, y, saved, saved_bytes, turnaround,
+                                        slots, slots_bytes, ws, ws_bytes, compute, copy);
+  if (st >= 0)
+    st = stream_layer_stack_bwd(cfg, store, store_bytes, lora, dy, M, saved, saved_bytes, dx0, dA, dB, accumulate,
+                                1, slots, slots_bytes, ws, ws_bytes, compute, copy);
+  hipGraph_t g = nullptr;
+  const hipError_t ec = hipStreamEndCapture(C, &g);  // always ends the capture
+  if (st < 0) {
+    if (g) (void)hipGraphDestroy(g);
+    return st;
+  }
+  if (ec != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    return set_error(QL_ERR_HIP, "%s: hipStreamEndCapture: %s", fn, hipGetErrorString(ec));
+  }
+  hipGraphExec_t e = nullptr;
+  const hipError_t ei = hipGraphInstantiate(&e, g, nullptr, nullptr, 0);
+  if (ei != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return set_error(QL_ERR_HIP, "%s: hipGraphInstantiate: %s", fn, hipGetErrorString(ei));
+  }
+  ql_step_graph_s* h = new ql_step_graph_s;
+  h->graph = g;
+  h->exec = e;
+  *out = h;
+  return QL_OK;
+}
+
+ql_status ql_step_graph_launch(ql_step_graph g, ql_stream stream) {
+  clear_error();
+  if (!g) return set_error(QL_ERR_ARG, "ql_step_graph_launch: graph is NULL");
+  QL_HIP_CHECK(hipGraphLaunch(g->exec, (hipStream_t)stream));
+  return QL_OK;
+}
+
+ql_status ql_step_graph_destroy(ql_step_graph g) {
+  clear_error();
+  if (!g) return QL_OK;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  delete g;
+  return QL_OK;
+}
+
 }  // extern "C"
