@@ -77,7 +77,7 @@ static ql_status device_flag(int** out) {
 // --------------------------------------------------------- linear helpers
 struct LinearWs {
   size_t fwd, bwd;
-  size_t bt_off, g_off, scratch_off;
+  size_t bt_off, g_off, scratch_off, partial_off;
 };
 
 static LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
@@ -90,7 +90,8 @@ static LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   size_t c1 = colred_ws_bytes(M, N, r), c2 = colred_ws_bytes(M, K, r);
   if (c1 > scratch) scratch = c1;
   if (c2 > scratch) scratch = c2;
-  w.bwd = w.scratch_off + align256(scratch);
+  w.partial_off = w.scratch_off + align256(scratch);
+  w.bwd = w.partial_off + align256(bwd_partial_bytes(M, K));
   return w;
 }
 
@@ -183,7 +184,7 @@ static SavedLayout saved_layout(const ql_stack_cfg* c, int64_t M) {
 // internal temporaries of the stack (offsets into ws); with recompute also one
 // layer of activations (ck, full layout) and the recomputed layer output
 struct StackWs {
-  size_t dhA, dhB, dhmid, dact, dg, du, dn, da32, dv, bt, G[5], scratch, ck, ck_out;
+  size_t dhA, dhB, dhmid, dact, dg, du, dn, da32, dv, bt, G[5], scratch, ck, ck_out, partial, partial_bytes;
   size_t absx[QL_NPROJ];  // absmax_dq: the layer's expanded float32 scales
   size_t total;
 };
@@ -217,6 +218,10 @@ static StackWs stack_ws(const ql_stack_cfg* c, int64_t M) {
   mx(colred_ws_bytes(M, I, r));
   mx(colred_ws_bytes(M, KV, r));
   w.scratch = take(sc);
+  // float32 partials of the split dX GEMMs (outputs of I or H columns)
+  w.partial_bytes = bwd_partial_bytes(M, I) > bwd_partial_bytes(M, H) ? bwd_partial_bytes(M, I)
+                                                                      : bwd_partial_bytes(M, H);
+  w.partial = take(w.partial_bytes);
   for (int p = 0; p < QL_NPROJ; ++p) w.absx[p] = 0;
   if (c->absmax_dq) {
     const int64_t n[QL_NPROJ] = {H, KV, KV, H, I, I, H};
@@ -409,6 +414,7 @@ static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     BwdArgs a{};
     a.M = M; a.K = I; a.r = r; a.s = s; a.out = T(WS.dact); a.nseg = 1;
     a.seg[0] = BwdSeg{dh, W.packed[QL_PROJ_DOWN], W.absmax[QL_PROJ_DOWN], Gd, u16(lo[QL_PROJ_DOWN].A), H};
+    a.partial = (float*)(ws + WS.partial); a.partial_bytes = WS.partial_bytes;
     QL_TRY(launch_gemm_bwd(a, st));
   }
   QL_TRY(lora_grads(dh, H, S(QL_SAVED_U0 + QL_PROJ_DOWN), S(QL_SAVED_ACT), I, 0, 0, I, Gd, M, r, s,
@@ -425,6 +431,7 @@ static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     a.M = M; a.K = H; a.r = r; a.s = s; a.out = T(WS.dn); a.nseg = 2;
     a.seg[0] = BwdSeg{T(WS.dg), W.packed[QL_PROJ_GATE], W.absmax[QL_PROJ_GATE], Gg, u16(lo[QL_PROJ_GATE].A), I};
     a.seg[1] = BwdSeg{T(WS.du), W.packed[QL_PROJ_UP], W.absmax[QL_PROJ_UP], Gu, u16(lo[QL_PROJ_UP].A), I};
+    a.partial = (float*)(ws + WS.partial); a.partial_bytes = WS.partial_bytes;
     QL_TRY(launch_gemm_bwd(a, st));
   }
   QL_TRY(lora_grads(T(WS.dg), I, S(QL_SAVED_U0 + QL_PROJ_GATE), S(QL_SAVED_N2), H, 0, 0, H, Gg, M, r, s,
@@ -441,6 +448,7 @@ static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     BwdArgs a{};
     a.M = M; a.K = H; a.r = r; a.s = s; a.out = ws + WS.da32; a.out_f32 = 1; a.nseg = 1;
     a.seg[0] = BwdSeg{dhm, W.packed[QL_PROJ_O], W.absmax[QL_PROJ_O], Go, u16(lo[QL_PROJ_O].A), H};
+    a.partial = (float*)(ws + WS.partial); a.partial_bytes = WS.partial_bytes;
     QL_TRY(launch_gemm_bwd(a, st));
   }
   QL_TRY(lora_grads(dhm, H, S(QL_SAVED_U0 + QL_PROJ_O), S(QL_SAVED_V), KV, c->head_dim, n_rep, H, Go, M,
@@ -453,6 +461,7 @@ static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     BwdArgs a{};
     a.M = M; a.K = H; a.r = r; a.s = s; a.out = T(WS.dn); a.nseg = 1;
     a.seg[0] = BwdSeg{T(WS.dv), W.packed[QL_PROJ_V], W.absmax[QL_PROJ_V], Gv, u16(lo[QL_PROJ_V].A), KV};
+    a.partial = (float*)(ws + WS.partial); a.partial_bytes = WS.partial_bytes;
     QL_TRY(launch_gemm_bwd(a, st));
   }
   QL_TRY(lora_grads(T(WS.dv), KV, S(QL_SAVED_U0 + QL_PROJ_V), S(QL_SAVED_N1), H, 0, 0, H, Gv, M, r, s,
@@ -850,6 +859,8 @@ ql_status qlora_linear_bwd(const void* dy, const void* x, const void* u_saved, i
     BwdArgs a{};
     a.M = M; a.K = W.K; a.r = L.r; a.s = sc; a.out = dx; a.nseg = 1;
     a.seg[0] = BwdSeg{u16(dy), W.packed, W.absmax, G, u16(L.A), W.N};
+    a.partial = (float*)(w8 + lw.partial_off);
+    a.partial_bytes = bwd_partial_bytes(M, W.K);
     QL_TRY(launch_gemm_bwd(a, st));
   }
   return lora_grads(u16(dy), W.N, u16(u_saved), u16(x), W.K, 0, 0, W.K, G, M, L.r, sc, dA, dB, accumulate,

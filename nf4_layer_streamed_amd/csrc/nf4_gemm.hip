@@ -623,7 +623,9 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
   const int t = threadIdx.x, lane = t & 63, g = lane >> 5, li = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w >> 1, wn = w & 1;
 
-  const int tile = (int)xcd_remap(blockIdx.x, (uint32_t)tiles_total);
+  // grid = tiles x nsplit; split sp of a tile takes weight steps [WS sp / S, WS (sp + 1) / S)
+  const int gt = (int)xcd_remap(blockIdx.x, (uint32_t)(tiles_total * a.nsplit));
+  const int sp = gt / tiles_total, tile = gt % tiles_total;
   const int64_t m0 = (int64_t)(tile % tiles_m) * BM;
   const int64_t k0 = (int64_t)k_base + (int64_t)(tile / tiles_m) * BN;
   const int64_t K = a.K, kbn = K / 64, M = a.M;
@@ -645,11 +647,20 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
   const __amdgpu_buffer_rsrc_t yr0 = ydesc(0, N0), yr1 = ydesc(1, N1), yr2 = ydesc(2, N2);
   const __amdgpu_buffer_rsrc_t cr0 = cdesc(0, N0), cr1 = cdesc(1, N1), cr2 = cdesc(2, N2);
   const __amdgpu_buffer_rsrc_t sr0 = sdesc(0, N0), sr1 = sdesc(1, N1), sr2 = sdesc(2, N2);
-  const int WS = (int)((N0 + BK - 1) / BK + (N1 + BK - 1) / BK + (N2 + BK - 1) / BK);
+  const int WS_all = (int)((N0 + BK - 1) / BK + (N1 + BK - 1) / BK + (N2 + BK - 1) / BK);
+  const int ws_begin = (int)((int64_t)WS_all * sp / a.nsplit);
+  const int WS = (int)((int64_t)WS_all * (sp + 1) / a.nsplit) - ws_begin;
 
   // DMA cursors (segment, first reduction row) of the next dY tile and the
-  // next raw step; both walk the weight steps in order.
-  int sgA = 0, nbA = 0, sgR = 0, nbR = 0;
+  // next raw step; both walk the weight steps in order from ws_begin.
+  int sgA = 0, nbA = 0;
+  {
+    int s = ws_begin;
+    const int st0 = (int)((N0 + BK - 1) / BK), st1 = (int)((N1 + BK - 1) / BK);
+    if (s >= st0) { s -= st0; ++sgA; if (s >= st1) { s -= st1; ++sgA; } }
+    nbA = s * BK;
+  }
+  int sgR = sgA, nbR = nbA;
   auto advance = [&](int& sg, int& nb) {
     const int64_t N = sel3(sg, N0, N1, N2);
     nb += BK;
@@ -817,7 +828,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
   const bool dthread = t < UNITS;
   const int drow = t & 63, dblk = (t >> 6) % (BN / 64);
   const int64_t dk = k0 + 64 * dblk;
-  for (int sg = 0; sg < nseg; ++sg) {
+  for (int sg = 0; sg < (sp == a.nsplit - 1 ? nseg : 0); ++sg) {
     const BwdSeg& S = a.seg[sg];
     uint8_t* As = smem + (sg & 1) * A_TILE;
     uint8_t* Bs = smem + OFF_D + (sg & 1) * DEC_BYTES;
@@ -866,6 +877,10 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
         if (k >= K) continue;
         const int64_t o = m * K + k;
         float f[4] = {acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]};
+        if (a.nsplit > 1) {  // float32 partial of this split; the sum kernel finishes the output
+          *(float4*)(a.partial + (int64_t)sp * M * K + o) = make_float4(f[0], f[1], f[2], f[3]);
+          continue;
+        }
         if (a.resid) {
           const uint2 rv = *(const uint2*)(a.resid + o);
           f[0] += __builtin_bit_cast(float, rv.x << 16);
@@ -968,13 +983,22 @@ FwdSeg seg_from(const FwdSeg& S, int64_t c, int64_t K, int r) {
 }  // namespace
 
 // Launch geometry. Tiles are 256 x 256 (wide) or 256 x 128 (narrow); the chip
-// runs cu_count workgroups per round. One partial round: the wide tile unless
-// narrow tiles fill more CUs. Several rounds: the whole rounds take wide tiles
-// and the column blocks of the last, partial round are re-cut into narrow
-// tiles (twice as many, half the work each) in a second launch, so that round
-// fills the chip (for the 8B gate|up at M = 2048: 3 wide rounds + 1 narrow
-// instead of 4 wide rounds). The geometry depends on shapes only, so resident
+// runs cu_count workgroups per round. A narrow tile does half a wide tile's
+// work but runs at a lower rate: it takes about kNarrowFwd (kNarrowBwd for dX)
+// of a wide tile's time, from the two builds' measured rates. A partial round
+// is re-cut into narrow tiles only when that takes fewer wide-tile times
+// (8B q|k|v forward at M = 2048: 192 wide tiles in one round beat 384 narrow
+// ones in two, 23% faster; 128 wide tiles are better as 256 narrow ones). With
+// several rounds the whole rounds take wide tiles and the last partial round
+// follows the same rule in a second launch (8B gate|up: 3 wide rounds + 1
+// narrow instead of 4 wide). The geometry depends on shapes only, so resident
 // and streamed runs pick the same kernels.
+constexpr double kNarrowFwd = 0.7, kNarrowBwd = 0.85;
+// 1 if re-cutting t wide tiles (t <= C) into tn narrow ones takes less time.
+int narrow_pays(int t, int tn, int C, double ratio) {
+  const int wide_rounds = (t + C - 1) / C, narrow_rounds = (tn + C - 1) / C;
+  return ratio * narrow_rounds < (double)wide_rounds ? 1 : 0;
+}
 ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st) {
   if (a.M == 0) return QL_OK;
   QL_TRY_PROF(ensure_attrs());
@@ -985,9 +1009,9 @@ ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st) {
     t256 += tiles_m * (int)((a.seg[s].N + 255) / 256);
     t128 += tiles_m * (int)((a.seg[s].N + 127) / 128);
   }
-  if (t256 <= C) return launch_fwd_tiles(a, t256 == C || t128 <= t256, st);
+  if (t256 <= C) return launch_fwd_tiles(a, narrow_pays(t256, t128, C, kNarrowFwd) == 0, st);
   const int full = (t256 / C) * C;
-  if (full == t256) return launch_fwd_tiles(a, true, st);
+  if (full == t256 || !narrow_pays(t256 - full, 2 * (t256 - full), C, kNarrowFwd)) return launch_fwd_tiles(a, true, st);
   // split at the column block holding wide tile `full` (enumeration order:
   // segment, column block, row block)
   FwdArgs aw = a, an = a;
@@ -1029,11 +1053,12 @@ ql_status launch_bwd_tiles(const BwdArgs& a, bool wide, int64_t k_base, int64_t 
   hipEvent_t e0 = nullptr, e1 = nullptr;
   const bool prof = profiling_on();
   if (prof) QL_TRY_PROF(profile_begin(&e0, &e1));
+  const int grid = total * a.nsplit;
   if (wide)
-    hipExtLaunchKernelGGL(k_gemm_bwd<128>, dim3(total), dim3(NT), bwd_lds<256>(), st, e0, e1, 0, a, tiles_m, total,
+    hipExtLaunchKernelGGL(k_gemm_bwd<128>, dim3(grid), dim3(NT), bwd_lds<256>(), st, e0, e1, 0, a, tiles_m, total,
                           (int)k_base);
   else
-    hipExtLaunchKernelGGL(k_gemm_bwd<64>, dim3(total), dim3(NT), bwd_lds<128>(), st, e0, e1, 0, a, tiles_m, total,
+    hipExtLaunchKernelGGL(k_gemm_bwd<64>, dim3(grid), dim3(NT), bwd_lds<128>(), st, e0, e1, 0, a, tiles_m, total,
                           (int)k_base);
   QL_HIP_CHECK(hipGetLastError());
   if (prof) {
@@ -1046,18 +1071,82 @@ ql_status launch_bwd_tiles(const BwdArgs& a, bool wide, int64_t k_base, int64_t 
 
 }  // namespace
 
-// Same geometry rule as the forward: whole rounds on wide tiles, the column
-// blocks of a last partial round on narrow tiles in a second launch.
-ql_status launch_gemm_bwd(const BwdArgs& a, hipStream_t st) {
-  if (a.M == 0) return QL_OK;
+// Sum of the split partials in split order, plus the residual, rounded once
+// (the same float32 operations as the unsplit epilogue: acc + resid).
+__global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ p, int nsplit, int64_t MK,
+                                                   const uint16_t* __restrict__ resid, void* __restrict__ out,
+                                                   int out_f32) {
+  const int64_t n4 = MK / 4, stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n4; g += stride) {
+    float4 f = ((const float4*)p)[g];
+    for (int s = 1; s < nsplit; ++s) {
+      const float4 q = ((const float4*)(p + (int64_t)s * MK))[g];
+      f.x += q.x;
+      f.y += q.y;
+      f.z += q.z;
+      f.w += q.w;
+    }
+    if (resid) {
+      const uint2 rv = ((const uint2*)resid)[g];
+      f.x += __builtin_bit_cast(float, rv.x << 16);
+      f.y += __builtin_bit_cast(float, rv.x & 0xffff0000u);
+      f.z += __builtin_bit_cast(float, rv.y << 16);
+      f.w += __builtin_bit_cast(float, rv.y & 0xffff0000u);
+    }
+    if (out_f32)
+      ((float4*)out)[g] = f;
+    else
+      ((uint2*)out)[g] = make_uint2(pack_bf16x2(f.x, f.y), pack_bf16x2(f.z, f.w));
+  }
+}
+
+int bwd_max_split(int64_t M, int64_t K) {
+  const int64_t t256 = ((M + BM - 1) / BM) * ((K + 255) / 256);
+  if (t256 <= 0 || 2 * t256 > 256) return 1;
+  const int64_t s = 256 / t256;
+  return (int)(s > 8 ? 8 : s);
+}
+
+// Geometry. When 256 x 256 tiles alone would leave at least half the chip idle
+// and the caller gave space for partials, the reduction is split across up to
+// 8 workgroups per tile (each split keeps at least 64 weight steps: whole-call
+// timings at M = 2048 show 8B gate|up dX, 448 steps, 6% faster split in two,
+// while the 64- and 16-step o and v dX lose to the partial pass) and a second
+// kernel sums the partials. Otherwise the forward's rule: whole rounds
+// on wide tiles, the column blocks of a last partial round on narrow tiles in
+// a second launch. Shapes alone decide, so resident and streamed runs match.
+ql_status launch_gemm_bwd(const BwdArgs& a_in, hipStream_t st) {
+  if (a_in.M == 0) return QL_OK;
   QL_TRY_PROF(ensure_attrs());
+  BwdArgs a = a_in;
+  a.nsplit = 1;
   const int tiles_m = (int)((a.M + BM - 1) / BM);
   const int C = cu_count();
   const int t256 = tiles_m * (int)((a.K + 255) / 256);
   const int t128 = tiles_m * (int)((a.K + 127) / 128);
-  if (t256 <= C) return launch_bwd_tiles(a, t256 == C || t128 <= t256, 0, a.K, st);
+  if (a.partial && 2 * t256 <= C) {
+    int S = C / t256;
+    const int cap = bwd_max_split(a.M, a.K);
+    if (S > cap) S = cap;
+    int ws = 0;
+    for (int s = 0; s < a.nseg; ++s) ws += (int)((a.seg[s].N + BK - 1) / BK);
+    while (S > 1 && ws < 64 * S) --S;  // shorter slices lose more to the partial pass than they gain
+    while (S > 1 && (size_t)S * (size_t)a.M * (size_t)a.K * 4 > a.partial_bytes) --S;
+    if (S > 1) {
+      a.nsplit = S;
+      QL_TRY_PROF(launch_bwd_tiles(a, true, 0, a.K, st));
+      const int64_t MK = a.M * a.K;
+      int64_t grid = (MK / 4 + 255) / 256;
+      if (grid > 4096) grid = 4096;
+      hipLaunchKernelGGL(k_split_sum, dim3((unsigned)grid), dim3(256), 0, st, (const float*)a.partial, S, MK,
+                         a.resid, a.out, a.out_f32);
+      QL_HIP_CHECK(hipGetLastError());
+      return QL_OK;
+    }
+  }
+  if (t256 <= C) return launch_bwd_tiles(a, narrow_pays(t256, t128, C, kNarrowBwd) == 0, 0, a.K, st);
   const int full = (t256 / C) * C;
-  if (full == t256) return launch_bwd_tiles(a, true, 0, a.K, st);
+  if (full == t256 || !narrow_pays(t256 - full, 2 * (t256 - full), C, kNarrowBwd)) return launch_bwd_tiles(a, true, 0, a.K, st);
   const int64_t kw = (int64_t)(full / tiles_m) * 256;
   if (kw > 0) QL_TRY_PROF(launch_bwd_tiles(a, true, 0, kw, st));
   return launch_bwd_tiles(a, false, kw, a.K - kw, st);

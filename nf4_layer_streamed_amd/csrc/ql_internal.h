@@ -129,7 +129,23 @@ struct BwdArgs {
   const uint16_t* resid;
   int32_t nseg;
   BwdSeg seg[kMaxSegs];
+  // Split reduction (set by launch_gemm_bwd): nsplit > 1 workgroups share a
+  // tile, each over an equal slice of the weight steps (the last also takes
+  // the LoRA steps), writing float32 partials [nsplit][M x K] that a second
+  // kernel sums in split order. partial / partial_bytes: the caller's space
+  // for them (0: no split).
+  float* partial;
+  size_t partial_bytes;
+  int32_t nsplit;
 };
+// Largest split of a dX GEMM with M rows and K output columns on a chip of at
+// most 256 CUs (workspace sizing; 1 = never split): the split fills the chip
+// with 256 x 256 tiles when they alone would leave half of it idle.
+int bwd_max_split(int64_t M, int64_t K);
+inline size_t bwd_partial_bytes(int64_t M, int64_t K) {
+  const int s = bwd_max_split(M, K);
+  return s > 1 ? (size_t)s * (size_t)M * (size_t)K * 4 : 0;
+}
 
 ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st);
 
