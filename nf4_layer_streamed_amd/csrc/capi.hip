@@ -77,12 +77,13 @@ static ql_status device_flag(int** out) {
 // --------------------------------------------------------- linear helpers
 struct LinearWs {
   size_t fwd, bwd;
-  size_t bt_off, g_off, scratch_off, partial_off;
+  size_t fpartial_off, bt_off, g_off, scratch_off, partial_off;
 };
 
 static LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   LinearWs w;
-  w.fwd = align256(skinny_ws_bytes(M, K, r, 1));
+  w.fpartial_off = align256(skinny_ws_bytes(M, K, r, 1));
+  w.fwd = w.fpartial_off + align256(bwd_partial_bytes(M, N));
   w.bt_off = 0;
   w.g_off = align256((size_t)r * N * 2);
   w.scratch_off = w.g_off + align256((size_t)M * r * 2);
@@ -365,6 +366,8 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     g.packed = W.packed[QL_PROJ_DOWN]; g.absmax = W.absmax[QL_PROJ_DOWN];
     g.U = on ? S(QL_SAVED_U0 + QL_PROJ_DOWN) : nullptr; g.B = on ? u16(lo[QL_PROJ_DOWN].B) : nullptr;
     g.out = h_out; g.N = H; g.ldo = H; g.resid = S(QL_SAVED_H_MID);
+    a.partial = (float*)(ws + WS.partial);
+    a.partial_bytes = WS.partial_bytes;
     QL_TRY(launch_gemm_fwd(a, st));
   }
   return QL_OK;
@@ -816,6 +819,8 @@ ql_status qlora_linear_fwd(const void* x, int64_t M, ql_nf4_weight W, ql_lora L,
   FwdSeg& g = a.seg[0];
   g.packed = W.packed; g.absmax = W.absmax; g.U = u16(u_save); g.B = u16(L.B); g.out = y; g.N = W.N;
   g.ldo = W.N; g.col0 = 0; g.resid = nullptr;
+  a.partial = (float*)((uint8_t*)ws + lw.fpartial_off);
+  a.partial_bytes = bwd_partial_bytes(M, W.N);
   return launch_gemm_fwd(a, st);
 }
 

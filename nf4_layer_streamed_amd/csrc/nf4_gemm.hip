@@ -276,14 +276,18 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
   const int t = threadIdx.x, lane = t & 63, g = lane >> 5, li = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
 
-  const int tile = (int)xcd_remap(blockIdx.x, (uint32_t)tiles_total);
+  // grid = tiles x nsplit; split sp of a tile takes K-steps [KT_all sp / S, KT_all (sp + 1) / S)
+  const int gt = (int)xcd_remap(blockIdx.x, (uint32_t)(tiles_total * a.nsplit));
+  const int sp = gt / tiles_total, tile = gt % tiles_total;
   const int sg = tile >= seg_tile0_2 ? 2 : (tile >= seg_tile0_1 ? 1 : 0);
   const int local = tile - (sg == 2 ? seg_tile0_2 : (sg == 1 ? seg_tile0_1 : 0));
   const FwdSeg& S = a.seg[sg];
   const int64_t m0 = (int64_t)(local % tiles_m) * BM;
   const int64_t n0 = (int64_t)(local / tiles_m) * BN;
   const int64_t K = a.K, kb = K / 64, M = a.M, N = S.N;
-  const int KT = (int)(K / BK);
+  const int KT_all = (int)(K / BK);
+  const int ks0 = (int)((int64_t)KT_all * sp / a.nsplit);
+  const int KT = (int)((int64_t)KT_all * (sp + 1) / a.nsplit) - ks0;
 
   // X tile rows m0.. (zero past M), W rows n0.. (zero past N)
   const int64_t xrows = M - m0 < BM ? M - m0 : BM;
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
   // head / n_rep) so the loop has no divisions or branches.
   const int hd = a.n_rep > 0 ? a.head_dim : (1 << 30);
   const int nrep = a.n_rep > 0 ? a.n_rep : 1;
-  int ci = 0, hr = 0, hq = 0;
+  int ci = ks0 * BK, hr = 0, hq = 0;  // a split starts at column ks0 BK (splits never use the remap)
   auto xcol_next = [&]() -> int {
     const int c = 2 * (hq * hd + ci);
     ci += BK;
@@ -343,9 +347,9 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
 #pragma unroll
       for (int cc = 0; cc < BN / 128; ++cc) {
         const int c = w + 4 * cc;
-        dma16(cr, cs + 1024 * c, cvoff + 32 * c * (int)(K / 2), step * 32);
+        dma16(cr, cs + 1024 * c, cvoff + 32 * c * (int)(K / 2), (ks0 + step) * 32);
       }
-      dma4(sr, cs + SCALES + 256 * w, svoff, step * 4);
+      dma4(sr, cs + SCALES + 256 * w, svoff, (ks0 + step) * 4);
     }
   };
 
@@ -500,15 +504,16 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
   {  // last weight step (stage 1); the LoRA step's A tile (U) goes to stage 2,
      // last read two steps ago (before the barrier of the previous step)
     mma_step(step, S1{}, F_{}, F_{});
-    if (a.r > 0) {
+    if (a.r > 0 && sp == a.nsplit - 1) {
       uint4 ar[8];
       load_a_rank(ar, S.U, a.r, M, m0, t);
       store_a<true>(A_of(2), ar, t);
       __syncthreads();
     }
   }
-  // LoRA step: [U | 0] [s B | 0]^T (none with r = 0: the adapter is off)
-  if (a.r > 0) {
+  // LoRA step: [U | 0] [s B | 0]^T (none with r = 0: the adapter is off;
+  // with a split reduction, in the last split only)
+  if (a.r > 0 && sp == a.nsplit - 1) {
     uint4 lb[NTW][4];
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
@@ -548,6 +553,10 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
         if (n >= N) continue;
         const int64_t o = m * S.ldo + S.col0 + n;
         float f[4] = {acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]};
+        if (a.nsplit > 1) {  // float32 partial of this split ([M x N], ldo == N); the sum kernel finishes
+          *(float4*)(a.partial + (int64_t)sp * M * N + o) = make_float4(f[0], f[1], f[2], f[3]);
+          continue;
+        }
         if (S.resid) {
           const uint2 rv = *(const uint2*)(S.resid + o);
           f[0] += __builtin_bit_cast(float, rv.x << 16);
@@ -954,11 +963,12 @@ ql_status launch_fwd_tiles(const FwdArgs& a, bool wide, hipStream_t st) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
   const bool prof = profiling_on();
   if (prof) QL_TRY_PROF(profile_begin(&e0, &e1));
+  const int grid = total * a.nsplit;
   if (wide)
-    hipExtLaunchKernelGGL(k_gemm_fwd<64>, dim3(total), dim3(NT), fwd_lds<256>(), st, e0, e1, 0, a, tiles_m, total,
+    hipExtLaunchKernelGGL(k_gemm_fwd<64>, dim3(grid), dim3(NT), fwd_lds<256>(), st, e0, e1, 0, a, tiles_m, total,
                           s1, s2);
   else
-    hipExtLaunchKernelGGL(k_gemm_fwd<32>, dim3(total), dim3(NT), fwd_lds<128>(), st, e0, e1, 0, a, tiles_m, total,
+    hipExtLaunchKernelGGL(k_gemm_fwd<32>, dim3(grid), dim3(NT), fwd_lds<128>(), st, e0, e1, 0, a, tiles_m, total,
                           s1, s2);
   QL_HIP_CHECK(hipGetLastError());
   if (prof) {
@@ -982,6 +992,35 @@ FwdSeg seg_from(const FwdSeg& S, int64_t c, int64_t K, int r) {
 
 }  // namespace
 
+// Sum of the split partials in split order, plus the residual, rounded once
+// (the same float32 operations as the unsplit epilogue: acc + resid).
+__global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ p, int nsplit, int64_t MK,
+                                                   const uint16_t* __restrict__ resid, void* __restrict__ out,
+                                                   int out_f32) {
+  const int64_t n4 = MK / 4, stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n4; g += stride) {
+    float4 f = ((const float4*)p)[g];
+    for (int s = 1; s < nsplit; ++s) {
+      const float4 q = ((const float4*)(p + (int64_t)s * MK))[g];
+      f.x += q.x;
+      f.y += q.y;
+      f.z += q.z;
+      f.w += q.w;
+    }
+    if (resid) {
+      const uint2 rv = ((const uint2*)resid)[g];
+      f.x += __builtin_bit_cast(float, rv.x << 16);
+      f.y += __builtin_bit_cast(float, rv.x & 0xffff0000u);
+      f.z += __builtin_bit_cast(float, rv.y << 16);
+      f.w += __builtin_bit_cast(float, rv.y & 0xffff0000u);
+    }
+    if (out_f32)
+      ((float4*)out)[g] = f;
+    else
+      ((uint2*)out)[g] = make_uint2(pack_bf16x2(f.x, f.y), pack_bf16x2(f.z, f.w));
+  }
+}
+
 // Launch geometry. Tiles are 256 x 256 (wide) or 256 x 128 (narrow); the chip
 // runs cu_count workgroups per round. A narrow tile does half a wide tile's
 // work but runs at a lower rate: it takes about kNarrowFwd (kNarrowBwd for dX)
@@ -999,15 +1038,41 @@ int narrow_pays(int t, int tn, int C, double ratio) {
   const int wide_rounds = (t + C - 1) / C, narrow_rounds = (tn + C - 1) / C;
   return ratio * narrow_rounds < (double)wide_rounds ? 1 : 0;
 }
-ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st) {
-  if (a.M == 0) return QL_OK;
+ql_status launch_gemm_fwd(const FwdArgs& a_in, hipStream_t st) {
+  if (a_in.M == 0) return QL_OK;
   QL_TRY_PROF(ensure_attrs());
+  FwdArgs a = a_in;
+  a.nsplit = 1;
   const int tiles_m = (int)((a.M + BM - 1) / BM);
   const int C = cu_count();
   int t256 = 0, t128 = 0;
   for (int s = 0; s < a.nseg; ++s) {
     t256 += tiles_m * (int)((a.seg[s].N + 255) / 256);
     t128 += tiles_m * (int)((a.seg[s].N + 127) / 128);
+  }
+  // split reduction (the dX GEMM's rule): one plain segment writing a
+  // contiguous [M x N] bf16 output, wide tiles that would leave half the chip
+  // idle, at least 64 K-steps per split
+  const FwdSeg& s0 = a.seg[0];
+  if (a.partial && a.nseg == 1 && a.n_rep == 0 && !a.out_f32 && s0.col0 == 0 && s0.ldo == s0.N &&
+      2 * t256 <= C) {
+    int S = C / t256;
+    const int cap = bwd_max_split(a.M, s0.N);
+    if (S > cap) S = cap;
+    const int kt = (int)(a.K / BK);
+    while (S > 1 && kt < 64 * S) --S;
+    while (S > 1 && (size_t)S * (size_t)a.M * (size_t)s0.N * 4 > a.partial_bytes) --S;
+    if (S > 1) {
+      a.nsplit = S;
+      QL_TRY_PROF(launch_fwd_tiles(a, true, st));
+      const int64_t MN = a.M * s0.N;
+      int64_t grid = (MN / 4 + 255) / 256;
+      if (grid > 4096) grid = 4096;
+      hipLaunchKernelGGL(k_split_sum, dim3((unsigned)grid), dim3(256), 0, st, (const float*)a.partial, S, MN,
+                         s0.resid, (void*)s0.out, 0);
+      QL_HIP_CHECK(hipGetLastError());
+      return QL_OK;
+    }
   }
   if (t256 <= C) return launch_fwd_tiles(a, narrow_pays(t256, t128, C, kNarrowFwd) == 0, st);
   const int full = (t256 / C) * C;
@@ -1070,35 +1135,6 @@ ql_status launch_bwd_tiles(const BwdArgs& a, bool wide, int64_t k_base, int64_t 
 }
 
 }  // namespace
-
-// Sum of the split partials in split order, plus the residual, rounded once
-// (the same float32 operations as the unsplit epilogue: acc + resid).
-__global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ p, int nsplit, int64_t MK,
-                                                   const uint16_t* __restrict__ resid, void* __restrict__ out,
-                                                   int out_f32) {
-  const int64_t n4 = MK / 4, stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n4; g += stride) {
-    float4 f = ((const float4*)p)[g];
-    for (int s = 1; s < nsplit; ++s) {
-      const float4 q = ((const float4*)(p + (int64_t)s * MK))[g];
-      f.x += q.x;
-      f.y += q.y;
-      f.z += q.z;
-      f.w += q.w;
-    }
-    if (resid) {
-      const uint2 rv = ((const uint2*)resid)[g];
-      f.x += __builtin_bit_cast(float, rv.x << 16);
-      f.y += __builtin_bit_cast(float, rv.x & 0xffff0000u);
-      f.z += __builtin_bit_cast(float, rv.y << 16);
-      f.w += __builtin_bit_cast(float, rv.y & 0xffff0000u);
-    }
-    if (out_f32)
-      ((float4*)out)[g] = f;
-    else
-      ((uint2*)out)[g] = make_uint2(pack_bf16x2(f.x, f.y), pack_bf16x2(f.z, f.w));
-  }
-}
 
 int bwd_max_split(int64_t M, int64_t K) {
   const int64_t t256 = ((M + BM - 1) / BM) * ((K + 255) / 256);

@@ -108,6 +108,13 @@ struct FwdArgs {
   int32_t out_f32;
   int32_t nseg;
   FwdSeg seg[kMaxSegs];
+  // Split reduction over K (set by launch_gemm_fwd; one segment, no column
+  // remap, contiguous [M x N] output): nsplit > 1 workgroups per tile write
+  // float32 partials [nsplit][M x N] that a second kernel sums in split
+  // order with the residual. partial / partial_bytes: the caller's space.
+  float* partial;
+  size_t partial_bytes;
+  int32_t nsplit;
 };
 
 // Reduction segment of the dX GEMM: dX += dY_s W_s + s G_s A_s.
