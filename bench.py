@@ -277,6 +277,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-resident", action="store_true")
+    ap.add_argument("--main-only", action="store_true",
+                    help="time only the headline step (no ring8 / reference / recompute / double-quant / "
+                         "small-stack / dense-GEMM lines), e.g. for counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -402,83 +405,85 @@ def main():
                 same_session_h2d_GBs=round(h2d_ceiling, 2), bytes_per_step=h2d_bytes,
                 copies_per_step=copies, record_bytes=rec)
 
-    # the same step with a deeper slot ring (the docs' stream_buffers up to 8):
-    # each turnaround reuses 8 layers, so 2 (L - 8) copies per step
-    log(f"bench: 8-slot ring, {args.steps} streamed steps")
-    cfg8 = ql.StackCfg(**{**cfg.__dict__, "n_buffers": 8})
-    slots8 = torch.empty(ql.stream_layer_stack_workspace(cfg8, M)[0], dtype=torch.uint8, device=dev)
-    slots_main = slots
-    slots = slots8
-    t8, _, _ = timed(cfg8, store, args.steps, args.warmup, False)
-    slots = slots_main
-    del slots8
-    ms8 = 1000.0 * t8 / args.steps
-    ring8 = dict(n_buffers=8, value=round(M * args.steps / t8, 1), unit="tok/s", ms_per_step=round(ms8, 3),
-                 copies_per_step=2 * (w["L"] - 8), pcie_GBs=round(2 * (w["L"] - 8) * rec / (ms8 * 1e-3) / 1e9, 2))
+    ring8 = with_ref = recompute = double_quant = small = dense = None
+    if not args.main_only:
+        # the same step with a deeper slot ring (the docs' stream_buffers up to 8):
+        # each turnaround reuses 8 layers, so 2 (L - 8) copies per step
+        log(f"bench: 8-slot ring, {args.steps} streamed steps")
+        cfg8 = ql.StackCfg(**{**cfg.__dict__, "n_buffers": 8})
+        slots8 = torch.empty(ql.stream_layer_stack_workspace(cfg8, M)[0], dtype=torch.uint8, device=dev)
+        slots_main = slots
+        slots = slots8
+        t8, _, _ = timed(cfg8, store, args.steps, args.warmup, False)
+        slots = slots_main
+        del slots8
+        ms8 = 1000.0 * t8 / args.steps
+        ring8 = dict(n_buffers=8, value=round(M * args.steps / t8, 1), unit="tok/s", ms_per_step=round(ms8, 3),
+                     copies_per_step=2 * (w["L"] - 8), pcie_GBs=round(2 * (w["L"] - 8) * rec / (ms8 * 1e-3) / 1e9, 2))
 
-    # preference-training step: policy + adapter-off reference forward in one
-    # pass over the streamed layers, then the backward (same copies per step)
-    log(f"bench: step with the reference forward, {args.steps} streamed steps")
-    _, per_layer = ql.stream_layer_stack_saved_layout(cfg, M)
-    ref_scratch = torch.empty(per_layer, dtype=torch.uint8, device=dev)
-    ref_y = torch.empty(M, w["H"], dtype=torch.bfloat16, device=dev)
+        # preference-training step: policy + adapter-off reference forward in one
+        # pass over the streamed layers, then the backward (same copies per step)
+        log(f"bench: step with the reference forward, {args.steps} streamed steps")
+        _, per_layer = ql.stream_layer_stack_saved_layout(cfg, M)
+        ref_scratch = torch.empty(per_layer, dtype=torch.uint8, device=dev)
+        ref_y = torch.empty(M, w["H"], dtype=torch.bfloat16, device=dev)
 
-    def pref_step(turnaround):
-        s1 = ql.stream_layer_stack_fwd_ref(cfg, store, lora, x, M, y, saved, ref_y, ref_scratch, slots, ws,
-                                           compute, copy, reuse_bwd_slots=int(turnaround))
-        s2 = ql.stream_layer_stack_bwd(cfg, store, lora, dy, M, saved, dx, dA, dB, 0, 1, slots, ws, compute, copy)
-        return max(s1, s2)
+        def pref_step(turnaround):
+            s1 = ql.stream_layer_stack_fwd_ref(cfg, store, lora, x, M, y, saved, ref_y, ref_scratch, slots, ws,
+                                               compute, copy, reuse_bwd_slots=int(turnaround))
+            s2 = ql.stream_layer_stack_bwd(cfg, store, lora, dy, M, saved, dx, dA, dB, 0, 1, slots, ws, compute, copy)
+            return max(s1, s2)
 
-    for i in range(args.warmup):
-        pref_step(i > 0)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        pref_step(True)
-    torch.cuda.synchronize()
-    tr = time.perf_counter() - t0
-    with_ref = dict(value=round(M * args.steps / tr, 1), unit="tok/s", ms_per_step=round(1000 * tr / args.steps, 3),
-                    copies_per_step=copies, note="policy + adapter-off reference forward share each layer copy")
-    del ref_scratch, ref_y
+        for i in range(args.warmup):
+            pref_step(i > 0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            pref_step(True)
+        torch.cuda.synchronize()
+        tr = time.perf_counter() - t0
+        with_ref = dict(value=round(M * args.steps / tr, 1), unit="tok/s", ms_per_step=round(1000 * tr / args.steps, 3),
+                        copies_per_step=copies, note="policy + adapter-off reference forward share each layer copy")
+        del ref_scratch, ref_y
 
-    # the same streamed step with per-layer recomputation (gradient
-    # checkpointing): the forward keeps only layer inputs, the backward
-    # recomputes each layer from its slot
-    log(f"bench: recompute mode, {args.steps} streamed steps")
-    cfg_rc = ql.StackCfg(**{**cfg.__dict__, "recompute": 1})
-    _, saved_rc_b, ws_rc_b = ql.stream_layer_stack_workspace(cfg_rc, M)
-    saved_main, ws_main = saved, ws
-    saved = torch.empty(saved_rc_b, dtype=torch.uint8, device=dev)
-    ws = torch.empty(ws_rc_b, dtype=torch.uint8, device=dev)
-    trc, _, _ = timed(cfg_rc, store, args.steps, args.warmup, False)
-    saved, ws = saved_main, ws_main
-    recompute = dict(value=round(M * args.steps / trc, 1), unit="tok/s", ms_per_step=round(1000 * trc / args.steps, 3),
-                     saved_bytes=int(saved_rc_b), saved_bytes_without=int(saved.numel()),
-                     ws_bytes=int(ws_rc_b), ws_bytes_without=int(ws.numel()))
+        # the same streamed step with per-layer recomputation (gradient
+        # checkpointing): the forward keeps only layer inputs, the backward
+        # recomputes each layer from its slot
+        log(f"bench: recompute mode, {args.steps} streamed steps")
+        cfg_rc = ql.StackCfg(**{**cfg.__dict__, "recompute": 1})
+        _, saved_rc_b, ws_rc_b = ql.stream_layer_stack_workspace(cfg_rc, M)
+        saved_main, ws_main = saved, ws
+        saved = torch.empty(saved_rc_b, dtype=torch.uint8, device=dev)
+        ws = torch.empty(ws_rc_b, dtype=torch.uint8, device=dev)
+        trc, _, _ = timed(cfg_rc, store, args.steps, args.warmup, False)
+        saved, ws = saved_main, ws_main
+        recompute = dict(value=round(M * args.steps / trc, 1), unit="tok/s", ms_per_step=round(1000 * trc / args.steps, 3),
+                         saved_bytes=int(saved_rc_b), saved_bytes_without=int(saved.numel()),
+                         ws_bytes=int(ws_rc_b), ws_bytes_without=int(ws.numel()))
 
-    # the same streamed step from a store with double-quantised scales (the
-    # pages' 3.60 GB form): 8% fewer bytes per layer copy
-    log("bench: double-quantised store")
-    cfg_dq, dq_store = build_dq_store(ql, torch, cfg, store, dev)
-    rec_dq = ql.stream_layer_stack_layout(cfg_dq)[0][1]
-    slots_dq_b, _, ws_dq_b = ql.stream_layer_stack_workspace(cfg_dq, M)
-    slots_main, ws_main = slots, ws
-    slots = torch.empty(slots_dq_b, dtype=torch.uint8, device=dev)
-    ws = torch.empty(ws_dq_b, dtype=torch.uint8, device=dev)
-    log(f"bench: double-quantised store, {args.steps} streamed steps")
-    tdq, status_dq, _ = timed(cfg_dq, dq_store, args.steps, args.warmup, False)
-    slots, ws = slots_main, ws_main
-    msdq = 1000.0 * tdq / args.steps
-    double_quant = dict(value=round(M * args.steps / tdq, 1), unit="tok/s", ms_per_step=round(msdq, 3),
-                        store_bytes=int(dq_store.numel()), record_bytes=int(rec_dq), copies_per_step=copies,
-                        pcie_GBs=round(copies * rec_dq / (msdq * 1e-3) / 1e9, 2), status=int(status_dq))
-    del dq_store
+        # the same streamed step from a store with double-quantised scales (the
+        # pages' 3.60 GB form): 8% fewer bytes per layer copy
+        log("bench: double-quantised store")
+        cfg_dq, dq_store = build_dq_store(ql, torch, cfg, store, dev)
+        rec_dq = ql.stream_layer_stack_layout(cfg_dq)[0][1]
+        slots_dq_b, _, ws_dq_b = ql.stream_layer_stack_workspace(cfg_dq, M)
+        slots_main, ws_main = slots, ws
+        slots = torch.empty(slots_dq_b, dtype=torch.uint8, device=dev)
+        ws = torch.empty(ws_dq_b, dtype=torch.uint8, device=dev)
+        log(f"bench: double-quantised store, {args.steps} streamed steps")
+        tdq, status_dq, _ = timed(cfg_dq, dq_store, args.steps, args.warmup, False)
+        slots, ws = slots_main, ws_main
+        msdq = 1000.0 * tdq / args.steps
+        double_quant = dict(value=round(M * args.steps / tdq, 1), unit="tok/s", ms_per_step=round(msdq, 3),
+                            store_bytes=int(dq_store.numel()), record_bytes=int(rec_dq), copies_per_step=copies,
+                            pcie_GBs=round(copies * rec_dq / (msdq * 1e-3) / 1e9, 2), status=int(status_dq))
+        del dq_store
 
-    log("bench: SmolLM2-shaped stack, eager and captured steps")
-    small = small_stack_graph(ql, synth, torch, dev)
+        log("bench: SmolLM2-shaped stack, eager and captured steps")
+        small = small_stack_graph(ql, synth, torch, dev)
 
-    dense = dense_gemm_ceiling(torch, dev, M, w)
-    gemm_all["vs_dense_bf16"] = round(gemm_all["tflops"] / dense["tflops"], 4)
+        dense = dense_gemm_ceiling(torch, dev, M, w)
+        gemm_all["vs_dense_bf16"] = round(gemm_all["tflops"] / dense["tflops"], 4)
 
     resident = None
     if not args.no_resident:
