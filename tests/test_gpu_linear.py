@@ -119,6 +119,39 @@ def test_exact_construction_bitwise():
     close(f64(got["dB"]), want["dB"], tol=1e-6, what="exact:dB")
 
 
+@pytest.mark.parametrize("M,K,N", [(256, 14336, 4096), (256, 4096, 14336)])
+def test_exact_construction_bitwise_split_reductions(M, K, N):
+    # Shapes whose GEMMs split the reduction across workgroups (the forward
+    # over K = 14336, the dX over N = 14336: three splits each at M = 256)
+    # and sum float32 partials in a second pass. With operands in {-1, 0, 1},
+    # at most 8192 non-zeros per row and absmax 1, every float32 partial sum is
+    # exact in any order, so y and dX must equal the exact result rounded once.
+    require_gpu()
+    r, alpha = 4, 8.0
+    g = np.random.default_rng(M + K + N)
+    codes = g.integers(0, 16, size=(N, K)).astype(np.uint8)
+    packed = torch.from_numpy(onf4.pack(codes.reshape(-1)))
+    absmax = torch.ones(N * K // 64, dtype=torch.float32)
+
+    def sparse_pm1(rows, cols):
+        v = g.integers(-1, 2, size=(rows, cols)).astype(np.float64)
+        for i in range(rows):   # at most 8192 non-zeros per row
+            nz = np.flatnonzero(v[i])
+            if nz.size > 8192:
+                v[i, g.choice(nz, nz.size - 8192, replace=False)] = 0.0
+        return v
+
+    x = sparse_pm1(M, K)
+    dy = sparse_pm1(M, N)
+    A = np.zeros((r, K)); A[np.arange(r), g.integers(0, K, size=r)] = 2.0 ** -4
+    B = np.zeros((N, r)); B[np.arange(N), g.integers(0, r, size=N)] = 2.0 ** -3
+    c = Case(M, K, N, r, alpha, ("exact-split", M, K, N), x=_bf16(x), packed=packed, absmax=absmax, A=_bf16(A),
+             B=_bf16(B), dy=_bf16(dy))
+    got, want = c.run(), c.oracle()
+    assert np.array_equal(bf16_bits_t(got["y"]), onf4.bf16_bits(want["y"]))
+    assert np.array_equal(bf16_bits_t(got["dx"]), onf4.bf16_bits(want["dx"]))
+
+
 def test_one_hot_rows_read_weight_columns():
     # x rows one-hot, B = 0: each y row is a column of the bf16 dequantised W
     # (isolates the fused loader's decode), bitwise.
