@@ -25,12 +25,6 @@ static void clear_error() { g_err[0] = 0; }
 
 static inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-#define QL_TRY(expr)                 \
-  do {                               \
-    ql_status rc_ = (expr);          \
-    if (rc_ != QL_OK) return rc_;    \
-  } while (0)
-
 // ------------------------------------------------------------ small helpers
 static ql_status check_ptr(const char* fn, const char* name, const void* p, size_t align) {
   if (!p) return set_error(QL_ERR_ARG, "%s: %s is NULL", fn, name);
@@ -82,15 +76,14 @@ struct LinearWs {
 
 static LinearWs linear_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   LinearWs w;
-  w.fpartial_off = align256(skinny_ws_bytes(M, K, r, 1));
+  w.fpartial_off = align256(rowc_ws_bytes(M, K, r));
   w.fwd = w.fpartial_off + align256(bwd_partial_bytes(M, N));
   w.bt_off = 0;
   w.g_off = align256((size_t)r * N * 2);
   w.scratch_off = w.g_off + align256((size_t)M * r * 2);
-  size_t scratch = skinny_ws_bytes(M, N, r, 1);
-  size_t c1 = colred_ws_bytes(M, N, r), c2 = colred_ws_bytes(M, K, r);
-  if (c1 > scratch) scratch = c1;
-  if (c2 > scratch) scratch = c2;
+  size_t scratch = rowc_ws_bytes(M, N, r);
+  const size_t c = colc_ws_bytes(M, N, r) + colc_ws_bytes(M, K, r);  // dB and dA in one launch
+  if (c > scratch) scratch = c;
   w.partial_off = w.scratch_off + align256(scratch);
   w.bwd = w.partial_off + align256(bwd_partial_bytes(M, K));
   return w;
@@ -185,7 +178,8 @@ static SavedLayout saved_layout(const ql_stack_cfg* c, int64_t M) {
 // internal temporaries of the stack (offsets into ws); with recompute also one
 // layer of activations (ck, full layout) and the recomputed layer output
 struct StackWs {
-  size_t dhA, dhB, dhmid, dact, dg, du, dn, da32, dv, bt, G[5], scratch, ck, ck_out, partial, partial_bytes;
+  size_t dhA, dhB, dhmid, dact, dg, du, dn, da32, dv, bt, G[5], scratch, scratch_bytes, ck, ck_out, partial,
+      partial_bytes;
   size_t absx[QL_NPROJ];  // absmax_dq: the layer's expanded float32 scales
   size_t total;
 };
@@ -208,17 +202,21 @@ static StackWs stack_ws(const ql_stack_cfg* c, int64_t M) {
   w.dn = take(M * H * 2);
   w.da32 = take(M * H * 4);
   w.dv = take(M * KV * 2);
-  const int64_t maxN = H > I ? H : I;
-  w.bt = take((size_t)r * maxN * 2);
+  // transposed B of down, gate, up, o, v (in that order)
+  w.bt = take((size_t)r * (H + I + I + H + KV) * 2 + 5 * 256);
   for (int i = 0; i < 5; ++i) w.G[i] = take((size_t)M * r * 2);
   size_t sc = 0;
   auto mx = [&](size_t v) { if (v > sc) sc = v; };
-  mx(skinny_ws_bytes(M, H, r, 3));
-  mx(skinny_ws_bytes(M, I, r, 1));
-  mx(colred_ws_bytes(M, H, r));
-  mx(colred_ws_bytes(M, I, r));
-  mx(colred_ws_bytes(M, KV, r));
+  mx(rowc_ws_bytes(M, H, 3 * r));                            // U of q | k | v
+  mx(rowc_ws_bytes(M, H, 2 * r));                            // U of gate | up
+  mx(rowc_ws_bytes(M, I, r));                                // U of down
+  mx(rowc_ws_bytes(M, H, r));                                // U of o; G of down, o
+  mx(2 * rowc_ws_bytes(M, I, r));                            // G of gate and up
+  mx(rowc_ws_bytes(M, KV, r));                               // G of v
+  mx(colc_ws_bytes(M, H, r) * 5 + colc_ws_bytes(M, I, r) * 3 + colc_ws_bytes(M, H, 2 * r) +
+     colc_ws_bytes(M, KV, r));                               // all adapter gradients of a layer
   w.scratch = take(sc);
+  w.scratch_bytes = sc;
   // float32 partials of the split dX GEMMs (outputs of I or H columns)
   w.partial_bytes = bwd_partial_bytes(M, I) > bwd_partial_bytes(M, H) ? bwd_partial_bytes(M, I)
                                                                       : bwd_partial_bytes(M, H);
@@ -297,10 +295,12 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
 
   QL_TRY(launch_rmsnorm_fwd(h_in, M, H, c->rms_eps, S(QL_SAVED_N1), st));
   if (on) {  // LoRA down of q, k, v (they share n1)
-    SkinnyArgs a{};
+    RowArgs ra{};
+    ra.nprob = 1;
+    RowProb& a = ra.p[0];
     a.X = S(QL_SAVED_N1); a.M = M; a.K = H; a.ldx = H; a.r = r; a.nseg = 3;
     for (int p = 0; p < 3; ++p) { a.Bt[p] = u16(lo[p].A); a.out[p] = S(QL_SAVED_U0 + p); }
-    QL_TRY(launch_skinny(a, scratch, st));
+    QL_TRY(launch_rowc(ra, scratch, WS.scratch_bytes, st));
   }
   {  // q | k | v in one launch
     FwdArgs a{};
@@ -316,11 +316,13 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
   }
   const int n_rep = (int)(H / KV);
   {  // o: input a = repeat_kv(v) read through the column remap; residual h_in
-    SkinnyArgs u{};
-    u.X = S(QL_SAVED_V); u.M = M; u.K = H; u.ldx = KV; u.head_dim = c->head_dim; u.n_rep = n_rep;
     if (on) {
+      RowArgs ra{};
+      ra.nprob = 1;
+      RowProb& u = ra.p[0];
+      u.X = S(QL_SAVED_V); u.M = M; u.K = H; u.ldx = KV; u.head_dim = c->head_dim; u.n_rep = n_rep;
       u.r = r; u.nseg = 1; u.Bt[0] = u16(lo[QL_PROJ_O].A); u.out[0] = S(QL_SAVED_U0 + QL_PROJ_O);
-      QL_TRY(launch_skinny(u, scratch, st));
+      QL_TRY(launch_rowc(ra, scratch, WS.scratch_bytes, st));
     }
     FwdArgs a{};
     a.X = S(QL_SAVED_V); a.M = M; a.K = H; a.ldx = KV; a.head_dim = c->head_dim; a.n_rep = n_rep;
@@ -333,12 +335,14 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
   }
   QL_TRY(launch_rmsnorm_fwd(S(QL_SAVED_H_MID), M, H, c->rms_eps, S(QL_SAVED_N2), st));
   {  // gate | up
-    SkinnyArgs u{};
     if (on) {
+      RowArgs ra{};
+      ra.nprob = 1;
+      RowProb& u = ra.p[0];
       u.X = S(QL_SAVED_N2); u.M = M; u.K = H; u.ldx = H; u.r = r; u.nseg = 2;
       u.Bt[0] = u16(lo[QL_PROJ_GATE].A); u.out[0] = S(QL_SAVED_U0 + QL_PROJ_GATE);
       u.Bt[1] = u16(lo[QL_PROJ_UP].A); u.out[1] = S(QL_SAVED_U0 + QL_PROJ_UP);
-      QL_TRY(launch_skinny(u, scratch, st));
+      QL_TRY(launch_rowc(ra, scratch, WS.scratch_bytes, st));
     }
     FwdArgs a{};
     a.X = S(QL_SAVED_N2); a.M = M; a.K = H; a.ldx = H; a.r = r; a.s = s; a.nseg = 2;
@@ -354,11 +358,13 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
   }
   QL_TRY(launch_swiglu_fwd(S(QL_SAVED_GATE), S(QL_SAVED_UP), M * I, S(QL_SAVED_ACT), st));
   {  // down, residual h_mid
-    SkinnyArgs u{};
     if (on) {
+      RowArgs ra{};
+      ra.nprob = 1;
+      RowProb& u = ra.p[0];
       u.X = S(QL_SAVED_ACT); u.M = M; u.K = I; u.ldx = I; u.r = r; u.nseg = 1;
       u.Bt[0] = u16(lo[QL_PROJ_DOWN].A); u.out[0] = S(QL_SAVED_U0 + QL_PROJ_DOWN);
-      QL_TRY(launch_skinny(u, scratch, st));
+      QL_TRY(launch_rowc(ra, scratch, WS.scratch_bytes, st));
     }
     FwdArgs a{};
     a.X = S(QL_SAVED_ACT); a.M = M; a.K = I; a.ldx = I; a.r = r; a.s = s; a.nseg = 1;
@@ -373,28 +379,35 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
   return QL_OK;
 }
 
-// G = bf16(dY B) for one projection (B [N x r] transposed into ws first)
-static ql_status lora_g(const uint16_t* dy, int64_t M, int64_t N, const ql_lora& lo, int r,
-                        uint16_t* bt, uint16_t* G, void* scratch, hipStream_t st) {
-  QL_TRY(launch_transpose_bf16(u16(lo.B), N, r, bt, st));
-  SkinnyArgs a{};
+// One row-contraction problem: G = bf16(dY Bt^T) (Bt: B transposed, [r x N])
+static RowProb g_prob(const uint16_t* dy, int64_t M, int64_t N, int r, const uint16_t* bt, uint16_t* G) {
+  RowProb a{};
   a.X = dy; a.M = M; a.K = N; a.ldx = N; a.r = r; a.nseg = 1; a.Bt[0] = bt; a.out[0] = G;
-  return launch_skinny(a, scratch, st);
+  return a;
 }
 
-// dB = s dY^T U (transposed store into [N x r]) and dA = s G^T X
-static ql_status lora_grads(const uint16_t* dy, int64_t N, const uint16_t* U, const uint16_t* X,
-                            int64_t ldx, int head_dim, int n_rep, int64_t K, const uint16_t* G,
-                            int64_t M, int r, float s, float* dA, float* dB, int accumulate,
-                            void* scratch, hipStream_t st) {
-  ColRedArgs b{};
-  b.Z = dy; b.M = M; b.C = N; b.ldz = N; b.V = U; b.r = r; b.s = s; b.out = dB;
+// Column-contraction problems of one projection: dB = s dY^T U, stored
+// transposed into [N x r], and dA = s G^T X (X columns remapped by repeat_kv
+// when n_rep > 0)
+static ColProb db_prob(const uint16_t* dy, int64_t M, int64_t N, const uint16_t* U, int r, float s, float* dB,
+                       int accumulate) {
+  ColProb b{};
+  b.Z = dy; b.M = M; b.C = N; b.ldz = N; b.r = r; b.nseg = 1; b.V[0] = U; b.out[0] = dB; b.s = s;
   b.transpose_out = 1; b.accumulate = accumulate;
-  QL_TRY(launch_colred(b, scratch, st));
-  ColRedArgs a{};
-  a.Z = X; a.M = M; a.C = K; a.ldz = ldx; a.head_dim = head_dim; a.n_rep = n_rep; a.V = G; a.r = r;
-  a.s = s; a.out = dA; a.transpose_out = 0; a.accumulate = accumulate;
-  return launch_colred(a, scratch, st);
+  return b;
+}
+static ColProb da_prob(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, int head_dim, int n_rep,
+                       const uint16_t* G, int r, float s, float* dA, int accumulate) {
+  ColProb a{};
+  a.Z = X; a.M = M; a.C = K; a.ldz = ldx; a.head_dim = head_dim; a.n_rep = n_rep; a.r = r; a.nseg = 1;
+  a.V[0] = G; a.out[0] = dA; a.s = s; a.transpose_out = 0; a.accumulate = accumulate;
+  return a;
+}
+// zero output of a gradient that is exactly zero ([rows x cols] float32)
+static ColProb zero_prob(float* out, int64_t n, int r) {
+  ColProb z{};
+  z.M = 0; z.C = n / r; z.r = r; z.nseg = 1; z.out[0] = out; z.accumulate = 0;
+  return z;
 }
 
 static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const LayerW& W,
@@ -407,12 +420,36 @@ static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const L
   auto S = [&](int i) { return (const uint16_t*)(sv + SV.off[i]); };
   auto T = [&](size_t off) { return (uint16_t*)(ws + off); };
   void* scratch = ws + WS.scratch;
-  uint16_t* bt = T(WS.bt);
   const int n_rep = (int)(H / KV);
+
+  // B of down, gate, up, o, v transposed to [r x N] in one launch
+  const int tp[5] = {QL_PROJ_DOWN, QL_PROJ_GATE, QL_PROJ_UP, QL_PROJ_O, QL_PROJ_V};
+  uint16_t* bt[5];
+  {
+    TransArgs ta{};
+    ta.n = 5;
+    size_t off = WS.bt;
+    for (int i = 0; i < 5; ++i) {
+      const int64_t N = SL.N[tp[i]];
+      bt[i] = T(off);
+      off += align256((size_t)r * N * 2);
+      ta.in[i] = u16(lo[tp[i]].B); ta.out[i] = bt[i]; ta.rows[i] = N; ta.cols[i] = r;
+    }
+    QL_TRY(launch_transpose_bf16(ta, st));
+  }
+  auto row1 = [&](const RowProb& p) {
+    RowArgs ra{};
+    ra.nprob = 1;
+    ra.p[0] = p;
+    return launch_rowc(ra, scratch, WS.scratch_bytes, st);
+  };
+  // the adapter gradients of the layer, one launch at the end
+  ColArgs grads{};
+  auto add = [&](const ColProb& p) { grads.p[grads.nprob++] = p; };
 
   // down: dact = dh W_d + s G_d A_d
   uint16_t* Gd = T(WS.G[0]);
-  QL_TRY(lora_g(dh, M, H, lo[QL_PROJ_DOWN], r, bt, Gd, scratch, st));
+  QL_TRY(row1(g_prob(dh, M, H, r, bt[0], Gd)));
   {
     BwdArgs a{};
     a.M = M; a.K = I; a.r = r; a.s = s; a.out = T(WS.dact); a.nseg = 1;
@@ -420,15 +457,20 @@ static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     a.partial = (float*)(ws + WS.partial); a.partial_bytes = WS.partial_bytes;
     QL_TRY(launch_gemm_bwd(a, st));
   }
-  QL_TRY(lora_grads(dh, H, S(QL_SAVED_U0 + QL_PROJ_DOWN), S(QL_SAVED_ACT), I, 0, 0, I, Gd, M, r, s,
-                    dA[QL_PROJ_DOWN], dB[QL_PROJ_DOWN], accumulate, scratch, st));
+  add(db_prob(dh, M, H, S(QL_SAVED_U0 + QL_PROJ_DOWN), r, s, dB[QL_PROJ_DOWN], accumulate));
+  add(da_prob(S(QL_SAVED_ACT), M, I, I, 0, 0, Gd, r, s, dA[QL_PROJ_DOWN], accumulate));
   // SwiGLU
   QL_TRY(launch_swiglu_bwd(S(QL_SAVED_GATE), S(QL_SAVED_UP), T(WS.dact), M * I, T(WS.dg), T(WS.du), st));
   // gate + up: dn2 = dg W_g + s G_g A_g + du W_u + s G_u A_u
   uint16_t* Gg = T(WS.G[1]);
   uint16_t* Gu = T(WS.G[2]);
-  QL_TRY(lora_g(T(WS.dg), M, I, lo[QL_PROJ_GATE], r, bt, Gg, scratch, st));
-  QL_TRY(lora_g(T(WS.du), M, I, lo[QL_PROJ_UP], r, bt, Gu, scratch, st));
+  {
+    RowArgs ra{};
+    ra.nprob = 2;
+    ra.p[0] = g_prob(T(WS.dg), M, I, r, bt[1], Gg);
+    ra.p[1] = g_prob(T(WS.du), M, I, r, bt[2], Gu);
+    QL_TRY(launch_rowc(ra, scratch, WS.scratch_bytes, st));
+  }
   {
     BwdArgs a{};
     a.M = M; a.K = H; a.r = r; a.s = s; a.out = T(WS.dn); a.nseg = 2;
@@ -437,16 +479,19 @@ static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     a.partial = (float*)(ws + WS.partial); a.partial_bytes = WS.partial_bytes;
     QL_TRY(launch_gemm_bwd(a, st));
   }
-  QL_TRY(lora_grads(T(WS.dg), I, S(QL_SAVED_U0 + QL_PROJ_GATE), S(QL_SAVED_N2), H, 0, 0, H, Gg, M, r, s,
-                    dA[QL_PROJ_GATE], dB[QL_PROJ_GATE], accumulate, scratch, st));
-  QL_TRY(lora_grads(T(WS.du), I, S(QL_SAVED_U0 + QL_PROJ_UP), S(QL_SAVED_N2), H, 0, 0, H, Gu, M, r, s,
-                    dA[QL_PROJ_UP], dB[QL_PROJ_UP], accumulate, scratch, st));
+  add(db_prob(T(WS.dg), M, I, S(QL_SAVED_U0 + QL_PROJ_GATE), r, s, dB[QL_PROJ_GATE], accumulate));
+  add(db_prob(T(WS.du), M, I, S(QL_SAVED_U0 + QL_PROJ_UP), r, s, dB[QL_PROJ_UP], accumulate));
+  {  // dA of gate and up share n2: one pass over it
+    ColProb a = da_prob(S(QL_SAVED_N2), M, H, H, 0, 0, Gg, r, s, dA[QL_PROJ_GATE], accumulate);
+    a.nseg = 2; a.V[1] = Gu; a.out[1] = dA[QL_PROJ_UP];
+    add(a);
+  }
   // RMSNorm 2 + residual
   QL_TRY(launch_rmsnorm_bwd(S(QL_SAVED_H_MID), T(WS.dn), dh, M, H, c->rms_eps, T(WS.dhmid), st));
   const uint16_t* dhm = T(WS.dhmid);
   // o: da = dh_mid W_o + s G_o A_o (float32), dv = head-group sum
   uint16_t* Go = T(WS.G[3]);
-  QL_TRY(lora_g(dhm, M, H, lo[QL_PROJ_O], r, bt, Go, scratch, st));
+  QL_TRY(row1(g_prob(dhm, M, H, r, bt[3], Go)));
   {
     BwdArgs a{};
     a.M = M; a.K = H; a.r = r; a.s = s; a.out = ws + WS.da32; a.out_f32 = 1; a.nseg = 1;
@@ -454,12 +499,12 @@ static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     a.partial = (float*)(ws + WS.partial); a.partial_bytes = WS.partial_bytes;
     QL_TRY(launch_gemm_bwd(a, st));
   }
-  QL_TRY(lora_grads(dhm, H, S(QL_SAVED_U0 + QL_PROJ_O), S(QL_SAVED_V), KV, c->head_dim, n_rep, H, Go, M,
-                    r, s, dA[QL_PROJ_O], dB[QL_PROJ_O], accumulate, scratch, st));
+  add(db_prob(dhm, M, H, S(QL_SAVED_U0 + QL_PROJ_O), r, s, dB[QL_PROJ_O], accumulate));
+  add(da_prob(S(QL_SAVED_V), M, H, KV, c->head_dim, n_rep, Go, r, s, dA[QL_PROJ_O], accumulate));
   QL_TRY(launch_repeat_kv_bwd((const float*)(ws + WS.da32), M, H, KV, c->head_dim, T(WS.dv), st));
   // v: dn1 = dv W_v + s G_v A_v
   uint16_t* Gv = T(WS.G[4]);
-  QL_TRY(lora_g(T(WS.dv), M, KV, lo[QL_PROJ_V], r, bt, Gv, scratch, st));
+  QL_TRY(row1(g_prob(T(WS.dv), M, KV, r, bt[4], Gv)));
   {
     BwdArgs a{};
     a.M = M; a.K = H; a.r = r; a.s = s; a.out = T(WS.dn); a.nseg = 1;
@@ -467,15 +512,16 @@ static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     a.partial = (float*)(ws + WS.partial); a.partial_bytes = WS.partial_bytes;
     QL_TRY(launch_gemm_bwd(a, st));
   }
-  QL_TRY(lora_grads(T(WS.dv), KV, S(QL_SAVED_U0 + QL_PROJ_V), S(QL_SAVED_N1), H, 0, 0, H, Gv, M, r, s,
-                    dA[QL_PROJ_V], dB[QL_PROJ_V], accumulate, scratch, st));
+  add(db_prob(T(WS.dv), M, KV, S(QL_SAVED_U0 + QL_PROJ_V), r, s, dB[QL_PROJ_V], accumulate));
+  add(da_prob(S(QL_SAVED_N1), M, H, H, 0, 0, Gv, r, s, dA[QL_PROJ_V], accumulate));
   // q, k feed nothing: their adapter gradients are exactly zero
   if (!accumulate) {
     for (int p = 0; p < 2; ++p) {
-      QL_TRY(launch_zero_f32(dA[p], (int64_t)r * H, st));
-      QL_TRY(launch_zero_f32(dB[p], SL.N[p] * r, st));
+      add(zero_prob(dA[p], (int64_t)r * H, r));
+      add(zero_prob(dB[p], SL.N[p] * r, r));
     }
   }
+  QL_TRY(launch_colc(grads, scratch, WS.scratch_bytes, st));
   // RMSNorm 1 + residual
   QL_TRY(launch_rmsnorm_bwd(S(QL_SAVED_H_IN), T(WS.dn), dhm, M, H, c->rms_eps, dh_out, st));
   return QL_OK;
@@ -810,10 +856,12 @@ ql_status qlora_linear_fwd(const void* x, int64_t M, ql_nf4_weight W, ql_lora L,
   if (ws_bytes < lw.fwd) return set_error(QL_ERR_WORKSPACE, "%s: ws_bytes (%zu) < %zu", fn, ws_bytes, lw.fwd);
   if (lw.fwd) QL_TRY(check_ptr(fn, "ws", ws, 16));
   hipStream_t st = (hipStream_t)s;
-  SkinnyArgs u{};
+  RowArgs ra{};
+  ra.nprob = 1;
+  RowProb& u = ra.p[0];
   u.X = u16(x); u.M = M; u.K = W.K; u.ldx = W.K; u.r = L.r; u.nseg = 1; u.Bt[0] = u16(L.A);
   u.out[0] = u16w(u_save);
-  QL_TRY(launch_skinny(u, ws, st));
+  QL_TRY(launch_rowc(ra, ws, lw.fpartial_off, st));
   FwdArgs a{};
   a.X = u16(x); a.M = M; a.K = W.K; a.ldx = W.K; a.r = L.r; a.s = L.alpha / (float)L.r; a.nseg = 1;
   FwdSeg& g = a.seg[0];
@@ -859,7 +907,16 @@ ql_status qlora_linear_bwd(const void* dy, const void* x, const void* u_saved, i
   uint16_t* bt = (uint16_t*)(w8 + lw.bt_off);
   uint16_t* G = (uint16_t*)(w8 + lw.g_off);
   void* scratch = w8 + lw.scratch_off;
-  QL_TRY(lora_g(u16(dy), M, W.N, L, L.r, bt, G, scratch, st));
+  const size_t scratch_bytes = lw.partial_off - lw.scratch_off;
+  {
+    TransArgs ta{};
+    ta.n = 1; ta.in[0] = u16(L.B); ta.out[0] = bt; ta.rows[0] = W.N; ta.cols[0] = L.r;
+    QL_TRY(launch_transpose_bf16(ta, st));
+    RowArgs ra{};
+    ra.nprob = 1;
+    ra.p[0] = g_prob(u16(dy), M, W.N, L.r, bt, G);
+    QL_TRY(launch_rowc(ra, scratch, scratch_bytes, st));
+  }
   if (dx) {
     BwdArgs a{};
     a.M = M; a.K = W.K; a.r = L.r; a.s = sc; a.out = dx; a.nseg = 1;
@@ -868,8 +925,11 @@ ql_status qlora_linear_bwd(const void* dy, const void* x, const void* u_saved, i
     a.partial_bytes = bwd_partial_bytes(M, W.K);
     QL_TRY(launch_gemm_bwd(a, st));
   }
-  return lora_grads(u16(dy), W.N, u16(u_saved), u16(x), W.K, 0, 0, W.K, G, M, L.r, sc, dA, dB, accumulate,
-                    scratch, st);
+  ColArgs grads{};
+  grads.nprob = 2;
+  grads.p[0] = db_prob(u16(dy), M, W.N, u16(u_saved), L.r, sc, dB, accumulate);
+  grads.p[1] = da_prob(u16(x), M, W.K, W.K, 0, 0, G, L.r, sc, dA, accumulate);
+  return launch_colc(grads, scratch, scratch_bytes, st);
 }
 
 ql_status stream_layer_stack_layout(const ql_stack_cfg* cfg, int64_t* layer_offsets, int64_t* proj_offsets,

@@ -1,214 +1,433 @@
 // LoRA side products of rank r (r <= 64): the skinny contractions around the
-// fused NF4 GEMMs. They are memory-bound (about r FLOP per byte read), so the
-// design goal is one coalesced pass over the large operand with a fixed
-// reduction order (no atomics): split the long dimension into chunks, write
-// float32 partial sums to a workspace, and sum the chunks in index order.
+// fused NF4 GEMMs. Only A and B train, and the adapter adds s (x A^T) B^T with
+// s = alpha / r (blog "How does Soup train an 8B model on a 4 GB GPU?").
 //
-//  skinny:  out[m][j] = bf16( sum_k X[m][k] Bt[j][k] )      U = x A^T, G = dY B
-//  colred:  out[j][c] = s * sum_m Z[m][c] V[m][j]           dA = s G^T x, dB = s dY^T U
+//  row:     out[m][j] = bf16( sum_k X[m][k] Bt[j][k] )      U = x A^T, G = dY B
+//  column:  out[j][c] = s * sum_m Z[m][c] V[m][j]           dA = s G^T x, dB = s dY^T U
 //
-// The adapter formula is the LoRA one (y = x W^T + s (x A^T) B^T, s = alpha/r);
-// only A and B train (blog "How does Soup train an 8B model on a 4 GB GPU?").
+// Each reads one large bf16 operand once and does 2 np FLOP per element of it
+// (np = r times the projections sharing the operand): bound by HBM. Both run
+// on MFMA 16x16x32 bf16, since float32 FMA alone would need np FLOP per byte
+// read, more than the vector ALUs sustain at the full HBM rate for np = 16.
+//
+// Row contraction: a workgroup owns 16 rows and one slice (split) of the
+// reduction; its waves interleave over 128-element steps, each lane loading
+// 16 bytes of X per MFMA (row = lane % 16) and the next step's operands while
+// the current step multiplies. The waves' sums meet in LDS in wave order.
+//
+// Column contraction: the reduction runs over rows while Z is row-major, so a
+// 32-row x 64-column tile goes through a wave-private LDS region and comes
+// back transposed with ds_read_b64_tr_b16 (gfx950): within each group of 16
+// lanes, lane 4a + b addresses an 8-byte piece (row a, columns 4b..4b+3) and
+// lane 4b + e receives element a of it, so every lane holds consecutive rows
+// of one column, the MFMA operand layout; V's rows are staged the same way.
+// A workgroup owns 64 columns and one slice of the rows; its four waves
+// interleave over 32-row steps and add their sums in LDS in wave order.
+//
+// A split writes float32 partials that a second kernel adds in split order.
+// Every sum has a fixed order, so equal inputs give equal bits. One launch can
+// carry several independent problems (all LoRA gradients of a layer).
 #include "ql_internal.h"
 
 namespace ql {
 namespace {
 
-constexpr int SK_ROWS = 64;    // rows of X per workgroup (16 per wave)
-constexpr int SK_SPLIT = 256;  // reduction length per split
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ int64_t remap_col(int64_t k, int head_dim, int n_rep) {
-  if (n_rep <= 0) return k;
-  const int64_t head = k / head_dim, i = k - head * head_dim;
-  return (head / n_rep) * head_dim + i;
+// floor(x / d) for x < 2^24, d >= 1: a float32 estimate is off by at most one
+__device__ __forceinline__ uint32_t udiv24(uint32_t x, uint32_t d, float inv_d) {
+  uint32_t q = (uint32_t)((float)x * inv_d);
+  const int32_t rem = (int32_t)(x - q * d);
+  if (rem < 0) --q;
+  else if (rem >= (int32_t)d) ++q;
+  return q;
 }
 
-// MFMA 16x16x32: A fragment = 16 rows of X, 8 reduction elements per lane;
-// B fragment = 16 columns (j) of Bt with the same 8 reduction elements.
+// physical column of logical column k of repeat_kv(x): head k / head_dim
+// reads kv head (k / head_dim) / n_rep (n_rep 0: identity)
+__device__ __forceinline__ int64_t remap_col(int64_t k, int head_dim, int n_rep) {
+  if (n_rep <= 0) return k;
+  const uint32_t hd = (uint32_t)head_dim;
+  const uint32_t head = udiv24((uint32_t)k, hd, 1.f / (float)hd);
+  const uint32_t i = (uint32_t)k - head * hd;
+  return (int64_t)udiv24(head, (uint32_t)n_rep, 1.f / (float)n_rep) * hd + i;
+}
+
+template <typename T>
+__device__ __forceinline__ T pick3(int i, T a, T b, T c) {
+  return i == 0 ? a : (i == 1 ? b : c);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// v if keep, else zeros, without a branch (a select here tends to become one)
+__device__ __forceinline__ uint4 keep_if(uint4 v, bool keep) {
+  const uint32_t m = 0u - (uint32_t)keep;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+__device__ __forceinline__ i16x4_t lds_tr(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p);
+}
+
+// ------------------------------------------------------- row contraction
+constexpr int RC_ROWS = 16;
+constexpr int RC_STEP = 128;  // reduction elements per wave step (4 MFMAs)
+constexpr int RC_WAVES = 4;
+
 template <int NCG>
-__global__ __launch_bounds__(256) void k_skinny_partial(const SkinnyArgs a, float* __restrict__ part) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * SK_ROWS + w * 16;
-  const int64_t kbeg = (int64_t)blockIdx.y * SK_SPLIT;
-  const int64_t kend = kbeg + SK_SPLIT < a.K ? kbeg + SK_SPLIT : a.K;
-  const int np = a.r * a.nseg;
+__global__ __launch_bounds__(64 * RC_WAVES) void k_rowc(const RowArgs a) {
+  constexpr int W = RC_WAVES;
+  __shared__ f32x4_t red[(W - 1) * NCG][64];
+  // w is wave-uniform; readfirstlane tells the compiler, so the step loops stay scalar
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int p = 0;
+  for (int i = 1; i < a.nprob; ++i)
+    if ((int)blockIdx.x >= a.p[i].tile0) p = i;
+  const RowProb& P = a.p[p];
+  const int64_t M = P.M, K = P.K;
+  const int r = P.r, np = r * P.nseg, ns = P.nsplit;
+  const int t = (int)blockIdx.x - P.tile0;
+  const int tile = t / ns, sp = t - tile * ns;
+  const int64_t m0 = (int64_t)tile * RC_ROWS;
+  const int64_t nsteps = (K + RC_STEP - 1) / RC_STEP;
+  const int64_t s_lo = nsteps * sp / ns, s_hi = nsteps * (sp + 1) / ns;
+  const int g = lane >> 4, s16 = lane & 15;
+  // rows past M read row 0: MFMA output row i depends on operand row i only,
+  // and those rows are never stored
+  const int64_t m = m0 + s16;
+  const uint16_t* xrow = P.X + (m < M ? m : 0) * P.ldx;
+  const uint16_t* bcol[NCG];
+#pragma unroll
+  for (int c = 0; c < NCG; ++c) {  // columns past np read row 0 of Bt[0] (never stored)
+    const int jt = 16 * c + s16;
+    const int sg = jt < np ? jt / r : 0, j = jt < np ? jt - sg * r : 0;
+    bcol[c] = pick3(sg, P.Bt[0], P.Bt[1], P.Bt[2]) + (int64_t)j * K;
+  }
+  // Loads have no branches (a branch around them would make the compiler
+  // wait for the prefetch too): reduction elements past K load element 0 and
+  // are zeroed in both operands before use.
+  auto load = [&](int64_t st, uint4 (&xa)[4], uint4 (&xb)[NCG][4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t k = st * RC_STEP + 32 * q + 8 * g;
+      const int64_t kc = k < K ? k : 0;
+      xa[q] = *(const uint4*)(xrow + remap_col(kc, P.head_dim, P.n_rep));
+#pragma unroll
+      for (int c = 0; c < NCG; ++c) xb[c][q] = *(const uint4*)(bcol[c] + kc);
+    }
+  };
   f32x4_t acc[NCG];
 #pragma unroll
   for (int c = 0; c < NCG; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int64_t m = m0 + (lane & 15);
-  for (int64_t k = kbeg; k < kend; k += 32) {
-    const int64_t kk = k + 8 * (lane >> 4);
-    uint4 av = make_uint4(0, 0, 0, 0);
-    if (m < a.M && kk < a.K) av = *(const uint4*)(a.X + m * a.ldx + remap_col(kk, a.head_dim, a.n_rep));
-    const bf16x8_t af = __builtin_bit_cast(bf16x8_t, av);
+  auto mma = [&](int64_t st, const uint4 (&xa)[4], const uint4 (&xb)[NCG][4]) {
 #pragma unroll
-    for (int c = 0; c < NCG; ++c) {
-      const int jt = 16 * c + (lane & 15);
-      uint4 bv = make_uint4(0, 0, 0, 0);
-      if (jt < np && kk < a.K) {
-        const int sg = jt / a.r, j = jt - sg * a.r;
-        const uint16_t* bt = sg == 0 ? a.Bt[0] : (sg == 1 ? a.Bt[1] : a.Bt[2]);
-        bv = *(const uint4*)(bt + (int64_t)j * a.K + kk);
-      }
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8_t, bv), acc[c], 0, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+      const bool in = st * RC_STEP + 32 * q + 8 * g < K;
+      const uint4 x = keep_if(xa[q], in);
+#pragma unroll
+      for (int c = 0; c < NCG; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x), as_bf16x8(keep_if(xb[c][q], in)), acc[c],
+                                                         0, 0, 0);
+    }
+  };
+  // two register sets take turns (no copies, which would wait for the
+  // prefetch); a step past the end reloads the current one (cache hits)
+  int64_t st = s_lo + w;
+  if (st < s_hi) {
+    uint4 xa0[4], xb0[NCG][4], xa1[4], xb1[NCG][4];
+    load(st, xa0, xb0);
+    while (true) {
+      load(st + W < s_hi ? st + W : st, xa1, xb1);
+      mma(st, xa0, xb0);
+      if (st + W >= s_hi) break;
+      st += W;
+      load(st + W < s_hi ? st + W : st, xa0, xb0);
+      mma(st, xa1, xb1);
+      if (st + W >= s_hi) break;
+      st += W;
     }
   }
-  // lane holds rows 4*(lane/16)+v, column lane%16 of each 16x16 tile
+  if (w > 0) {
+#pragma unroll
+    for (int c = 0; c < NCG; ++c) red[(w - 1) * NCG + c][lane] = acc[c];
+  }
+  __syncthreads();
+  if (w > 0) return;
+#pragma unroll
+  for (int q = 0; q < W - 1; ++q)
+#pragma unroll
+    for (int c = 0; c < NCG; ++c) acc[c] += red[q * NCG + c][lane];
+  // lane holds rows 4 (lane / 16) + v, column lane % 16 of each 16 x 16 tile
 #pragma unroll
   for (int c = 0; c < NCG; ++c)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int64_t mm = m0 + 4 * (lane >> 4) + v;
-      const int jt = 16 * c + (lane & 15);
-      if (mm < a.M && jt < np) part[((int64_t)blockIdx.y * a.M + mm) * np + jt] = acc[c][v];
+      const int64_t mm = m0 + 4 * g + v;
+      const int jt = 16 * c + s16;
+      if (mm >= M || jt >= np) continue;
+      if (ns == 1) {
+        const int sg = jt / r, j = jt - sg * r;
+        uint16_t* o = pick3(sg, P.out[0], P.out[1], P.out[2]);
+        o[mm * r + j] = f32_to_bf16(acc[c][v]);
+      } else {
+        P.part[((int64_t)sp * M + mm) * np + jt] = acc[c][v];
+      }
     }
 }
 
-__global__ void k_skinny_reduce(const SkinnyArgs a, const float* __restrict__ part, int nsplit) {
-  const int np = a.r * a.nseg;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.M * np) return;
+__global__ __launch_bounds__(256) void k_rowc_reduce(const RowArgs a) {
+  int p = 0;
+  for (int i = 1; i < a.nprob; ++i)
+    if ((int)blockIdx.x >= a.p[i].rtile0) p = i;
+  const RowProb& P = a.p[p];
+  const int r = P.r, np = r * P.nseg;
+  const int64_t idx = (int64_t)((int)blockIdx.x - P.rtile0) * 256 + threadIdx.x;
+  if (idx >= P.M * np) return;
   const int64_t m = idx / np;
   const int jt = (int)(idx - m * np);
   float s = 0.f;
-  for (int p = 0; p < nsplit; ++p) s += part[((int64_t)p * a.M + m) * np + jt];
-  const int sg = jt / a.r, j = jt - sg * a.r;
-  uint16_t* o = sg == 0 ? a.out[0] : (sg == 1 ? a.out[1] : a.out[2]);
-  o[m * a.r + j] = f32_to_bf16(s);
+  for (int sp = 0; sp < P.nsplit; ++sp) s += P.part[((int64_t)sp * P.M + m) * np + jt];
+  const int sg = jt / r, j = jt - sg * r;
+  uint16_t* o = pick3(sg, P.out[0], P.out[1], P.out[2]);
+  o[m * r + j] = f32_to_bf16(s);
 }
 
-int64_t skinny_nsplit(int64_t K) { return (K + SK_SPLIT - 1) / SK_SPLIT; }
+// ---------------------------------------------------- column contraction
+constexpr int CC_COLS = 64;
+constexpr int CC_ROWS = 32;
 
-// Column reduction out[j][c] = s * sum_m Z[m][c] V[m][j]. A workgroup owns
-// CR_COLS columns (two per lane: one 4-byte load per row) and one block of
-// rows, 16 ranks per pass (blockIdx.z). Its four waves take interleaved rows;
-// the block's V rows are staged in LDS as float32 (read by broadcast). The
-// waves' sums are combined in LDS in wave order. With one row block the
-// workgroup writes the result; with several, float32 partials go to the
-// workspace and a second pass adds them in block order.
-constexpr int CR_COLS = 128;
-constexpr int CR_SUB = 256;  // V rows staged per LDS round
+// NJ: 16-column groups of V (np <= 16 NJ); VEC: r % 8 == 0, so 8 consecutive
+// columns of V lie in one projection and load as 16 bytes.
+template <int NJ, bool VEC>
+__global__ __launch_bounds__(256) void k_colc(const ColArgs a) {
+  // V rows are padded to an odd multiple of 32 bytes: the four rows one
+  // transposed read touches per 16 lanes then fall on distinct banks
+  constexpr int PV = 32 * (NJ | 1);
+  constexpr int ZB = CC_ROWS * 128;     // Z tile: 32 rows x 64 bf16
+  constexpr int WB = ZB + CC_ROWS * PV;  // one wave's region
+  constexpr int RB = 3 * 4 * NJ * 64 * 16;
+  constexpr int LB = 4 * WB > RB ? 4 * WB : RB;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LB];
+  // w is wave-uniform; readfirstlane tells the compiler, so the step loops stay scalar
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int p = 0;
+  for (int i = 1; i < a.nprob; ++i)
+    if ((int)blockIdx.x >= a.p[i].tile0) p = i;
+  const ColProb& P = a.p[p];
+  const int64_t C = P.C;
+  const int r = P.r, np = r * P.nseg, ns = P.nsplit;
+  const int t = (int)blockIdx.x - P.tile0;
+  const int cb = t / ns, sp = t - cb * ns;
+  const int64_t c0 = (int64_t)cb * CC_COLS;
+  const int64_t r_lo = (int64_t)sp * P.rows_per_split;
+  const int64_t r_hi = r_lo + P.rows_per_split < P.M ? r_lo + P.rows_per_split : P.M;
+  const int64_t nsteps = (r_hi - r_lo + CC_ROWS - 1) / CC_ROWS;
+  uint8_t* zt = smem + w * WB;
+  uint8_t* vt = zt + ZB;
 
-__global__ __launch_bounds__(256) void k_colred_partial(const ColRedArgs a, int64_t rows_per_block, int nblk,
-                                                        float* __restrict__ part) {
-  __shared__ float vs[CR_SUB][16];
-  __shared__ float red[3][CR_COLS][17];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int64_t c = (int64_t)blockIdx.x * CR_COLS + 2 * lane;
-  const int64_t mb = (int64_t)blockIdx.y * rows_per_block;
-  const int64_t me = mb + rows_per_block < a.M ? mb + rows_per_block : a.M;
-  const int j0 = blockIdx.z * 16;
-  const bool live = c < a.C;
-  // columns c, c + 1 stay inside one head under the repeat_kv remap (C, head_dim even)
-  const int64_t pc = live ? remap_col(c, a.head_dim, a.n_rep) : 0;
-  const uint32_t* zp = (const uint32_t*)(a.Z + pc);
-  const int64_t ldw = a.ldz / 2;
-  float acc0[16], acc1[16];
+  // Z: lane loads rows zr + 8u (u < 4), 16-byte chunk zc of the 64 columns.
+  // Columns past C read column 0 (MFMA output row c depends on column c
+  // only). Loads have no branches (a branch around them would make the
+  // compiler wait for the prefetch too): rows past the slice load row r_lo and
+  // are zeroed, with their V rows, when the tile is stored to LDS.
+  const int zr = lane >> 3, zc = lane & 7;
+  const int64_t zcol = c0 + 8 * zc;
+  const uint16_t* zbase = P.Z + remap_col(zcol < C ? zcol : 0, P.head_dim, P.n_rep);
+  const int64_t ldz8 = 8 * P.ldz;
+  const uint16_t* zlo = zbase + r_lo * P.ldz;
+  auto loadZ = [&](int64_t mb, uint4 (&z)[4]) {
+    const uint16_t* p0 = zbase + (mb + zr) * P.ldz;
 #pragma unroll
-  for (int jj = 0; jj < 16; ++jj) acc0[jj] = acc1[jj] = 0.f;
-  for (int64_t sb = mb; sb < me; sb += CR_SUB) {
-    const int64_t se = sb + CR_SUB < me ? sb + CR_SUB : me;
-    __syncthreads();
-    for (int64_t i = t; i < (se - sb) * 16; i += 256) {
-      const int64_t mi = i >> 4;
-      const int jj = (int)(i & 15);
-      vs[mi][jj] = (j0 + jj < a.r) ? bf16_to_f32(a.V[(sb + mi) * a.r + j0 + jj]) : 0.f;
+    for (int u = 0; u < 4; ++u) {
+      const uint16_t* pu = mb + zr + 8 * u < r_hi ? p0 + u * ldz8 : zlo;
+      z[u] = *(const uint4*)pu;
     }
-    __syncthreads();
-    if (live) {
-      int64_t m = sb + w;
-      for (; m + 12 < se; m += 16) {  // four rows of this wave in flight
-        uint32_t zz[4];
+  };
+  // V: chunk q = lane + 64 i is row q / (2 NJ), columns 8 (q % (2 NJ)) .. + 7
+  constexpr int VE = VEC ? 4 : 8;  // registers per chunk: 16 bytes, or one element each
+  auto loadV = [&](int64_t mb, uint32_t (&v)[NJ][VE]) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) zz[u] = zp[(m + 4 * u) * ldw];
+    for (int i = 0; i < NJ; ++i) {
+      const int q = lane + 64 * i;
+      const int row = q / (2 * NJ), jt0 = 8 * (q - row * 2 * NJ);
+      const int64_t mm = mb + row < r_hi ? mb + row : r_lo;
+      if (VEC) {
+        const int jc = jt0 < np ? jt0 : 0;
+        const int sg = jc / r, j = jc - sg * r;
+        const uint4 x = *(const uint4*)(pick3(sg, P.V[0], P.V[1], P.V[2]) + mm * r + j);
+        v[i][0] = x.x; v[i][1] = x.y; v[i][2] = x.z; v[i][3] = x.w;
+      } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float z0 = __builtin_bit_cast(float, zz[u] << 16);
-          const float z1 = __builtin_bit_cast(float, zz[u] & 0xffff0000u);
-          const float* vr = vs[m + 4 * u - sb];
-#pragma unroll
-          for (int jj = 0; jj < 16; ++jj) {
-            acc0[jj] += z0 * vr[jj];
-            acc1[jj] += z1 * vr[jj];
-          }
+        for (int k = 0; k < VE; ++k) {
+          const int jc = jt0 + k < np ? jt0 + k : 0;
+          const int sg = jc / r, j = jc - sg * r;
+          v[i][k] = pick3(sg, P.V[0], P.V[1], P.V[2])[mm * r + j];
         }
       }
-      for (; m < se; m += 4) {
-        const uint32_t zz = zp[m * ldw];
-        const float z0 = __builtin_bit_cast(float, zz << 16);
-        const float z1 = __builtin_bit_cast(float, zz & 0xffff0000u);
-        const float* vr = vs[m - sb];
+    }
+  };
+  // Z rows are 128 B; chunk zc of row R sits at chunk zc ^ 2 (R & 3), so the
+  // four rows of one transposed read cover all banks
+  auto stash = [&](int64_t mb, const uint4 (&z)[4], const uint32_t (&v)[NJ][VE]) {
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          acc0[jj] += z0 * vr[jj];
-          acc1[jj] += z1 * vr[jj];
-        }
+    for (int u = 0; u < 4; ++u) {
+      const int R = zr + 8 * u;
+      *(uint4*)(zt + R * 128 + ((zc ^ (2 * (R & 3))) << 4)) = keep_if(z[u], mb + R < r_hi);
+    }
+#pragma unroll
+    for (int i = 0; i < NJ; ++i) {
+      const int q = lane + 64 * i;
+      const int row = q / (2 * NJ), ch = q - row * 2 * NJ, jt0 = 8 * ch;
+      const bool rok = mb + row < r_hi;
+      uint4 x;
+      if (VEC) {
+        x = keep_if(make_uint4(v[i][0], v[i][1], v[i][2], v[i][3]), rok && jt0 < np);
+      } else {
+        uint32_t e[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) e[k] = v[i][k] & (0u - (uint32_t)(rok && jt0 + k < np)) & 0xffffu;
+        x = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
       }
+      *(uint4*)(vt + row * PV + ch * 16) = x;
+    }
+  };
+  // transposed reads: lane 16 g + 4 ra + cbq addresses rows 8 g + ra (+4),
+  // the 4-column piece cbq of a 16-column group
+  const int g = lane >> 4, s16 = lane & 15, ra = s16 >> 2, cbq = s16 & 3;
+  auto frag_z = [&](int tt) {
+    const int ch = 2 * tt + (cbq >> 1);
+    const int off = (8 * g + ra) * 128 + ((ch ^ (2 * ra)) << 4) + (cbq & 1) * 8;
+    const i16x4_t lo = lds_tr(zt + off), hi = lds_tr(zt + off + 4 * 128);
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
+  auto frag_v = [&](int jj) {
+    const int off = (8 * g + ra) * PV + jj * 32 + cbq * 8;
+    const i16x4_t lo = lds_tr(vt + off), hi = lds_tr(vt + off + 4 * PV);
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
+
+  f32x4_t acc[4][NJ];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) acc[tt][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](int64_t mb, const uint4 (&z)[4], const uint32_t (&v)[NJ][VE]) {
+    // LDS runs one wave's operations in order: these writes land after the
+    // previous step's transposed reads
+    stash(mb, z, v);
+    bf16x8_t bv[NJ];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) bv[jj] = frag_v(jj);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const bf16x8_t av = frag_z(tt);
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj)
+        acc[tt][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[jj], acc[tt][jj], 0, 0, 0);
+    }
+  };
+  // two register sets take turns (no copies, which would wait for the
+  // prefetch); a step past the end reloads the current one (cache hits)
+  int64_t st = w;
+  if (st < nsteps) {
+    uint4 z0[4], z1[4];
+    uint32_t v0[NJ][VE], v1[NJ][VE];
+    loadZ(r_lo + st * CC_ROWS, z0);
+    loadV(r_lo + st * CC_ROWS, v0);
+    while (true) {
+      int64_t nx = st + 4 < nsteps ? st + 4 : st;
+      loadZ(r_lo + nx * CC_ROWS, z1);
+      loadV(r_lo + nx * CC_ROWS, v1);
+      mma(r_lo + st * CC_ROWS, z0, v0);
+      if (st + 4 >= nsteps) break;
+      st += 4;
+      nx = st + 4 < nsteps ? st + 4 : st;
+      loadZ(r_lo + nx * CC_ROWS, z0);
+      loadV(r_lo + nx * CC_ROWS, v0);
+      mma(r_lo + st * CC_ROWS, z1, v1);
+      if (st + 4 >= nsteps) break;
+      st += 4;
     }
   }
-  // waves 1..3 hand their sums to wave 0, which adds them in wave order
+  // waves 1..3 hand their sums to wave 0 through LDS (over the tiles)
+  __syncthreads();
+  f32x4_t* red = (f32x4_t*)smem;
   if (w > 0) {
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      red[w - 1][2 * lane][jj] = acc0[jj];
-      red[w - 1][2 * lane + 1][jj] = acc1[jj];
-    }
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) red[(((w - 1) * 4 + tt) * NJ + jj) * 64 + lane] = acc[tt][jj];
   }
   __syncthreads();
-  if (w > 0 || !live) return;
+  if (w > 0) return;
 #pragma unroll
   for (int q = 0; q < 3; ++q)
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      acc0[jj] += red[q][2 * lane][jj];
-      acc1[jj] += red[q][2 * lane + 1][jj];
-    }
+    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-  for (int jj = 0; jj < 16; ++jj) {
-    const int j = j0 + jj;
-    if (j >= a.r) break;
-    if (nblk == 1) {
-      const float v0 = a.s * acc0[jj], v1 = a.s * acc1[jj];
-      const int64_t o0 = a.transpose_out ? c * a.r + j : j * a.C + c;
-      const int64_t o1 = a.transpose_out ? (c + 1) * a.r + j : j * a.C + c + 1;
-      a.out[o0] = a.accumulate ? a.out[o0] + v0 : v0;
-      a.out[o1] = a.accumulate ? a.out[o1] + v1 : v1;
-    } else {
-      float* pp = part + ((int64_t)blockIdx.y * a.r + j) * a.C + c;
-      pp[0] = acc0[jj];
-      pp[1] = acc1[jj];
-    }
+      for (int jj = 0; jj < NJ; ++jj) acc[tt][jj] += red[((q * 4 + tt) * NJ + jj) * 64 + lane];
+  // lane holds columns c0 + 16 tt + 4 g + v, V column 16 jj + lane % 16
+  const int64_t CR = C * r;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t c = c0 + 16 * tt + 4 * g + v;
+        const int jt = 16 * jj + s16;
+        if (c >= C || jt >= np) continue;
+        const int sg = jt / r, j = jt - sg * r;
+        const int64_t o = P.transpose_out ? c * r + j : j * C + c;
+        const float x = acc[tt][jj][v];
+        if (ns == 1) {
+          float* out = pick3(sg, P.out[0], P.out[1], P.out[2]);
+          const float y = P.s * x;
+          out[o] = P.accumulate ? out[o] + y : y;
+        } else {
+          P.part[((int64_t)sp * P.nseg + sg) * CR + o] = x;
+        }
+      }
+}
+
+// Split sums (in split order) of split problems, and the zero outputs of
+// problems without rows.
+__global__ __launch_bounds__(256) void k_colc_reduce(const ColArgs a) {
+  int p = 0;
+  for (int i = 1; i < a.nprob; ++i)
+    if ((int)blockIdx.x >= a.p[i].rtile0) p = i;
+  const ColProb& P = a.p[p];
+  const int64_t n = P.C * P.r;
+  const int64_t idx = (int64_t)((int)blockIdx.x - P.rtile0) * 256 + threadIdx.x;
+  if (idx >= n * P.nseg) return;
+  const int sg = (int)(idx / n);
+  const int64_t o = idx - sg * n;
+  float* out = pick3(sg, P.out[0], P.out[1], P.out[2]);
+  if (P.M == 0) {
+    if (!P.accumulate) out[o] = 0.f;
+    return;
   }
+  float x = 0.f;
+  for (int sp = 0; sp < P.nsplit; ++sp) x += P.part[((int64_t)sp * P.nseg + sg) * n + o];
+  const float y = P.s * x;
+  out[o] = P.accumulate ? out[o] + y : y;
 }
 
-__global__ void k_colred_reduce(const ColRedArgs a, const float* __restrict__ part, int nchunk) {
+// ------------------------------------------------------------- misc
+__global__ __launch_bounds__(256) void k_transpose_bf16(const TransArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.C * a.r) return;
-  const int64_t j = idx / a.C, c = idx - j * a.C;
-  float s = 0.f;
-  for (int p = 0; p < nchunk; ++p) s += part[((int64_t)p * a.r + j) * a.C + c];
-  s *= a.s;
-  const int64_t o = a.transpose_out ? c * a.r + j : j * a.C + c;
-  a.out[o] = a.accumulate ? a.out[o] + s : s;
-}
-
-// Row blocks of a column reduction: enough for about 512 workgroups, at
-// least 64 rows each.
-int colred_blocks(int64_t M, int64_t C, int32_t r) {
-  const int64_t tiles = ((C + CR_COLS - 1) / CR_COLS) * ((r + 15) / 16);
-  int64_t nb = 512 / (tiles > 0 ? tiles : 1);
-  const int64_t maxb = M / 64 > 1 ? M / 64 : 1;
-  if (nb > maxb) nb = maxb;
-  if (nb < 1) nb = 1;
-  return (int)nb;
-}
-
-__global__ void k_transpose_bf16(const uint16_t* __restrict__ in, int64_t rows, int64_t cols,
-                                 uint16_t* __restrict__ out) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= rows * cols) return;
-  const int64_t r = idx / cols, c = idx - r * cols;
-  out[c * rows + r] = in[idx];
+  if (idx >= a.end[a.n - 1]) return;
+  int b = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxTrans - 1; ++i) b += (i < a.n - 1 && idx >= a.end[i]) ? 1 : 0;
+  const int64_t local = idx - (b ? a.end[b - 1] : 0);
+  const int64_t rows = a.rows[b], cols = a.cols[b];
+  const int64_t rr = local / cols, cc = local - rr * cols;
+  a.out[b][cc * rows + rr] = a.in[b][local];
 }
 
 __global__ void k_zero_f32(float* p, int64_t n) {
@@ -216,66 +435,199 @@ __global__ void k_zero_f32(float* p, int64_t n) {
   if (idx < n) p[idx] = 0.f;
 }
 
-}  // namespace
-
-size_t skinny_ws_bytes(int64_t M, int64_t K, int32_t r, int32_t nseg) {
-  return (size_t)skinny_nsplit(K) * (size_t)M * (size_t)(r * nseg) * sizeof(float);
+// Row splits: enough workgroups of 16 rows for about two per CU, each split
+// at least 512 reduction elements.
+int rowc_split(int64_t M, int64_t K) {
+  const int64_t tiles = (M + RC_ROWS - 1) / RC_ROWS;
+  int64_t s = (512 + tiles - 1) / (tiles > 0 ? tiles : 1);
+  const int64_t maxs = K / 512 > 1 ? K / 512 : 1;
+  if (s > maxs) s = maxs;
+  if (s < 1) s = 1;
+  return (int)s;
 }
 
-ql_status launch_skinny(const SkinnyArgs& a, void* ws, hipStream_t st) {
-  if (a.M == 0) return QL_OK;
-  const int np = a.r * a.nseg;
-  const int ncg = (np + 15) / 16;
-  const int64_t nsplit = skinny_nsplit(a.K);
-  dim3 grid((unsigned)((a.M + SK_ROWS - 1) / SK_ROWS), (unsigned)nsplit);
-  float* part = (float*)ws;
-  switch (ncg) {
-#define QL_SK(n) case n: hipLaunchKernelGGL(k_skinny_partial<n>, grid, dim3(256), 0, st, a, part); break;
-    QL_SK(1) QL_SK(2) QL_SK(3) QL_SK(4) QL_SK(5) QL_SK(6) QL_SK(7) QL_SK(8) QL_SK(9) QL_SK(10)
-    QL_SK(11) QL_SK(12)
-#undef QL_SK
-    default: return set_error(QL_ERR_UNSUPPORTED, "skinny: %d columns exceed 192", np);
-  }
-  QL_HIP_CHECK(hipGetLastError());
-  const int64_t n = a.M * np;
-  hipLaunchKernelGGL(k_skinny_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, part,
-                     (int)nsplit);
-  QL_HIP_CHECK(hipGetLastError());
+// Column splits: slices of about 1024 rows (the partials then add about 3%
+// to the bytes read for r = 16), at most 8.
+int colc_split(int64_t M) {
+  int64_t s = (M + 1023) / 1024;
+  if (s > 8) s = 8;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+ql_status check_row(const RowProb& P) {
+  if (P.r < 1 || P.r > 64 || P.nseg < 1 || P.nseg > kMaxSegs)
+    return set_error(QL_ERR_UNSUPPORTED, "row contraction: r %d, nseg %d", P.r, P.nseg);
+  if (P.K % 8 || P.ldx % 8 || (P.n_rep > 0 && P.head_dim % 8))
+    return set_error(QL_ERR_SHAPE, "row contraction: K, row stride and head size must be multiples of 8");
+  if (P.n_rep > 0 && P.K >= (1 << 24)) return set_error(QL_ERR_SHAPE, "row contraction: remapped K >= 2^24");
   return QL_OK;
 }
 
-size_t colred_ws_bytes(int64_t M, int64_t C, int32_t r) {
-  const int nb = colred_blocks(M, C, r);
-  return nb > 1 ? (size_t)nb * (size_t)r * (size_t)C * sizeof(float) : 0;
+template <int NCG>
+void launch_rowc_t(const RowArgs& a, unsigned grid, hipStream_t st) {
+  hipLaunchKernelGGL(k_rowc<NCG>, dim3(grid), dim3(64 * RC_WAVES), 0, st, a);
 }
 
-ql_status launch_colred(const ColRedArgs& a, void* ws, hipStream_t st) {
-  const int64_t n = a.C * a.r;
-  if (a.M == 0) {
-    if (!a.accumulate && n > 0) return launch_zero_f32(a.out, n, st);
-    return QL_OK;
+}  // namespace
+
+size_t rowc_ws_bytes(int64_t M, int64_t K, int32_t np) {
+  const int s = rowc_split(M, K);
+  return s > 1 ? align256((size_t)s * (size_t)M * (size_t)np * 4) : 0;
+}
+
+ql_status launch_rowc(RowArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (a.nprob < 1 || a.nprob > kMaxRowProb) return set_error(QL_ERR_ARG, "row contraction: %d problems", a.nprob);
+  // more than 64 columns: one launch per projection (keeps the operand
+  // registers of a wave in bounds)
+  for (int i = 0; i < a.nprob; ++i) {
+    QL_TRY(check_row(a.p[i]));
+    if (a.p[i].r * a.p[i].nseg > 64 && a.p[i].nseg > 1) {
+      for (int i2 = 0; i2 < a.nprob; ++i2) {
+        const RowProb& P = a.p[i2];
+        for (int sgi = 0; sgi < P.nseg; ++sgi) {
+          RowArgs b{};
+          b.nprob = 1;
+          b.p[0] = P;
+          b.p[0].nseg = 1;
+          b.p[0].Bt[0] = P.Bt[sgi];
+          b.p[0].out[0] = P.out[sgi];
+          QL_TRY(launch_rowc(b, ws, ws_bytes, st));
+        }
+      }
+      return QL_OK;
+    }
   }
-  if ((a.C & 1) || (a.ldz & 1) || (a.n_rep > 0 && (a.head_dim & 1)))
-    return set_error(QL_ERR_SHAPE, "colred: column count and row stride must be even");
-  const int nb = colred_blocks(a.M, a.C, a.r);
-  const int64_t rows = (a.M + nb - 1) / nb;
-  dim3 grid((unsigned)((a.C + CR_COLS - 1) / CR_COLS), (unsigned)nb, (unsigned)((a.r + 15) / 16));
-  float* part = (float*)ws;
-  hipLaunchKernelGGL(k_colred_partial, grid, dim3(256), 0, st, a, rows, nb, part);
+  int ncg = 1, tiles = 0, rtiles = 0;
+  size_t off = 0;
+  for (int i = 0; i < a.nprob; ++i) {
+    RowProb& P = a.p[i];
+    const int np = P.r * P.nseg;
+    const int c = (np + 15) / 16;
+    if (c > ncg) ncg = c;
+    P.tile0 = tiles;
+    P.rtile0 = rtiles;
+    P.nsplit = 1;
+    P.part = nullptr;
+    if (P.M <= 0) continue;
+    P.nsplit = rowc_split(P.M, P.K);
+    tiles += (int)((P.M + RC_ROWS - 1) / RC_ROWS) * P.nsplit;
+    if (P.nsplit > 1) {
+      P.part = (float*)((uint8_t*)ws + off);
+      off += rowc_ws_bytes(P.M, P.K, np);
+      rtiles += (int)((P.M * np + 255) / 256);
+    }
+  }
+  if (off > ws_bytes) return set_error(QL_ERR_WORKSPACE, "row contraction: workspace %zu < %zu", ws_bytes, off);
+  if (tiles == 0) return QL_OK;
+  switch (ncg) {
+    case 1: launch_rowc_t<1>(a, (unsigned)tiles, st); break;
+    case 2: launch_rowc_t<2>(a, (unsigned)tiles, st); break;
+    case 3: launch_rowc_t<3>(a, (unsigned)tiles, st); break;
+    case 4: launch_rowc_t<4>(a, (unsigned)tiles, st); break;
+    default: return set_error(QL_ERR_UNSUPPORTED, "row contraction: %d column groups", ncg);
+  }
   QL_HIP_CHECK(hipGetLastError());
-  if (nb > 1) {
-    hipLaunchKernelGGL(k_colred_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, part, nb);
+  if (rtiles > 0) {
+    hipLaunchKernelGGL(k_rowc_reduce, dim3((unsigned)rtiles), dim3(256), 0, st, a);
     QL_HIP_CHECK(hipGetLastError());
   }
   return QL_OK;
 }
 
-ql_status launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
-                                hipStream_t st) {
-  const int64_t n = rows * cols;
-  if (n == 0) return QL_OK;
-  hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, in, rows,
-                     cols, out);
+size_t colc_ws_bytes(int64_t M, int64_t C, int32_t np) {
+  const int s = colc_split(M);
+  return s > 1 ? align256((size_t)s * (size_t)np * (size_t)C * 4) : 0;
+}
+
+ql_status launch_colc(ColArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (a.nprob < 1 || a.nprob > kMaxColProb) return set_error(QL_ERR_ARG, "column contraction: %d problems", a.nprob);
+  for (int i = 0; i < a.nprob; ++i) {
+    const ColProb& P = a.p[i];
+    if (P.r < 1 || P.r > 64 || P.nseg < 1 || P.nseg > kMaxSegs)
+      return set_error(QL_ERR_UNSUPPORTED, "column contraction: r %d, nseg %d", P.r, P.nseg);
+  }
+  // more than 64 columns: one launch per projection (keeps the accumulators
+  // of a wave in registers); partials are reused launch after launch
+  for (int i = 0; i < a.nprob; ++i) {
+    if (a.p[i].r * a.p[i].nseg <= 64) continue;
+    for (int i2 = 0; i2 < a.nprob; ++i2) {
+      const ColProb& P = a.p[i2];
+      for (int sgi = 0; sgi < P.nseg; ++sgi) {
+        ColArgs b{};
+        b.nprob = 1;
+        b.p[0] = P;
+        b.p[0].nseg = 1;
+        b.p[0].V[0] = P.V[sgi];
+        b.p[0].out[0] = P.out[sgi];
+        QL_TRY(launch_colc(b, ws, ws_bytes, st));
+      }
+    }
+    return QL_OK;
+  }
+  int nj = 1, tiles = 0, rtiles = 0;
+  bool vec = true;
+  size_t off = 0;
+  for (int i = 0; i < a.nprob; ++i) {
+    ColProb& P = a.p[i];
+    const int np = P.r * P.nseg;
+    if (P.C % 8 || (P.M > 0 && (P.ldz % 8 || (P.n_rep > 0 && P.head_dim % 8))))
+      return set_error(QL_ERR_SHAPE, "column contraction: C, row stride and head size must be multiples of 8");
+    if (P.n_rep > 0 && P.C >= (1 << 24)) return set_error(QL_ERR_SHAPE, "column contraction: remapped C >= 2^24");
+    P.tile0 = tiles;
+    P.rtile0 = rtiles;
+    P.nsplit = 0;
+    P.part = nullptr;
+    P.rows_per_split = 0;
+    const int64_t nout = P.C * P.r * P.nseg;
+    if (P.M > 0) {
+      const int s0 = colc_split(P.M);
+      const int64_t rps = ((P.M + s0 - 1) / s0 + CC_ROWS - 1) / CC_ROWS * CC_ROWS;
+      P.rows_per_split = rps;
+      P.nsplit = (int)((P.M + rps - 1) / rps);
+      tiles += (int)((P.C + CC_COLS - 1) / CC_COLS) * P.nsplit;
+      const int c = (np + 15) / 16;
+      if (c > nj) nj = c;
+      if (P.r % 8) vec = false;
+      if (P.nsplit > 1) {
+        P.part = (float*)((uint8_t*)ws + off);
+        off += align256((size_t)P.nsplit * (size_t)nout * 4);
+        rtiles += (int)((nout + 255) / 256);
+      }
+    } else if (!P.accumulate) {
+      rtiles += (int)((nout + 255) / 256);
+    }
+  }
+  if (off > ws_bytes) return set_error(QL_ERR_WORKSPACE, "column contraction: workspace %zu < %zu", ws_bytes, off);
+  if (tiles > 0) {
+#define QL_CC(n)                                                                                      \
+  case n:                                                                                             \
+    if (vec) hipLaunchKernelGGL((k_colc<n, true>), dim3((unsigned)tiles), dim3(256), 0, st, a);       \
+    else hipLaunchKernelGGL((k_colc<n, false>), dim3((unsigned)tiles), dim3(256), 0, st, a);          \
+    break;
+    switch (nj) {
+      QL_CC(1) QL_CC(2) QL_CC(3) QL_CC(4)
+      default: return set_error(QL_ERR_UNSUPPORTED, "column contraction: %d column groups", nj);
+    }
+#undef QL_CC
+    QL_HIP_CHECK(hipGetLastError());
+  }
+  if (rtiles > 0) {
+    hipLaunchKernelGGL(k_colc_reduce, dim3((unsigned)rtiles), dim3(256), 0, st, a);
+    QL_HIP_CHECK(hipGetLastError());
+  }
+  return QL_OK;
+}
+
+ql_status launch_transpose_bf16(TransArgs a, hipStream_t st) {
+  if (a.n < 1 || a.n > kMaxTrans) return set_error(QL_ERR_ARG, "transpose: %d matrices", a.n);
+  int64_t tot = 0;
+  for (int i = 0; i < a.n; ++i) {
+    tot += a.rows[i] * a.cols[i];
+    a.end[i] = tot;
+  }
+  if (tot == 0) return QL_OK;
+  hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, a);
   QL_HIP_CHECK(hipGetLastError());
   return QL_OK;
 }

@@ -56,6 +56,12 @@ ql_status set_error(ql_status st, const char* fmt, ...);
       return ::ql::set_error(QL_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
 
+#define QL_TRY(expr)                 \
+  do {                               \
+    ql_status rc_ = (expr);          \
+    if (rc_ != QL_OK) return rc_;    \
+  } while (0)
+
 // ---------------------------------------------------------------- launchers
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -162,39 +168,69 @@ ql_status profile_begin(hipEvent_t* start, hipEvent_t* stop);
 ql_status profile_end(hipEvent_t start, hipEvent_t stop, int kernel, double flop);
 ql_status launch_gemm_bwd(const BwdArgs& a, hipStream_t st);
 
-// Skinny NT product with split-K: out_j[m][0..r) = bf16(sum_k X[m][k] * Bt_j[.][k]).
-// X columns optionally remapped by repeat_kv. Up to kMaxSegs projections at once
-// (they share X). Needs splitk_ws_bytes() of workspace.
-struct SkinnyArgs {
+// LoRA side products (lora.hip). Both contractions reduce in a fixed order
+// (no atomics), so equal inputs give equal bits whatever the stream timing.
+//
+// Row contraction: out_s[m][j] = bf16(sum_k X[m][k'] Bt_s[j][k]) for the nseg
+// projections that share X (k' = k, or its repeat_kv remap). A launch takes up
+// to kMaxRowProb problems of the same kind; the launcher fills the fields
+// below the line.
+struct RowProb {
   const uint16_t* X;  // bf16 [M x ldx]
   int64_t M, K, ldx;
   int32_t head_dim, n_rep;
-  int32_t r;  // columns per projection
+  int32_t r;  // columns per projection (1..64)
   int32_t nseg;
   const uint16_t* Bt[kMaxSegs];  // bf16 [r x K]
   uint16_t* out[kMaxSegs];       // bf16 [M x r]
+  // ---- launcher
+  float* part;  // float32 [nsplit][M][r * nseg] when nsplit > 1
+  int32_t nsplit, tile0, rtile0;
 };
-size_t skinny_ws_bytes(int64_t M, int64_t K, int32_t r, int32_t nseg);
-ql_status launch_skinny(const SkinnyArgs& a, void* ws, hipStream_t st);
+constexpr int kMaxRowProb = 2;
+struct RowArgs {
+  int32_t nprob;
+  RowProb p[kMaxRowProb];
+};
+// Workspace of one row problem (float32 split partials; 0 if unsplit).
+size_t rowc_ws_bytes(int64_t M, int64_t K, int32_t np);
+ql_status launch_rowc(RowArgs a, void* ws, size_t ws_bytes, hipStream_t st);
 
-// Column reduction over rows with a fixed order: out[j][c] = s * sum_m Z[m][c] * V[m][j]
-// (+ out if accumulate); Z columns optionally remapped by repeat_kv; V is [M x r] bf16.
-// transpose_out writes out[c * r + j] instead of out[j * C + c].
-struct ColRedArgs {
+// Column contraction: out_s[j][c] = s * sum_m Z[m][c'] V_s[m][j] (+ out_s if
+// accumulate), c' = c or its repeat_kv remap; transpose_out stores
+// out_s[c * r + j] instead. M == 0 writes zeros (keeps out_s if accumulate).
+struct ColProb {
   const uint16_t* Z;  // bf16 [M x ldz]
   int64_t M, C, ldz;
   int32_t head_dim, n_rep;
-  const uint16_t* V;  // bf16 [M x r]
-  int32_t r;
+  int32_t r, nseg;
+  const uint16_t* V[kMaxSegs];  // bf16 [M x r]
+  float* out[kMaxSegs];
   float s;
-  float* out;
   int32_t transpose_out, accumulate;
+  // ---- launcher
+  float* part;  // float32 [nsplit][nseg][C * r] when nsplit > 1
+  int64_t rows_per_split;
+  int32_t nsplit, tile0, rtile0;
 };
-size_t colred_ws_bytes(int64_t M, int64_t C, int32_t r);
-ql_status launch_colred(const ColRedArgs& a, void* ws, hipStream_t st);
+constexpr int kMaxColProb = 14;
+struct ColArgs {
+  int32_t nprob;
+  ColProb p[kMaxColProb];
+};
+size_t colc_ws_bytes(int64_t M, int64_t C, int32_t np);
+ql_status launch_colc(ColArgs a, void* ws, size_t ws_bytes, hipStream_t st);
 
-ql_status launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
-                                hipStream_t st);
+// out_i = in_i^T (bf16 [rows x cols] -> [cols x rows]) for up to kMaxTrans matrices.
+constexpr int kMaxTrans = 6;
+struct TransArgs {
+  int32_t n;
+  const uint16_t* in[kMaxTrans];
+  uint16_t* out[kMaxTrans];
+  int64_t rows[kMaxTrans], cols[kMaxTrans];
+  int64_t end[kMaxTrans];  // launcher: cumulative element counts
+};
+ql_status launch_transpose_bf16(TransArgs a, hipStream_t st);
 ql_status launch_zero_f32(float* p, int64_t n, hipStream_t st);
 
 // Glue of the decoder-layer stand-in.
