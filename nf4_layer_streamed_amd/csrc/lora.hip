@@ -435,22 +435,33 @@ __global__ void k_zero_f32(float* p, int64_t n) {
   if (idx < n) p[idx] = 0.f;
 }
 
-// Row splits: enough workgroups of 16 rows for about two per CU, each split
-// at least 512 reduction elements.
+// Row splits: enough workgroups of 16 rows for one per CU, each split at
+// least 1024 reduction elements (measured: more splits cost more in partials
+// and the second pass than they gain in parallelism).
 int rowc_split(int64_t M, int64_t K) {
   const int64_t tiles = (M + RC_ROWS - 1) / RC_ROWS;
-  int64_t s = (512 + tiles - 1) / (tiles > 0 ? tiles : 1);
-  const int64_t maxs = K / 512 > 1 ? K / 512 : 1;
+  int64_t s = (256 + tiles - 1) / (tiles > 0 ? tiles : 1);
+  const int64_t maxs = K / 1024 > 1 ? K / 1024 : 1;
   if (s > maxs) s = maxs;
   if (s < 1) s = 1;
   return (int)s;
 }
 
-// Column splits: slices of about 1024 rows (the partials then add about 3%
-// to the bytes read for r = 16), at most 8.
-int colc_split(int64_t M) {
-  int64_t s = (M + 1023) / 1024;
+// Column splits, at most one per 512 rows and at most 8 (workspace sizing).
+int colc_max_split(int64_t M) {
+  int64_t s = (M + 511) / 512;
   if (s > 8) s = 8;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+// Split of a launch with `tiles` 64-column tiles in all: none once the tiles
+// alone give about one workgroup per CU (a wave then streams its rows with no
+// second pass, measured fastest), else enough to fill the chip.
+int colc_split(int64_t tiles, int64_t M) {
+  int64_t s = tiles > 0 ? 256 / tiles : 1;
+  const int64_t mx = colc_max_split(M);
+  if (s > mx) s = mx;
   if (s < 1) s = 1;
   return (int)s;
 }
@@ -536,7 +547,7 @@ ql_status launch_rowc(RowArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
 }
 
 size_t colc_ws_bytes(int64_t M, int64_t C, int32_t np) {
-  const int s = colc_split(M);
+  const int s = colc_max_split(M);
   return s > 1 ? align256((size_t)s * (size_t)np * (size_t)C * 4) : 0;
 }
 
@@ -565,6 +576,9 @@ ql_status launch_colc(ColArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
     }
     return QL_OK;
   }
+  int64_t tiles1 = 0;  // column tiles of the launch before splitting
+  for (int i = 0; i < a.nprob; ++i)
+    if (a.p[i].M > 0) tiles1 += (a.p[i].C + CC_COLS - 1) / CC_COLS;
   int nj = 1, tiles = 0, rtiles = 0;
   bool vec = true;
   size_t off = 0;
@@ -581,7 +595,7 @@ ql_status launch_colc(ColArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
     P.rows_per_split = 0;
     const int64_t nout = P.C * P.r * P.nseg;
     if (P.M > 0) {
-      const int s0 = colc_split(P.M);
+      const int s0 = colc_split(tiles1, P.M);
       const int64_t rps = ((P.M + s0 - 1) / s0 + CC_ROWS - 1) / CC_ROWS * CC_ROWS;
       P.rows_per_split = rps;
       P.nsplit = (int)((P.M + rps - 1) / rps);
