@@ -75,6 +75,7 @@ def test_pr1_linear_matches_oracle():
     (77, 320, 208, 5, 7.0),     # ragged M, N not a tile multiple, r not a multiple of 8, s not a power of 2
     (130, 192, 144, 64, 64.0),  # r at its maximum, M just over one tile
     (300, 1024, 400, 16, 32.0), # several tiles each way with ragged tails
+    (1100, 128, 80, 12, 24.0),  # the adapter-gradient reductions split over rows (float32 partials)
 ])
 def test_ragged_shapes_match_oracle(M, K, N, r, alpha):
     require_gpu()
@@ -92,6 +93,20 @@ def test_accumulate_adds_to_existing_grads():
     acc = c.run(need_dx=False, accumulate=True, dA0=dA0, dB0=dB0)
     assert acc["dx"] is None
     # the same float32 addition on both sides
+    assert torch.equal(acc["dA"], dA0 + base["dA"])
+    assert torch.equal(acc["dB"], dB0 + base["dB"])
+
+
+def test_accumulate_with_split_reductions():
+    # M = 1100 splits the dA / dB row reductions; the second pass adds the
+    # split sums, scales and accumulates
+    require_gpu()
+    c = Case(1100, 128, 80, 12, 24.0, ("ragged", 1100, 128, 80, 12))
+    base = c.run()
+    g = torch.Generator().manual_seed(4)
+    dA0 = torch.randn(12, 128, generator=g)
+    dB0 = torch.randn(80, 12, generator=g)
+    acc = c.run(need_dx=False, accumulate=True, dA0=dA0, dB0=dB0)
     assert torch.equal(acc["dA"], dA0 + base["dA"])
     assert torch.equal(acc["dB"], dB0 + base["dB"])
 

@@ -254,8 +254,9 @@ def test_ring_longer_than_or_equal_to_stack(L, nb):
     assert identical(got, s.results())
 
 
-@pytest.mark.parametrize("L,M", [(1, 77), (3, 1)])
+@pytest.mark.parametrize("L,M", [(1, 77), (3, 1), (1, 700)])
 def test_small_stacks_ragged_rows(L, M):
+    # M = 700: the layer's adapter-gradient reductions split over rows
     require_gpu()
     s = GpuStack("smollm2_stack", L=L, M=M)
     assert s.step(resident=False, reuse=True) == ql.QL_OK
