@@ -197,6 +197,7 @@ __global__ __launch_bounds__(256) void k_rowc_reduce(const RowArgs a) {
 // ---------------------------------------------------- column contraction
 constexpr int CC_COLS = 64;
 constexpr int CC_ROWS = 32;
+constexpr int CC_ZERO = 4096;  // outputs zeroed per workgroup for a problem without rows
 
 // NJ: 16-column groups of V (np <= 16 NJ); VEC: r % 8 == 0, so 8 consecutive
 // columns of V lie in one projection and load as 16 bytes.
@@ -219,6 +220,18 @@ __global__ __launch_bounds__(256) void k_colc(const ColArgs a) {
   const int64_t C = P.C;
   const int r = P.r, np = r * P.nseg, ns = P.nsplit;
   const int t = (int)blockIdx.x - P.tile0;
+  if (P.M == 0) {  // a gradient that is exactly zero: CC_ZERO outputs per workgroup
+    const int64_t n = C * r;
+#pragma unroll
+    for (int k = 0; k < CC_ZERO / 256; ++k) {
+      const int64_t e = (int64_t)t * CC_ZERO + k * 256 + threadIdx.x;
+      if (e < n * P.nseg) {
+        const int sg = (int)(e / n);
+        pick3(sg, P.out[0], P.out[1], P.out[2])[e - sg * n] = 0.f;
+      }
+    }
+    return;
+  }
   const int cb = t / ns, sp = t - cb * ns;
   const int64_t c0 = (int64_t)cb * CC_COLS;
   const int64_t r_lo = (int64_t)sp * P.rows_per_split;
@@ -394,8 +407,7 @@ __global__ __launch_bounds__(256) void k_colc(const ColArgs a) {
       }
 }
 
-// Split sums (in split order) of split problems, and the zero outputs of
-// problems without rows.
+// Split sums, in split order.
 __global__ __launch_bounds__(256) void k_colc_reduce(const ColArgs a) {
   int p = 0;
   for (int i = 1; i < a.nprob; ++i)
@@ -407,10 +419,6 @@ __global__ __launch_bounds__(256) void k_colc_reduce(const ColArgs a) {
   const int sg = (int)(idx / n);
   const int64_t o = idx - sg * n;
   float* out = pick3(sg, P.out[0], P.out[1], P.out[2]);
-  if (P.M == 0) {
-    if (!P.accumulate) out[o] = 0.f;
-    return;
-  }
   float x = 0.f;
   for (int sp = 0; sp < P.nsplit; ++sp) x += P.part[((int64_t)sp * P.nseg + sg) * n + o];
   const float y = P.s * x;
@@ -590,7 +598,7 @@ ql_status launch_colc(ColArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
     if (P.n_rep > 0 && P.C >= (1 << 24)) return set_error(QL_ERR_SHAPE, "column contraction: remapped C >= 2^24");
     P.tile0 = tiles;
     P.rtile0 = rtiles;
-    P.nsplit = 0;
+    P.nsplit = 1;
     P.part = nullptr;
     P.rows_per_split = 0;
     const int64_t nout = P.C * P.r * P.nseg;
@@ -609,7 +617,7 @@ ql_status launch_colc(ColArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
         rtiles += (int)((nout + 255) / 256);
       }
     } else if (!P.accumulate) {
-      rtiles += (int)((nout + 255) / 256);
+      tiles += (int)((nout + CC_ZERO - 1) / CC_ZERO);
     }
   }
   if (off > ws_bytes) return set_error(QL_ERR_WORKSPACE, "column contraction: workspace %zu < %zu", ws_bytes, off);
