@@ -356,15 +356,18 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     }
     QL_TRY(launch_gemm_fwd(a, st));
   }
-  QL_TRY(launch_swiglu_fwd(S(QL_SAVED_GATE), S(QL_SAVED_UP), M * I, S(QL_SAVED_ACT), st));
   {  // down, residual h_mid
-    if (on) {
+    if (on) {  // act = SwiGLU(gate, up) and U of down in one pass
       RowArgs ra{};
       ra.nprob = 1;
+      ra.mode = 1;
       RowProb& u = ra.p[0];
-      u.X = S(QL_SAVED_ACT); u.M = M; u.K = I; u.ldx = I; u.r = r; u.nseg = 1;
+      u.Xin[0] = S(QL_SAVED_GATE); u.Xin[1] = S(QL_SAVED_UP); u.Xout[0] = S(QL_SAVED_ACT);
+      u.M = M; u.K = I; u.ldx = I; u.r = r; u.nseg = 1;
       u.Bt[0] = u16(lo[QL_PROJ_DOWN].A); u.out[0] = S(QL_SAVED_U0 + QL_PROJ_DOWN);
       QL_TRY(launch_rowc(ra, scratch, WS.scratch_bytes, st));
+    } else {
+      QL_TRY(launch_swiglu_fwd(S(QL_SAVED_GATE), S(QL_SAVED_UP), M * I, S(QL_SAVED_ACT), st));
     }
     FwdArgs a{};
     a.X = S(QL_SAVED_ACT); a.M = M; a.K = I; a.ldx = I; a.r = r; a.s = s; a.nseg = 1;
@@ -459,12 +462,21 @@ static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const L
   }
   add(db_prob(dh, M, H, S(QL_SAVED_U0 + QL_PROJ_DOWN), r, s, dB[QL_PROJ_DOWN], accumulate));
   add(da_prob(S(QL_SAVED_ACT), M, I, I, 0, 0, Gd, r, s, dA[QL_PROJ_DOWN], accumulate));
-  // SwiGLU
-  QL_TRY(launch_swiglu_bwd(S(QL_SAVED_GATE), S(QL_SAVED_UP), T(WS.dact), M * I, T(WS.dg), T(WS.du), st));
-  // gate + up: dn2 = dg W_g + s G_g A_g + du W_u + s G_u A_u
+  // SwiGLU backward and G of gate and up: one pass when the rank allows
   uint16_t* Gg = T(WS.G[1]);
   uint16_t* Gu = T(WS.G[2]);
-  {
+  if (r <= kSwigluBwdMaxR) {
+    RowArgs ra{};
+    ra.nprob = 1;
+    ra.mode = 2;
+    RowProb& q = ra.p[0];
+    q.Xin[0] = S(QL_SAVED_GATE); q.Xin[1] = S(QL_SAVED_UP); q.Xin[2] = T(WS.dact);
+    q.Xout[0] = T(WS.dg); q.Xout[1] = T(WS.du);
+    q.M = M; q.K = I; q.ldx = I; q.r = r; q.nseg = 2;
+    q.Bt[0] = bt[1]; q.Bt[1] = bt[2]; q.out[0] = Gg; q.out[1] = Gu;
+    QL_TRY(launch_rowc(ra, scratch, WS.scratch_bytes, st));
+  } else {
+    QL_TRY(launch_swiglu_bwd(S(QL_SAVED_GATE), S(QL_SAVED_UP), T(WS.dact), M * I, T(WS.dg), T(WS.du), st));
     RowArgs ra{};
     ra.nprob = 2;
     ra.p[0] = g_prob(T(WS.dg), M, I, r, bt[1], Gg);

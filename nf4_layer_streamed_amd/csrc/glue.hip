@@ -7,20 +7,6 @@
 namespace ql {
 namespace {
 
-__device__ __forceinline__ void unpack8(const uint4 q, float (&f)[8]) {
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
-    f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
-  }
-}
-
-__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
-  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                    pack_bf16x2(f[6], f[7]));
-}
-
 __device__ __forceinline__ float wave_sum(float v) {
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
@@ -92,40 +78,19 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict_
   }
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
-
 __global__ __launch_bounds__(256) void k_swiglu_fwd(const uint4* __restrict__ g, const uint4* __restrict__ u,
                                                     int64_t nq, uint4* __restrict__ act) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += stride) {
-    float gf[8], uf[8], o[8];
-    unpack8(g[q], gf);
-    unpack8(u[q], uf);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = gf[i] * sigmoidf_(gf[i]) * uf[i];
-    act[q] = pack8(o);
-  }
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += stride)
+    act[q] = swiglu_act8(g[q], u[q]);
 }
 
-// dg = dact * u * sig(g) (1 + g (1 - sig(g))), du = dact * silu(g)
 __global__ __launch_bounds__(256) void k_swiglu_bwd(const uint4* __restrict__ g, const uint4* __restrict__ u,
                                                     const uint4* __restrict__ da, int64_t nq,
                                                     uint4* __restrict__ dg, uint4* __restrict__ du) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += stride) {
-    float gf[8], uf[8], df[8], og[8], ou[8];
-    unpack8(g[q], gf);
-    unpack8(u[q], uf);
-    unpack8(da[q], df);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float sg = sigmoidf_(gf[i]);
-      og[i] = df[i] * uf[i] * (sg * (1.0f + gf[i] * (1.0f - sg)));
-      ou[i] = df[i] * (gf[i] * sg);
-    }
-    dg[q] = pack8(og);
-    du[q] = pack8(ou);
-  }
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += stride)
+    swiglu_grad8(g[q], u[q], da[q], dg[q], du[q]);
 }
 
 __global__ void k_repeat_kv_bwd(const float* __restrict__ da, int64_t M, int64_t H, int64_t kv, int d,

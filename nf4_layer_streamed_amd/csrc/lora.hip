@@ -76,9 +76,14 @@ constexpr int RC_ROWS = 16;
 constexpr int RC_STEP = 128;  // reduction elements per wave step (4 MFMAs)
 constexpr int RC_WAVES = 4;
 
-template <int NCG>
+// MODE 0: X is read. MODE 1: X = SwiGLU(gate, up) is made from Xin and
+// stored. MODE 2: dg, du are made from gate, up, dact and stored; column
+// groups 0 .. NCG/2-1 contract dg with Bt[0], the rest du with Bt[1].
+template <int NCG, int MODE>
 __global__ __launch_bounds__(64 * RC_WAVES) void k_rowc(const RowArgs a) {
   constexpr int W = RC_WAVES;
+  constexpr int NIN = MODE == 0 ? 1 : (MODE == 1 ? 2 : 3);  // operand streams loaded per chunk
+  constexpr int NCGS = MODE == 2 ? NCG / 2 : NCG;           // column groups per projection (modes 1, 2)
   __shared__ f32x4_t red[(W - 1) * NCG][64];
   // w is wave-uniform; readfirstlane tells the compiler, so the step loops stay scalar
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -97,23 +102,43 @@ __global__ __launch_bounds__(64 * RC_WAVES) void k_rowc(const RowArgs a) {
   // rows past M read row 0: MFMA output row i depends on operand row i only,
   // and those rows are never stored
   const int64_t m = m0 + s16;
-  const uint16_t* xrow = P.X + (m < M ? m : 0) * P.ldx;
+  const bool mrow = m < M;
+  const int64_t roff = (mrow ? m : 0) * P.ldx;
+  const uint16_t* xin[NIN];
+#pragma unroll
+  for (int i = 0; i < NIN; ++i) xin[i] = (MODE == 0 ? P.X : P.Xin[i]) + roff;
+  // output column of group c for this lane: projection sg, column j
+  auto colmap = [&](int c, int& sg, int& j) -> bool {
+    if (MODE == 0) {
+      const int jt = 16 * c + s16;
+      sg = jt < np ? jt / r : 0;
+      j = jt < np ? jt - sg * r : 0;
+      return jt < np;
+    }
+    sg = c / NCGS;
+    j = 16 * (c - sg * NCGS) + s16;
+    const bool ok = j < r;
+    if (!ok) j = 0;
+    return ok;
+  };
   const uint16_t* bcol[NCG];
 #pragma unroll
-  for (int c = 0; c < NCG; ++c) {  // columns past np read row 0 of Bt[0] (never stored)
-    const int jt = 16 * c + s16;
-    const int sg = jt < np ? jt / r : 0, j = jt < np ? jt - sg * r : 0;
+  for (int c = 0; c < NCG; ++c) {  // columns past r read row 0 (never stored)
+    int sg, j;
+    colmap(c, sg, j);
     bcol[c] = pick3(sg, P.Bt[0], P.Bt[1], P.Bt[2]) + (int64_t)j * K;
   }
   // Loads have no branches (a branch around them would make the compiler
   // wait for the prefetch too): reduction elements past K load element 0 and
   // are zeroed in both operands before use.
-  auto load = [&](int64_t st, uint4 (&xa)[4], uint4 (&xb)[NCG][4]) {
+  auto load = [&](int64_t st, uint4 (&xa)[NIN][4], uint4 (&xb)[NCG][4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t k = st * RC_STEP + 32 * q + 8 * g;
       const int64_t kc = k < K ? k : 0;
-      xa[q] = *(const uint4*)(xrow + remap_col(kc, P.head_dim, P.n_rep));
+      const int64_t kx = MODE == 0 ? remap_col(kc, P.head_dim, P.n_rep) : kc;
+#pragma unroll
+      for (int i = 0; i < NIN; ++i) xa[i][q] = *(const uint4*)(xin[i] + kx);
 #pragma unroll
       for (int c = 0; c < NCG; ++c) xb[c][q] = *(const uint4*)(bcol[c] + kc);
     }
@@ -121,22 +146,37 @@ __global__ __launch_bounds__(64 * RC_WAVES) void k_rowc(const RowArgs a) {
   f32x4_t acc[NCG];
 #pragma unroll
   for (int c = 0; c < NCG; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](int64_t st, const uint4 (&xa)[4], const uint4 (&xb)[NCG][4]) {
+  auto mma = [&](int64_t st, const uint4 (&xa)[NIN][4], const uint4 (&xb)[NCG][4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const bool in = st * RC_STEP + 32 * q + 8 * g < K;
-      const uint4 x = keep_if(xa[q], in);
+      const int64_t k = st * RC_STEP + 32 * q + 8 * g;
+      const bool in = k < K;
+      uint4 x0 = xa[0][q], x1 = x0;
+      if (MODE == 1) {
+        x0 = swiglu_act8(xa[0][q], xa[1][q]);
+        if (in && mrow) *(uint4*)(P.Xout[0] + roff + k) = x0;
+      } else if (MODE == 2) {
+        swiglu_grad8(xa[0][q], xa[1][q], xa[2][q], x0, x1);
+        if (in && mrow) {
+          *(uint4*)(P.Xout[0] + roff + k) = x0;
+          *(uint4*)(P.Xout[1] + roff + k) = x1;
+        }
+      }
+      x0 = keep_if(x0, in);
+      x1 = keep_if(x1, in);
 #pragma unroll
-      for (int c = 0; c < NCG; ++c)
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x), as_bf16x8(keep_if(xb[c][q], in)), acc[c],
+      for (int c = 0; c < NCG; ++c) {
+        const uint4 xc = (MODE == 2 && c >= NCGS) ? x1 : x0;
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xc), as_bf16x8(keep_if(xb[c][q], in)), acc[c],
                                                          0, 0, 0);
+      }
     }
   };
   // two register sets take turns (no copies, which would wait for the
   // prefetch); a step past the end reloads the current one (cache hits)
   int64_t st = s_lo + w;
   if (st < s_hi) {
-    uint4 xa0[4], xb0[NCG][4], xa1[4], xb1[NCG][4];
+    uint4 xa0[NIN][4], xb0[NCG][4], xa1[NIN][4], xb1[NCG][4];
     load(st, xa0, xb0);
     while (true) {
       load(st + W < s_hi ? st + W : st, xa1, xb1);
@@ -161,20 +201,21 @@ __global__ __launch_bounds__(64 * RC_WAVES) void k_rowc(const RowArgs a) {
     for (int c = 0; c < NCG; ++c) acc[c] += red[q * NCG + c][lane];
   // lane holds rows 4 (lane / 16) + v, column lane % 16 of each 16 x 16 tile
 #pragma unroll
-  for (int c = 0; c < NCG; ++c)
+  for (int c = 0; c < NCG; ++c) {
+    int sg, j;
+    if (!colmap(c, sg, j)) continue;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t mm = m0 + 4 * g + v;
-      const int jt = 16 * c + s16;
-      if (mm >= M || jt >= np) continue;
+      if (mm >= M) continue;
       if (ns == 1) {
-        const int sg = jt / r, j = jt - sg * r;
         uint16_t* o = pick3(sg, P.out[0], P.out[1], P.out[2]);
         o[mm * r + j] = f32_to_bf16(acc[c][v]);
       } else {
-        P.part[((int64_t)sp * M + mm) * np + jt] = acc[c][v];
+        P.part[((int64_t)sp * M + mm) * np + sg * r + j] = acc[c][v];
       }
     }
+  }
 }
 
 __global__ __launch_bounds__(256) void k_rowc_reduce(const RowArgs a) {
@@ -483,9 +524,9 @@ ql_status check_row(const RowProb& P) {
   return QL_OK;
 }
 
-template <int NCG>
+template <int NCG, int MODE>
 void launch_rowc_t(const RowArgs& a, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL(k_rowc<NCG>, dim3(grid), dim3(64 * RC_WAVES), 0, st, a);
+  hipLaunchKernelGGL((k_rowc<NCG, MODE>), dim3(grid), dim3(64 * RC_WAVES), 0, st, a);
 }
 
 }  // namespace
@@ -497,16 +538,26 @@ size_t rowc_ws_bytes(int64_t M, int64_t K, int32_t np) {
 
 ql_status launch_rowc(RowArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
   if (a.nprob < 1 || a.nprob > kMaxRowProb) return set_error(QL_ERR_ARG, "row contraction: %d problems", a.nprob);
+  if (a.mode < 0 || a.mode > 2) return set_error(QL_ERR_ARG, "row contraction: mode %d", a.mode);
+  for (int i = 0; i < a.nprob; ++i) {
+    const RowProb& P = a.p[i];
+    QL_TRY(check_row(P));
+    if (a.mode == 1 && (P.nseg != 1 || P.n_rep > 0))
+      return set_error(QL_ERR_ARG, "row contraction: the SwiGLU forward mode takes one projection, no remap");
+    if (a.mode == 2 && (P.nseg != 2 || P.n_rep > 0 || P.r > kSwigluBwdMaxR))
+      return set_error(QL_ERR_ARG, "row contraction: the SwiGLU backward mode takes two projections of r <= %d",
+                       kSwigluBwdMaxR);
+  }
   // more than 64 columns: one launch per projection (keeps the operand
   // registers of a wave in bounds)
-  for (int i = 0; i < a.nprob; ++i) {
-    QL_TRY(check_row(a.p[i]));
+  for (int i = 0; i < a.nprob && a.mode == 0; ++i) {
     if (a.p[i].r * a.p[i].nseg > 64 && a.p[i].nseg > 1) {
       for (int i2 = 0; i2 < a.nprob; ++i2) {
         const RowProb& P = a.p[i2];
         for (int sgi = 0; sgi < P.nseg; ++sgi) {
           RowArgs b{};
           b.nprob = 1;
+          b.mode = 0;
           b.p[0] = P;
           b.p[0].nseg = 1;
           b.p[0].Bt[0] = P.Bt[sgi];
@@ -522,7 +573,7 @@ ql_status launch_rowc(RowArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
   for (int i = 0; i < a.nprob; ++i) {
     RowProb& P = a.p[i];
     const int np = P.r * P.nseg;
-    const int c = (np + 15) / 16;
+    const int c = a.mode == 2 ? 2 * ((P.r + 15) / 16) : (np + 15) / 16;
     if (c > ncg) ncg = c;
     P.tile0 = tiles;
     P.rtile0 = rtiles;
@@ -539,12 +590,29 @@ ql_status launch_rowc(RowArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
   }
   if (off > ws_bytes) return set_error(QL_ERR_WORKSPACE, "row contraction: workspace %zu < %zu", ws_bytes, off);
   if (tiles == 0) return QL_OK;
-  switch (ncg) {
-    case 1: launch_rowc_t<1>(a, (unsigned)tiles, st); break;
-    case 2: launch_rowc_t<2>(a, (unsigned)tiles, st); break;
-    case 3: launch_rowc_t<3>(a, (unsigned)tiles, st); break;
-    case 4: launch_rowc_t<4>(a, (unsigned)tiles, st); break;
-    default: return set_error(QL_ERR_UNSUPPORTED, "row contraction: %d column groups", ncg);
+  const unsigned grid = (unsigned)tiles;
+  if (a.mode == 0) {
+    switch (ncg) {
+      case 1: launch_rowc_t<1, 0>(a, grid, st); break;
+      case 2: launch_rowc_t<2, 0>(a, grid, st); break;
+      case 3: launch_rowc_t<3, 0>(a, grid, st); break;
+      case 4: launch_rowc_t<4, 0>(a, grid, st); break;
+      default: return set_error(QL_ERR_UNSUPPORTED, "row contraction: %d column groups", ncg);
+    }
+  } else if (a.mode == 1) {
+    switch (ncg) {
+      case 1: launch_rowc_t<1, 1>(a, grid, st); break;
+      case 2: launch_rowc_t<2, 1>(a, grid, st); break;
+      case 3: launch_rowc_t<3, 1>(a, grid, st); break;
+      case 4: launch_rowc_t<4, 1>(a, grid, st); break;
+      default: return set_error(QL_ERR_UNSUPPORTED, "row contraction: %d column groups", ncg);
+    }
+  } else {
+    switch (ncg) {
+      case 2: launch_rowc_t<2, 2>(a, grid, st); break;
+      case 4: launch_rowc_t<4, 2>(a, grid, st); break;
+      default: return set_error(QL_ERR_UNSUPPORTED, "row contraction: %d column groups", ncg);
+    }
   }
   QL_HIP_CHECK(hipGetLastError());
   if (rtiles > 0) {

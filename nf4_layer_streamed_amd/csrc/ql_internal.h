@@ -46,6 +46,47 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// 8 bf16 <-> 8 float32 (element 0 in the low half of the first dword)
+__device__ __forceinline__ void unpack8(const uint4 q, float (&f)[8]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+// SwiGLU on 8 bf16 elements (one code path for the elementwise kernels and
+// the kernels that fuse it): act = bf16(g sig(g) u);
+// dg = bf16(dact u sig(g) (1 + g (1 - sig(g)))), du = bf16(dact g sig(g)).
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ uint4 swiglu_act8(uint4 g, uint4 u) {
+  float gf[8], uf[8], o[8];
+  unpack8(g, gf);
+  unpack8(u, uf);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = gf[i] * sigmoidf_(gf[i]) * uf[i];
+  return pack8(o);
+}
+__device__ __forceinline__ void swiglu_grad8(uint4 g, uint4 u, uint4 da, uint4& dg, uint4& du) {
+  float gf[8], uf[8], df[8], og[8], ou[8];
+  unpack8(g, gf);
+  unpack8(u, uf);
+  unpack8(da, df);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float sg = sigmoidf_(gf[i]);
+    og[i] = df[i] * uf[i] * (sg * (1.0f + gf[i] * (1.0f - sg)));
+    ou[i] = df[i] * (gf[i] * sg);
+  }
+  dg = pack8(og);
+  du = pack8(ou);
+}
+
 // Error reporting (thread-local message), defined in capi.hip.
 ql_status set_error(ql_status st, const char* fmt, ...);
 
@@ -183,6 +224,12 @@ struct RowProb {
   int32_t nseg;
   const uint16_t* Bt[kMaxSegs];  // bf16 [r x K]
   uint16_t* out[kMaxSegs];       // bf16 [M x r]
+  // SwiGLU producer modes (RowArgs::mode, rows of stride ldx, no remap):
+  //  1: Xin = gate, up; X := act = swiglu(gate, up), stored to Xout[0]; nseg 1
+  //  2: Xin = gate, up, dact; dg, du stored to Xout[0], Xout[1]; projection 0
+  //     contracts dg, projection 1 du (nseg 2)
+  const uint16_t* Xin[3];
+  uint16_t* Xout[2];
   // ---- launcher
   float* part;  // float32 [nsplit][M][r * nseg] when nsplit > 1
   int32_t nsplit, tile0, rtile0;
@@ -190,8 +237,12 @@ struct RowProb {
 constexpr int kMaxRowProb = 2;
 struct RowArgs {
   int32_t nprob;
+  int32_t mode;  // 0: plain X; 1, 2: SwiGLU producers (see RowProb)
   RowProb p[kMaxRowProb];
 };
+// Largest rank the SwiGLU-backward producer mode takes (two projections'
+// accumulators per wave); larger ranks use the elementwise kernel.
+constexpr int kSwigluBwdMaxR = 32;
 // Workspace of one row problem (float32 split partials; 0 if unsplit).
 size_t rowc_ws_bytes(int64_t M, int64_t K, int32_t np);
 ql_status launch_rowc(RowArgs a, void* ws, size_t ws_bytes, hipStream_t st);
