@@ -10,12 +10,14 @@ from gpu_util import DEV, f64, ql
 
 class GpuStack:
     def __init__(self, name, L=None, M=None, gen_device="cpu", pinned=True, resident_copy=True, n_buffers=2,
-                 recompute=0, absmax_dq=0):
+                 recompute=0, absmax_dq=0, r=None):
         w = dict(synth.WORKLOADS[name])
         if L is not None:
             w["L"] = L
         if M is not None:
             w["M"] = M
+        if r is not None:  # another adapter rank, alpha = 2 r
+            w["r"], w["alpha"] = r, 2.0 * r
         self.w = w
         self.name = name
         self.M = w["M"]

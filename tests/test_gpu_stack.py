@@ -274,6 +274,26 @@ def test_small_stacks_ragged_rows(L, M):
             close(f64(got["dB"][li][p]), grads[li][p][1], what=f"L{li}:{p}:dB")
 
 
+@pytest.mark.parametrize("r", [40, 64])
+def test_ranks_above_the_fused_swiglu_backward(r):
+    # r > 32 takes the separate SwiGLU backward and the two-problem row launch
+    # for G of gate and up; r = 64 also splits q | k | v's LoRA down per projection
+    require_gpu()
+    s = GpuStack("smollm2_stack", L=1, M=77, r=r)
+    assert s.step(resident=False, reuse=True) == ql.QL_OK
+    got = s.results()
+    assert s.step(resident=True) == ql.QL_OK
+    assert identical(got, s.results())
+    layers = s.oracle_layers()
+    h, saved = ostack.stack_fwd(layers, f64(s.x))
+    close(f64(got["y"]), h, what="y")
+    dx0, grads = ostack.stack_bwd(layers, saved, f64(s.dy))
+    close(f64(got["dx"]), dx0, what="dx0")
+    for p in ("v", "o", "gate", "up", "down"):
+        close(f64(got["dA"][0][p]), grads[0][p][0], what=f"{p}:dA")
+        close(f64(got["dB"][0][p]), grads[0][p][1], what=f"{p}:dB")
+
+
 def test_stack_argument_errors(smol):
     with pytest.raises(ql.QlError) as e:
         ql.stream_layer_stack_fwd(smol.cfg, smol.store, smol.lora, smol.x, smol.M, smol.y, smol.saved,
