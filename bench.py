@@ -22,6 +22,10 @@ the whole step (M tokens per step). The JSON line also carries:
   (2.5166 PFLOP/s); `traffic` is its
   HBM bytes per launch from the committed counter summary (null if the kernel
   sources changed since). gemm_all: all fused-GEMM launches together.
+* hbm_kernels - the HBM-bound kernels against the 8 TB/s HBM peak: the LoRA
+  side products of the step (k_rowc: U, G, with the fused SwiGLU; k_colc: dA,
+  dB), timed in the same pass as the GEMMs, with the bytes each launch must
+  move once; and the standalone nf4_dequant of one gate projection.
 * dense_bf16_gemm - same-session practical ceiling: torch's dense bf16 GEMM
   (hipBLASLt) on pre-dequantised weights at the stack's forward and dX
   shapes; gemm_all.vs_dense_bf16 is the fused NF4 GEMMs' rate over it.
@@ -72,6 +76,17 @@ def kernel_source_hash():
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
+def hbm_entry(n, ms, nbytes, steps):
+    """Rate of an HBM-bound kernel id from its timed launches (bytes = the
+    algorithmic bytes the library records for each launch)."""
+    gbs = nbytes / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+    e = dict(bound="hbm", launches=n, avg_us=round(1000.0 * ms / n, 2), bytes_per_launch=round(nbytes / n),
+             achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4))
+    if steps:
+        e["ms_per_step"] = round(ms / steps, 3)
+    return e
 
 
 def measured_traffic(kernel):
@@ -335,7 +350,7 @@ def main():
         prof = None
         if profile:
             ql.ql_profile_enable(0)
-            prof = {k: ql.ql_profile_read(k) for k in ql.KERNEL_SYMBOLS}
+            prof = {k: ql.ql_profile_read(k) for k in list(ql.KERNEL_SYMBOLS) + list(ql.HBM_KERNEL_SYMBOLS)}
         return t, status, prof
 
     log(f"bench: warmup {args.warmup}, timing {args.steps} streamed steps")
@@ -373,6 +388,12 @@ def main():
                     unit="TFLOP/s", frac=round(dk["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
                     traffic=traffic, flop_per_launch=dk["flop"] / dk["launches"],
                     avg_launch_us=round(dk["avg_us"], 2), launches=dk["launches"])
+    # HBM-bound kernels of the step (LoRA side products), timed in the same pass
+    hbm = {}
+    for k in (ql.QL_KERNEL_LORA_ROW, ql.QL_KERNEL_LORA_COL):
+        n, kms, kb = prof[k]
+        if n:
+            hbm[ql.HBM_KERNEL_SYMBOLS[k]] = hbm_entry(n, kms, kb, args.steps)
     gemm_ms_per_step = sum(v["total_ms"] for v in kern.values()) / args.steps
     gemm_flop = sum(v["flop"] for v in kern.values())
     gemm_all = dict(tflops=round(gemm_flop / (sum(v["total_ms"] for v in kern.values()) * 1e-3) / 1e12, 1))
@@ -385,6 +406,26 @@ def main():
     calib_dst.copy_(calib)
     torch.cuda.synchronize()
     del calib, calib_dst
+
+    # standalone nf4_dequant of one layer's gate projection (14336 x 4096) to bf16
+    Ng, Kg = cfg.proj_shape("gate")
+    _, proj_offs, _ = ql.stream_layer_stack_layout(cfg)
+    po, ao = proj_offs["gate"]  # layer 0's record starts the store
+    gpk = store[po: po + Ng * Kg // 2].to(dev)
+    gam = store[ao: ao + Ng * Kg // 16].to(dev).view(torch.float32)
+    gout = torch.empty(Ng * Kg, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        ql.nf4_dequant(gpk, gam, Ng * Kg, gout)
+    torch.cuda.synchronize()
+    ql.ql_profile_enable(1)
+    for _ in range(20):
+        ql.nf4_dequant(gpk, gam, Ng * Kg, gout)
+    torch.cuda.synchronize()
+    ql.ql_profile_enable(0)
+    n, kms, kb = ql.ql_profile_read(ql.QL_KERNEL_DEQUANT)
+    hbm["k_nf4_dequant"] = dict(hbm_entry(n, kms, kb, None),
+                                what="nf4_dequant of a %d x %d projection to bf16, back to back" % (Ng, Kg))
+    del gpk, gam, gout
 
     # same-session PCIe ceiling: one 1 GiB pinned host-to-device copy
     nb = 1 << 30
@@ -525,6 +566,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kern.items()},
         "roofline": roofline,
+        "hbm_kernels": hbm,
         "dense_bf16_gemm": dense,
         "pcie": pcie,
         "ring8": ring8,

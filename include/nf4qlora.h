@@ -345,27 +345,35 @@ ql_status ql_step_graph_destroy(ql_step_graph g);
 
 /* ----------------------------------------------------------- measurement
  * Kernel timing for roofline measurement. While enabled, every launch of the
- * fused NF4 GEMM kernels is bracketed by two hipEvents recorded on the stream
- * it runs on, together with its algorithmic FLOP count (2 M N (K + r) for the
- * forward, 2 M K (N + r) per reduction segment for dX, over the columns the
- * launch covers). Each kernel comes in a wide-tile (256 x 256 outputs per
- * workgroup) and a narrow-tile (256 x 128) build, timed separately.
+ * timed kernels is bracketed by two hipEvents recorded on the stream it runs
+ * on, together with its algorithmic work:
+ *  - fused NF4 GEMMs (MFMA-bound): FLOPs, 2 M N (K + r) for the forward and
+ *    2 M K (N + r) per reduction segment for dX, over the columns the launch
+ *    covers. Each comes in a wide-tile (256 x 256 outputs per workgroup) and a
+ *    narrow-tile (256 x 128) build, timed separately;
+ *  - the LoRA side products and the standalone dequantisation (HBM-bound):
+ *    bytes each must move once (operands read, outputs written; for a split
+ *    launch the float32 partials written and read back are counted too, and
+ *    the time spans both of its kernels).
  * ql_profile_enable(1) starts a fresh record and reserves a pool of events
  * (reused across records, so timed launches create none), ql_profile_enable(0)
  * stops recording. ql_profile_read waits for the recorded events and returns,
- * for one kernel, the number of launches, their summed duration (ms) and
- * summed FLOPs. Results are unaffected by profiling. The events belong to the
+ * for one kernel id, the number of launches, their summed duration (ms) and
+ * summed work. Results are unaffected by profiling. The events belong to the
  * device current at ql_profile_enable(1). Not thread-safe against concurrent
  * calls on other threads. */
 enum {
-  QL_KERNEL_GEMM_FWD = 0,        /* forward, wide tiles */
-  QL_KERNEL_GEMM_BWD = 1,        /* dX, wide tiles */
-  QL_KERNEL_GEMM_FWD_NARROW = 2, /* forward, narrow tiles */
-  QL_KERNEL_GEMM_BWD_NARROW = 3, /* dX, narrow tiles */
-  QL_KERNEL_COUNT = 4
+  QL_KERNEL_GEMM_FWD = 0,        /* forward, wide tiles (FLOP) */
+  QL_KERNEL_GEMM_BWD = 1,        /* dX, wide tiles (FLOP) */
+  QL_KERNEL_GEMM_FWD_NARROW = 2, /* forward, narrow tiles (FLOP) */
+  QL_KERNEL_GEMM_BWD_NARROW = 3, /* dX, narrow tiles (FLOP) */
+  QL_KERNEL_LORA_ROW = 4,        /* U = x A^T, G = dY B, with a fused SwiGLU when asked (bytes) */
+  QL_KERNEL_LORA_COL = 5,        /* dA = s G^T x, dB = s dY^T U (bytes) */
+  QL_KERNEL_DEQUANT = 6,         /* nf4_dequant (bytes) */
+  QL_KERNEL_COUNT = 7
 };
 ql_status ql_profile_enable(int32_t on);
-ql_status ql_profile_read(int32_t kernel, int64_t* launches, double* ms, double* flop);
+ql_status ql_profile_read(int32_t kernel, int64_t* launches, double* ms, double* work);
 
 #ifdef __cplusplus
 }

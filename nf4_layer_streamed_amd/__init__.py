@@ -33,8 +33,11 @@ EXPORTS = (
     "ql_profile_read", "stream_layer_stack_step_capture", "ql_step_graph_launch", "ql_step_graph_destroy",
 )
 QL_KERNEL_GEMM_FWD, QL_KERNEL_GEMM_BWD, QL_KERNEL_GEMM_FWD_NARROW, QL_KERNEL_GEMM_BWD_NARROW = 0, 1, 2, 3
-# kernel symbol of each profiling id (the names rocprofv3 reports)
+QL_KERNEL_LORA_ROW, QL_KERNEL_LORA_COL, QL_KERNEL_DEQUANT = 4, 5, 6
+# kernel symbol of each profiling id (the names rocprofv3 reports): the fused
+# GEMMs (work in FLOPs) and the HBM-bound kernels (work in bytes)
 KERNEL_SYMBOLS = {0: "k_gemm_fwd<64>", 1: "k_gemm_bwd<128>", 2: "k_gemm_fwd<32>", 3: "k_gemm_bwd<64>"}
+HBM_KERNEL_SYMBOLS = {4: "k_rowc", 5: "k_colc", 6: "k_nf4_dequant"}
 
 
 class QlError(RuntimeError):
@@ -388,7 +391,8 @@ def ql_profile_enable(on):
 
 
 def ql_profile_read(kernel):
-    """-> (launches, total ms, total algorithmic FLOPs) of one fused GEMM kernel."""
+    """-> (launches, total ms, total algorithmic work) of one kernel id: FLOPs
+    for the fused GEMMs, bytes for the HBM-bound kernels."""
     n, ms, fl = ctypes.c_int64(), ctypes.c_double(), ctypes.c_double()
     _check(load().ql_profile_read(kernel, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl)))
     return n.value, ms.value, fl.value

@@ -667,7 +667,7 @@ static ql_status validate_stack(const char* fn, const ql_stack_cfg* cfg, const v
 struct ProfRec {
   hipEvent_t a, b;
   int kernel;
-  double flop;
+  double work;  // FLOPs or bytes, by kernel id
 };
 static std::mutex g_prof_mu;
 static bool g_prof_on = false;
@@ -702,9 +702,9 @@ ql_status profile_begin(hipEvent_t* start, hipEvent_t* stop) {
   return QL_OK;
 }
 
-ql_status profile_end(hipEvent_t start, hipEvent_t stop, int kernel, double flop) {
+ql_status profile_end(hipEvent_t start, hipEvent_t stop, int kernel, double work) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof.push_back(ProfRec{start, stop, kernel, flop});
+  g_prof.push_back(ProfRec{start, stop, kernel, work});
   return QL_OK;
 }
 
@@ -733,7 +733,7 @@ ql_status ql_profile_enable(int32_t on) {
   return QL_OK;
 }
 
-ql_status ql_profile_read(int32_t kernel, int64_t* launches, double* ms, double* flop) {
+ql_status ql_profile_read(int32_t kernel, int64_t* launches, double* ms, double* work) {
   clear_error();
   if (kernel < 0 || kernel >= QL_KERNEL_COUNT)
     return set_error(QL_ERR_ARG, "ql_profile_read: kernel (%d) out of range", kernel);
@@ -747,11 +747,11 @@ ql_status ql_profile_read(int32_t kernel, int64_t* launches, double* ms, double*
     QL_HIP_CHECK(hipEventElapsedTime(&e, r.a, r.b));
     ++n;
     t += e;
-    f += r.flop;
+    f += r.work;
   }
   if (launches) *launches = n;
   if (ms) *ms = t;
-  if (flop) *flop = f;
+  if (work) *work = f;
   return QL_OK;
 }
 

@@ -27,6 +27,8 @@
 // A split writes float32 partials that a second kernel adds in split order.
 // Every sum has a fixed order, so equal inputs give equal bits. One launch can
 // carry several independent problems (all LoRA gradients of a layer).
+#include <hip/hip_ext.h>
+
 #include "ql_internal.h"
 
 namespace ql {
@@ -525,8 +527,44 @@ ql_status check_row(const RowProb& P) {
 }
 
 template <int NCG, int MODE>
-void launch_rowc_t(const RowArgs& a, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_rowc<NCG, MODE>), dim3(grid), dim3(64 * RC_WAVES), 0, st, a);
+void launch_rowc_t(const RowArgs& a, unsigned grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  hipExtLaunchKernelGGL((k_rowc<NCG, MODE>), dim3(grid), dim3(64 * RC_WAVES), 0, st, e0, e1, 0, a);
+}
+
+// Bytes a row launch must move once: its operand streams, the SwiGLU values
+// it stores, Bt, the outputs, and the float32 partials of a split (written
+// and read back).
+double rowc_bytes(const RowArgs& a) {
+  double b = 0;
+  for (int i = 0; i < a.nprob; ++i) {
+    const RowProb& P = a.p[i];
+    if (P.M <= 0) continue;
+    const double M = (double)P.M, K = (double)P.K, np = (double)(P.r * P.nseg);
+    const double xcols = P.n_rep > 0 ? K / P.n_rep : K;
+    const int nin = a.mode == 0 ? 1 : (a.mode == 1 ? 2 : 3), nout = a.mode;
+    b += 2.0 * M * xcols * nin + 2.0 * M * K * nout + 2.0 * np * K + 2.0 * M * np;
+    if (P.nsplit > 1) b += 8.0 * P.nsplit * M * np;
+  }
+  return b;
+}
+
+// The same for a column launch: Z, V, the outputs (read too when
+// accumulating), split partials; zero outputs of problems without rows.
+double colc_bytes(const ColArgs& a) {
+  double b = 0;
+  for (int i = 0; i < a.nprob; ++i) {
+    const ColProb& P = a.p[i];
+    const double nout = (double)P.C * P.r * P.nseg;
+    if (P.M <= 0) {
+      if (!P.accumulate) b += 4.0 * nout;
+      continue;
+    }
+    const double M = (double)P.M, C = (double)P.C;
+    const double zcols = P.n_rep > 0 ? C / P.n_rep : C;
+    b += 2.0 * M * zcols + 2.0 * M * P.r * P.nseg + 4.0 * nout * (P.accumulate ? 2 : 1);
+    if (P.nsplit > 1) b += 8.0 * P.nsplit * nout;
+  }
+  return b;
 }
 
 }  // namespace
@@ -591,34 +629,40 @@ ql_status launch_rowc(RowArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
   if (off > ws_bytes) return set_error(QL_ERR_WORKSPACE, "row contraction: workspace %zu < %zu", ws_bytes, off);
   if (tiles == 0) return QL_OK;
   const unsigned grid = (unsigned)tiles;
+  // timing events span the launch and its second pass
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  const bool prof = profiling_on();
+  if (prof) QL_TRY(profile_begin(&e0, &e1));
+  hipEvent_t e1m = rtiles > 0 ? nullptr : e1;
   if (a.mode == 0) {
     switch (ncg) {
-      case 1: launch_rowc_t<1, 0>(a, grid, st); break;
-      case 2: launch_rowc_t<2, 0>(a, grid, st); break;
-      case 3: launch_rowc_t<3, 0>(a, grid, st); break;
-      case 4: launch_rowc_t<4, 0>(a, grid, st); break;
+      case 1: launch_rowc_t<1, 0>(a, grid, st, e0, e1m); break;
+      case 2: launch_rowc_t<2, 0>(a, grid, st, e0, e1m); break;
+      case 3: launch_rowc_t<3, 0>(a, grid, st, e0, e1m); break;
+      case 4: launch_rowc_t<4, 0>(a, grid, st, e0, e1m); break;
       default: return set_error(QL_ERR_UNSUPPORTED, "row contraction: %d column groups", ncg);
     }
   } else if (a.mode == 1) {
     switch (ncg) {
-      case 1: launch_rowc_t<1, 1>(a, grid, st); break;
-      case 2: launch_rowc_t<2, 1>(a, grid, st); break;
-      case 3: launch_rowc_t<3, 1>(a, grid, st); break;
-      case 4: launch_rowc_t<4, 1>(a, grid, st); break;
+      case 1: launch_rowc_t<1, 1>(a, grid, st, e0, e1m); break;
+      case 2: launch_rowc_t<2, 1>(a, grid, st, e0, e1m); break;
+      case 3: launch_rowc_t<3, 1>(a, grid, st, e0, e1m); break;
+      case 4: launch_rowc_t<4, 1>(a, grid, st, e0, e1m); break;
       default: return set_error(QL_ERR_UNSUPPORTED, "row contraction: %d column groups", ncg);
     }
   } else {
     switch (ncg) {
-      case 2: launch_rowc_t<2, 2>(a, grid, st); break;
-      case 4: launch_rowc_t<4, 2>(a, grid, st); break;
+      case 2: launch_rowc_t<2, 2>(a, grid, st, e0, e1m); break;
+      case 4: launch_rowc_t<4, 2>(a, grid, st, e0, e1m); break;
       default: return set_error(QL_ERR_UNSUPPORTED, "row contraction: %d column groups", ncg);
     }
   }
   QL_HIP_CHECK(hipGetLastError());
   if (rtiles > 0) {
-    hipLaunchKernelGGL(k_rowc_reduce, dim3((unsigned)rtiles), dim3(256), 0, st, a);
+    hipExtLaunchKernelGGL(k_rowc_reduce, dim3((unsigned)rtiles), dim3(256), 0, st, nullptr, e1, 0, a);
     QL_HIP_CHECK(hipGetLastError());
   }
+  if (prof) QL_TRY(profile_end(e0, e1, QL_KERNEL_LORA_ROW, rowc_bytes(a)));
   return QL_OK;
 }
 
@@ -689,11 +733,17 @@ ql_status launch_colc(ColArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
     }
   }
   if (off > ws_bytes) return set_error(QL_ERR_WORKSPACE, "column contraction: workspace %zu < %zu", ws_bytes, off);
+  if (tiles == 0 && rtiles == 0) return QL_OK;
+  // timing events span the launch and its second pass
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  const bool prof = profiling_on();
+  if (prof) QL_TRY(profile_begin(&e0, &e1));
+  hipEvent_t e1m = rtiles > 0 ? nullptr : e1;
   if (tiles > 0) {
-#define QL_CC(n)                                                                                      \
-  case n:                                                                                             \
-    if (vec) hipLaunchKernelGGL((k_colc<n, true>), dim3((unsigned)tiles), dim3(256), 0, st, a);       \
-    else hipLaunchKernelGGL((k_colc<n, false>), dim3((unsigned)tiles), dim3(256), 0, st, a);          \
+#define QL_CC(n)                                                                                           \
+  case n:                                                                                                  \
+    if (vec) hipExtLaunchKernelGGL((k_colc<n, true>), dim3((unsigned)tiles), dim3(256), 0, st, e0, e1m, 0, a); \
+    else hipExtLaunchKernelGGL((k_colc<n, false>), dim3((unsigned)tiles), dim3(256), 0, st, e0, e1m, 0, a);    \
     break;
     switch (nj) {
       QL_CC(1) QL_CC(2) QL_CC(3) QL_CC(4)
@@ -703,9 +753,11 @@ ql_status launch_colc(ColArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
     QL_HIP_CHECK(hipGetLastError());
   }
   if (rtiles > 0) {
-    hipLaunchKernelGGL(k_colc_reduce, dim3((unsigned)rtiles), dim3(256), 0, st, a);
+    hipExtLaunchKernelGGL(k_colc_reduce, dim3((unsigned)rtiles), dim3(256), 0, st, tiles > 0 ? nullptr : e0, e1, 0,
+                          a);
     QL_HIP_CHECK(hipGetLastError());
   }
+  if (prof) QL_TRY(profile_end(e0, e1, QL_KERNEL_LORA_COL, colc_bytes(a)));
   return QL_OK;
 }
 

@@ -6,6 +6,8 @@
 // little-endian word: byte j of the word holds code j in its low nibble and
 // code j + 4 in its high nibble. (This order lets a decoder split a word into
 // two byte-lane index vectors with one mask and one shift each.)
+#include <hip/hip_ext.h>
+
 #include "ql_internal.h"
 
 namespace ql {
@@ -123,13 +125,18 @@ ql_status launch_nf4_dequant(const uint8_t* packed, const float* absmax, int64_t
   if (ngroups == 0) return QL_OK;
   int64_t grid = (ngroups + 255) / 256;
   if (grid > 256 * 64) grid = 256 * 64;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  const bool prof = profiling_on();
+  if (prof) QL_TRY(profile_begin(&e0, &e1));
   if (out_f32)
-    hipLaunchKernelGGL(k_nf4_dequant<true>, dim3((unsigned)grid), dim3(256), 0, st,
-                       (const uint32_t*)packed, absmax, ngroups, out);
+    hipExtLaunchKernelGGL(k_nf4_dequant<true>, dim3((unsigned)grid), dim3(256), 0, st, e0, e1, 0,
+                          (const uint32_t*)packed, absmax, ngroups, out);
   else
-    hipLaunchKernelGGL(k_nf4_dequant<false>, dim3((unsigned)grid), dim3(256), 0, st,
-                       (const uint32_t*)packed, absmax, ngroups, out);
+    hipExtLaunchKernelGGL(k_nf4_dequant<false>, dim3((unsigned)grid), dim3(256), 0, st, e0, e1, 0,
+                          (const uint32_t*)packed, absmax, ngroups, out);
   QL_HIP_CHECK(hipGetLastError());
+  // codes and scales read once (0.5625 B per weight), the output written once
+  if (prof) QL_TRY(profile_end(e0, e1, QL_KERNEL_DEQUANT, (double)n * (0.5625 + (out_f32 ? 4.0 : 2.0))));
   return QL_OK;
 }
 

@@ -203,10 +203,11 @@ inline size_t bwd_partial_bytes(int64_t M, int64_t K) {
 
 ql_status launch_gemm_fwd(const FwdArgs& a, hipStream_t st);
 
-// Kernel timing (ql_profile_enable): brackets a launch with events when on.
+// Kernel timing (ql_profile_enable): brackets a launch with events when on;
+// work is FLOPs or bytes by kernel id.
 bool profiling_on();
 ql_status profile_begin(hipEvent_t* start, hipEvent_t* stop);
-ql_status profile_end(hipEvent_t start, hipEvent_t stop, int kernel, double flop);
+ql_status profile_end(hipEvent_t start, hipEvent_t stop, int kernel, double work);
 ql_status launch_gemm_bwd(const BwdArgs& a, hipStream_t st);
 
 // LoRA side products (lora.hip). Both contractions reduce in a fixed order

@@ -159,3 +159,12 @@ def test_double_quantised_store_is_the_pages_size():
     # and the block layout matches the oracle's
     for n in (1, 256, 1000, 917504):
         assert ql.nf4_dq_layout(n) == dq_oracle.block_layout(n)
+
+
+def test_profile_read_refuses_unknown_kernel_ids():
+    for k in (-1, 7):
+        with pytest.raises(ql.QlError) as e:
+            ql.ql_profile_read(k)
+        assert e.value.status == ql.QL_ERR_ARG
+    n, ms, work = ql.ql_profile_read(ql.QL_KERNEL_DEQUANT)   # nothing recorded: zeros, no GPU work
+    assert n == 0 and ms == 0.0 and work == 0.0
