@@ -78,6 +78,19 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t n) {
   return xcd * q + (xcd < rem ? xcd : rem) + local;
 }
 
+// Coordinates of tile t of a tiles_m x tiles_n grid (dX). Consecutive tiles
+// (one XCD's share after xcd_remap) cover blocks of 4 M-tiles across several
+// column tiles, so each XCD's L2 fetches fewer distinct dY rows and weight rows
+// than with all M-tiles of one column block first (4-5% faster at the 8B
+// shapes; the forward keeps M-tiles first, which measured faster there).
+// tiles_m not a multiple of 4: M-tiles first.
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& mt, int& nt) {
+  const int gm = tiles_m % 4 == 0 ? 4 : tiles_m;
+  const int rb = t / (gm * tiles_n), u = t - rb * gm * tiles_n;
+  mt = rb * gm + u % gm;
+  nt = u / gm;
+}
+
 __device__ __forceinline__ int64_t remap_col(int64_t k, int head_dim, int n_rep) {
   if (n_rep <= 0) return k;
   const int64_t head = k / head_dim, i = k - head * head_dim;
@@ -635,8 +648,10 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
   // grid = tiles x nsplit; split sp of a tile takes weight steps [WS sp / S, WS (sp + 1) / S)
   const int gt = (int)xcd_remap(blockIdx.x, (uint32_t)(tiles_total * a.nsplit));
   const int sp = gt / tiles_total, tile = gt % tiles_total;
-  const int64_t m0 = (int64_t)(tile % tiles_m) * BM;
-  const int64_t k0 = (int64_t)k_base + (int64_t)(tile / tiles_m) * BN;
+  int mt, nt;
+  tile_coords(tile, tiles_m, tiles_total / tiles_m, mt, nt);
+  const int64_t m0 = (int64_t)mt * BM;
+  const int64_t k0 = (int64_t)k_base + (int64_t)nt * BN;
   const int64_t K = a.K, kbn = K / 64, M = a.M;
   const int64_t xrows = M - m0 < BM ? M - m0 : BM;
   const int nseg = a.nseg;
