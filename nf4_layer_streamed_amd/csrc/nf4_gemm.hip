@@ -1181,7 +1181,13 @@ ql_status launch_gemm_bwd(const BwdArgs& a_in, hipStream_t st) {
     if (S > cap) S = cap;
     int ws = 0;
     for (int s = 0; s < a.nseg; ++s) ws += (int)((a.seg[s].N + BK - 1) / BK);
-    while (S > 1 && ws < 64 * S) --S;  // shorter slices lose more to the partial pass than they gain
+    // Minimum weight steps per split (measured): when narrow tiles alone
+    // would fill the chip, a split must beat them, which takes about 32 steps
+    // per slice (the o dX at M=2048: 90 us split in two against 99 us narrow;
+    // the v dX, 16 steps, loses); otherwise more workgroups win down to about
+    // 4 steps per slice (M=512: o dX 37 us at 8 splits, 84 us narrow).
+    const int min_steps = t128 >= C ? 32 : 4;
+    while (S > 1 && ws < min_steps * S) --S;
     while (S > 1 && (size_t)S * (size_t)a.M * (size_t)a.K * 4 > a.partial_bytes) --S;
     if (S > 1) {
       a.nsplit = S;
