@@ -587,14 +587,21 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
 
 // =============================================================== backward dX
 // LDS B tile: [64 reduction rows n][BN output columns k] bf16, rows of 2 BN
-// bytes; the 16-B chunk index is XORed (low 3 bits) with f(n) so that both the
-// row-chunk writes and the transposed 4-row reads are bank-conflict free.
-__device__ __forceinline__ int swz_f(int n) { return ((n & 3) << 1) | ((n >> 2) & 1); }
+// bytes (a multiple of 256, so every row starts at bank 0). The LDS serves
+// 256 B (64 banks) per clock, so conflict-free means 16 distinct 16-B chunk
+// slots mod 16 among the lanes served together:
+// - a 16-B row-chunk write (16 lanes: 16 consecutive rows, one chunk) gets
+//   slot bits 0-2 from n mod 8 and bit 3 from n bit 3;
+// - a transposed 8-B read (32 lanes: rows 4a..4a+3, chunks 4b..4b+3) gets
+//   bits 1-2 from n mod 4, bit 0 from the chunk, and bit 3 from chunk bit 1.
+// The XOR term depends on the chunk only through bit 1, which it leaves
+// unchanged, so each row's chunks stay a permutation.
+__device__ __forceinline__ int swz_f(int n) { return ((n & 3) << 1) | ((n >> 2) & 1) | (((n >> 3) & 1) << 3); }
 
 template <int BN>
 __device__ __forceinline__ int bt_off(int n, int k) {
   const int chunk = k >> 3;
-  return n * (BN * 2) + ((chunk ^ swz_f(n)) << 4) + ((k & 4) << 1);
+  return n * (BN * 2) + ((chunk ^ swz_f(n) ^ (((chunk >> 1) & 1) << 3)) << 4) + ((k & 4) << 1);
 }
 
 // Raw weight data of one reduction step in LDS: the codes of 64 rows x BN
