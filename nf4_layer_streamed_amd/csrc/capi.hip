@@ -305,6 +305,8 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
   {  // q | k | v in one launch
     FwdArgs a{};
     a.X = S(QL_SAVED_N1); a.M = M; a.K = H; a.ldx = H; a.r = r; a.s = s; a.nseg = 3;
+    a.partial = (float*)(ws + WS.partial);
+    a.partial_bytes = WS.partial_bytes;
     const int outs[3] = {QL_SAVED_Q, QL_SAVED_K, QL_SAVED_V};
     for (int p = 0; p < 3; ++p) {
       FwdSeg& g = a.seg[p];
@@ -327,6 +329,8 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     FwdArgs a{};
     a.X = S(QL_SAVED_V); a.M = M; a.K = H; a.ldx = KV; a.head_dim = c->head_dim; a.n_rep = n_rep;
     a.r = r; a.s = s; a.nseg = 1;
+    a.partial = (float*)(ws + WS.partial);
+    a.partial_bytes = WS.partial_bytes;
     FwdSeg& g = a.seg[0];
     g.packed = W.packed[QL_PROJ_O]; g.absmax = W.absmax[QL_PROJ_O];
     g.U = on ? S(QL_SAVED_U0 + QL_PROJ_O) : nullptr; g.B = on ? u16(lo[QL_PROJ_O].B) : nullptr;

@@ -326,7 +326,13 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
   // head / n_rep) so the loop has no divisions or branches.
   const int hd = a.n_rep > 0 ? a.head_dim : (1 << 30);
   const int nrep = a.n_rep > 0 ? a.n_rep : 1;
-  int ci = ks0 * BK, hr = 0, hq = 0;  // a split starts at column ks0 BK (splits never use the remap)
+  int ci, hr, hq;  // of the slice's first step, K-step ks0
+  {
+    const int k0 = ks0 * BK, head = k0 / hd;
+    ci = k0 - head * hd;
+    hr = head % nrep;
+    hq = head / nrep;
+  }
   auto xcol_next = [&]() -> int {
     const int c = 2 * (hq * hd + ci);
     ci += BK;
@@ -549,6 +555,9 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
     }
   }
 
+  // Partials of a split reduction: per segment, nsplit blocks of [M x N]
+  // float32 after those of the earlier segments.
+  const int64_t ppart = (int64_t)a.nsplit * M * ((sg >= 1 ? a.seg[0].N : 0) + (sg >= 2 ? a.seg[1].N : 0));
   // Epilogue. The products above are C = W X^T (the weight operand first), so
   // lane (li, g) of accumulator [i][j] holds output row m = m0 + 32 i + li and,
   // in entries 4 v .. 4 v + 3, the four consecutive columns
@@ -566,8 +575,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
         if (n >= N) continue;
         const int64_t o = m * S.ldo + S.col0 + n;
         float f[4] = {acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]};
-        if (a.nsplit > 1) {  // float32 partial of this split ([M x N], ldo == N); the sum kernel finishes
-          *(float4*)(a.partial + (int64_t)sp * M * N + o) = make_float4(f[0], f[1], f[2], f[3]);
+        if (a.nsplit > 1) {  // float32 partial of this split; the sum kernel finishes
+          *(float4*)(a.partial + ppart + ((int64_t)sp * M + m) * N + n) = make_float4(f[0], f[1], f[2], f[3]);
           continue;
         }
         if (S.resid) {
@@ -1043,6 +1052,50 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ p, 
   }
 }
 
+// Sum of a forward split reduction, per segment: out[m][col0 + n] = sum over
+// splits in order of the float32 partials (+ the bf16 residual, same layout
+// as out). grid: x over 4-column groups, y over rows, z over segments.
+struct SumSeg {
+  const float* p;  // [nsplit][M x N]
+  void* out;
+  const uint16_t* resid;
+  int64_t N, ldo, col0;
+};
+struct SumArgs {
+  SumSeg seg[kMaxSegs];
+  int64_t M;
+  int32_t nsplit, out_f32;
+};
+__global__ __launch_bounds__(256) void k_split_sum_segs(const SumArgs a) {
+  const int z = blockIdx.z;
+  const SumSeg S = z == 0 ? a.seg[0] : (z == 1 ? a.seg[1] : a.seg[2]);
+  const int64_t n4 = S.N / 4, MN = a.M * S.N;
+  for (int64_t m = blockIdx.y; m < a.M; m += gridDim.y) {
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n4; c += (int64_t)gridDim.x * blockDim.x) {
+      const int64_t pi = m * S.N + 4 * c, o = m * S.ldo + S.col0 + 4 * c;
+      float4 f = *(const float4*)(S.p + pi);
+      for (int sp = 1; sp < a.nsplit; ++sp) {
+        const float4 q = *(const float4*)(S.p + sp * MN + pi);
+        f.x += q.x;
+        f.y += q.y;
+        f.z += q.z;
+        f.w += q.w;
+      }
+      if (S.resid) {
+        const uint2 rv = *(const uint2*)(S.resid + o);
+        f.x += __builtin_bit_cast(float, rv.x << 16);
+        f.y += __builtin_bit_cast(float, rv.x & 0xffff0000u);
+        f.z += __builtin_bit_cast(float, rv.y << 16);
+        f.w += __builtin_bit_cast(float, rv.y & 0xffff0000u);
+      }
+      if (a.out_f32)
+        *(float4*)((float*)S.out + o) = f;
+      else
+        *(uint2*)((uint16_t*)S.out + o) = make_uint2(pack_bf16x2(f.x, f.y), pack_bf16x2(f.z, f.w));
+    }
+  }
+}
+
 // Launch geometry. Tiles are 256 x 256 (wide) or 256 x 128 (narrow); the chip
 // runs cu_count workgroups per round. A narrow tile does half a wide tile's
 // work but runs at a lower rate: it takes about kNarrowFwd (kNarrowBwd for dX)
@@ -1055,6 +1108,10 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ p, 
 // narrow instead of 4 wide). The geometry depends on shapes only, so resident
 // and streamed runs pick the same kernels.
 constexpr double kNarrowFwd = 0.7, kNarrowBwd = 0.85;
+// Minimum K-steps per forward split slice when narrow tiles alone would fill
+// the chip (measured: the 4096 x 4096 forward at M=2048 runs 84 us split in
+// two, 32 steps each, against 86 us on narrow tiles).
+constexpr int kFwdMinSteps = 32;
 // 1 if re-cutting t wide tiles (t <= C) into tn narrow ones takes less time.
 int narrow_pays(int t, int tn, int C, double ratio) {
   const int wide_rounds = (t + C - 1) / C, narrow_rounds = (tn + C - 1) / C;
@@ -1072,26 +1129,37 @@ ql_status launch_gemm_fwd(const FwdArgs& a_in, hipStream_t st) {
     t256 += tiles_m * (int)((a.seg[s].N + 255) / 256);
     t128 += tiles_m * (int)((a.seg[s].N + 127) / 128);
   }
-  // split reduction (the dX GEMM's rule): one plain segment writing a
-  // contiguous [M x N] bf16 output, wide tiles that would leave half the chip
-  // idle, at least 64 K-steps per split
-  const FwdSeg& s0 = a.seg[0];
-  if (a.partial && a.nseg == 1 && a.n_rep == 0 && !a.out_f32 && s0.col0 == 0 && s0.ldo == s0.N &&
-      2 * t256 <= C) {
+  // Split reduction over K when wide tiles would leave at least half the chip
+  // idle and the caller gave space for partials: up to 8 workgroups per tile,
+  // with at least kFwdMinSteps K-steps per slice when narrow tiles alone
+  // would fill the chip (a split must then beat them), else at least 4
+  // (M=512: the 8B down forward 73 us split against 127, k 31 against 69).
+  if (a.partial && 2 * t256 <= C) {
     int S = C / t256;
-    const int cap = bwd_max_split(a.M, s0.N);
-    if (S > cap) S = cap;
+    if (S > 8) S = 8;
     const int kt = (int)(a.K / BK);
-    while (S > 1 && kt < 64 * S) --S;
-    while (S > 1 && (size_t)S * (size_t)a.M * (size_t)s0.N * 4 > a.partial_bytes) --S;
+    const int min_steps = t128 >= C ? kFwdMinSteps : 4;
+    while (S > 1 && kt < min_steps * S) --S;
+    int64_t ntot = 0;
+    for (int s = 0; s < a.nseg; ++s) ntot += a.seg[s].N;
+    while (S > 1 && (size_t)S * (size_t)a.M * (size_t)ntot * 4 > a.partial_bytes) --S;
     if (S > 1) {
       a.nsplit = S;
       QL_TRY_PROF(launch_fwd_tiles(a, true, st));
-      const int64_t MN = a.M * s0.N;
-      int64_t grid = (MN / 4 + 255) / 256;
-      if (grid > 4096) grid = 4096;
-      hipLaunchKernelGGL(k_split_sum, dim3((unsigned)grid), dim3(256), 0, st, (const float*)a.partial, S, MN,
-                         s0.resid, (void*)s0.out, 0);
+      SumArgs sa{};
+      sa.M = a.M;
+      sa.nsplit = S;
+      sa.out_f32 = a.out_f32;
+      int64_t off = 0, nmax = 0;
+      for (int s = 0; s < a.nseg; ++s) {
+        const FwdSeg& G = a.seg[s];
+        sa.seg[s] = SumSeg{a.partial + off, G.out, G.resid, G.N, G.ldo, G.col0};
+        off += (int64_t)S * a.M * G.N;
+        nmax = G.N > nmax ? G.N : nmax;
+      }
+      const int gx = (int)((nmax / 4 + 255) / 256);
+      const int gy = (int)(a.M < 1024 ? a.M : 1024);
+      hipLaunchKernelGGL(k_split_sum_segs, dim3(gx, gy, a.nseg), dim3(256), 0, st, sa);
       QL_HIP_CHECK(hipGetLastError());
       return QL_OK;
     }
@@ -1167,10 +1235,8 @@ int bwd_max_split(int64_t M, int64_t K) {
 
 // Geometry. When 256 x 256 tiles alone would leave at least half the chip idle
 // and the caller gave space for partials, the reduction is split across up to
-// 8 workgroups per tile (each split keeps at least 64 weight steps: whole-call
-// timings at M = 2048 show 8B gate|up dX, 448 steps, 6% faster split in two,
-// while the 64- and 16-step o and v dX lose to the partial pass) and a second
-// kernel sums the partials. Otherwise the forward's rule: whole rounds
+// 8 workgroups per tile (the minimum slice depth below) and a second kernel
+// sums the partials. Otherwise the forward's rule: whole rounds
 // on wide tiles, the column blocks of a last partial round on narrow tiles in
 // a second launch. Shapes alone decide, so resident and streamed runs match.
 ql_status launch_gemm_bwd(const BwdArgs& a_in, hipStream_t st) {

@@ -155,10 +155,10 @@ struct FwdArgs {
   int32_t out_f32;
   int32_t nseg;
   FwdSeg seg[kMaxSegs];
-  // Split reduction over K (set by launch_gemm_fwd; one segment, no column
-  // remap, contiguous [M x N] output): nsplit > 1 workgroups per tile write
-  // float32 partials [nsplit][M x N] that a second kernel sums in split
-  // order with the residual. partial / partial_bytes: the caller's space.
+  // Split reduction over K (set by launch_gemm_fwd): nsplit > 1 workgroups
+  // per tile write float32 partials, per segment [nsplit][M x N] after the
+  // earlier segments' blocks, that a second kernel sums in split order with
+  // the residual into out. partial / partial_bytes: the caller's space.
   float* partial;
   size_t partial_bytes;
   int32_t nsplit;
