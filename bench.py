@@ -42,6 +42,11 @@ the whole step (M tokens per step). The JSON line also carries:
   double-quantised (nf4_double_quant; the pages' 3.60 GB form of this store).
 * small_stack_graph - the launch-bound SmolLM2-shaped stack: eager steps
   against the same step captured once into a HIP graph and replayed.
+* qwen3b_stack - the Qwen2.5-3B-shaped streamed stack at M = 512 (PCIe-bound
+  like the 8B stack): tok/s, its H2D rate and the tok/s 64 GB/s would allow.
+* llama8b_layer_m512 - one 8B-shaped layer's seven projections, resident, at
+  M = 512 through the single-linear calls: layer time and TFLOP/s, and the
+  fused GEMMs' FLOP-weighted rate against the bf16 peak.
 * resident - the same step with the store resident in HBM (no copies).
 * cpu_baseline - the CPU oracle timed on a bounded sample.
 """
@@ -204,6 +209,104 @@ def small_stack_graph(ql, synth, torch, dev, steps=20, warmup=3):
     return dict(workload="smollm2_stack: 30 layers, hidden 576, intermediate 1536, kv 192, r8, M=512, streamed",
                 eager=dict(value=round(M / te, 1), ms_per_step=round(1000 * te, 3)),
                 graph=dict(value=round(M / tg, 1), ms_per_step=round(1000 * tg, 3)), unit="tok/s")
+
+
+def qwen3b_stack(ql, synth, torch, dev, steps=10, warmup=2):
+    """The Qwen2.5-3B-shaped streamed stack (36 layers, hidden 2048,
+    intermediate 11008, kv 256, M = 512): tok/s of the streamed step, its H2D
+    rate, and the tok/s that 64 GB/s of PCIe would allow for its copies."""
+    w = synth.WORKLOADS["qwen3b_stack"]
+    M, L = w["M"], w["L"]
+    cfg, store, offs, lora, x, dy = build_inputs(ql, synth, torch, w, dev)
+    rec = offs[1]
+    slots_b, saved_b, ws_b = ql.stream_layer_stack_workspace(cfg, M)
+    slots = torch.empty(slots_b, dtype=torch.uint8, device=dev)
+    saved = torch.empty(saved_b, dtype=torch.uint8, device=dev)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    y = torch.empty(M, w["H"], dtype=torch.bfloat16, device=dev)
+    dx = torch.empty_like(y)
+    dA = [{p: torch.empty(w["r"], cfg.proj_shape(p)[1], device=dev) for p in ql.PROJ} for _ in range(L)]
+    dB = [{p: torch.empty(cfg.proj_shape(p)[0], w["r"], device=dev) for p in ql.PROJ} for _ in range(L)]
+    compute, copy = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+
+    def step(turnaround):
+        ql.stream_layer_stack_fwd(cfg, store, lora, x, M, y, saved, slots, ws, compute, copy,
+                                  reuse_bwd_slots=int(turnaround))
+        ql.stream_layer_stack_bwd(cfg, store, lora, dy, M, saved, dx, dA, dB, 0, 1, slots, ws, compute, copy)
+
+    for i in range(warmup):
+        step(i > 0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / steps
+    copies = 2 * (L - cfg.n_buffers)
+    return dict(workload="qwen3b_stack: 36 layers, hidden 2048, intermediate 11008, kv 256, r16, M=512, streamed",
+                value=round(M / t, 1), unit="tok/s", ms_per_step=round(1000 * t, 3), copies_per_step=copies,
+                record_bytes=int(rec), pcie_GBs=round(copies * rec / t / 1e9, 2),
+                pcie_bound_tok_s=round(M / (copies * rec / (PCIE_PEAK_GBS * 1e9)), 1))
+
+
+def llama8b_layer_m512(ql, synth, torch, dev, reps=10):
+    """One Llama-3.1-8B-shaped layer's seven projections, resident, at M = 512
+    (batch 1, seq 512): each projection's forward and backward through
+    qlora_linear_fwd / qlora_linear_bwd on its own seeded x and dY. The whole
+    layer's time and FLOP rate, and the fused GEMMs' FLOP-weighted rate from
+    the library's kernel timing, against the bf16 peak."""
+    w = synth.WORKLOADS["llama8b_layer"]
+    M, H, I, KV, r, alpha = (w[k] for k in ("M", "H", "I", "KV", "r", "alpha"))
+    projs, flop, wsb = [], 0, 0
+    for p in synth.PROJ:
+        N, K = synth.proj_shape(p, H, I, KV)
+        packed, absmax = synth.nf4_store(N * K, "llama8b_layer", p, device=dev)
+        inp = synth.linear_inputs(M, K, N, r, ("llama8b_layer", p), device=dev)
+        del inp["W"]
+        W = ql.NF4Weight(packed, absmax, N, K)
+        Lr = ql.Lora(inp["A"], inp["B"], r, alpha)
+        fw, bw = ql.qlora_linear_workspace(M, N, K, r)
+        wsb = max(wsb, fw, bw)
+        bufs = dict(y=torch.empty(M, N, dtype=torch.bfloat16, device=dev),
+                    U=torch.empty(M, r, dtype=torch.bfloat16, device=dev),
+                    dx=torch.empty(M, K, dtype=torch.bfloat16, device=dev),
+                    dA=torch.empty(r, K, device=dev), dB=torch.empty(N, r, device=dev))
+        projs.append((W, Lr, inp, bufs))
+        # fwd: x W^T, U = x A^T, U B^T; bwd: dX = dY W, G = dY B, G A; dA = G^T x, dB = dY^T U
+        flop += 2 * M * N * K + 2 * M * K * r + 2 * M * r * N
+        flop += 2 * M * N * K + 2 * M * N * r + 2 * M * r * K + 2 * r * M * K + 2 * N * M * r
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def layer():
+        for W, Lr, inp, b in projs:
+            ql.qlora_linear_fwd(inp["x"], M, W, Lr, b["y"], b["U"], ws)
+            ql.qlora_linear_bwd(inp["dy"], inp["x"], b["U"], M, W, Lr, b["dx"], b["dA"], b["dB"], 0, ws)
+
+    for _ in range(2):
+        layer()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        layer()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    ql.ql_profile_enable(1)
+    layer()
+    torch.cuda.synchronize()
+    ql.ql_profile_enable(0)
+    gms, gfl = 0.0, 0.0
+    for k in (ql.QL_KERNEL_GEMM_FWD, ql.QL_KERNEL_GEMM_BWD, ql.QL_KERNEL_GEMM_FWD_NARROW, ql.QL_KERNEL_GEMM_BWD_NARROW):
+        _, kms, kfl = ql.ql_profile_read(k)
+        gms += kms
+        gfl += kfl
+    g_tf = gfl / (gms * 1e-3) / 1e12
+    return dict(workload="llama8b_layer: q, k, v, o, gate, up, down of one 8B-shaped layer, r16 alpha32, M=512, "
+                         "resident, each on its own x and dY",
+                ms_per_layer=round(1000 * t, 3), layer_flop=int(flop), tflops=round(flop / t / 1e12, 1),
+                gemm=dict(tflops=round(g_tf, 1), frac=round(g_tf / MFMA_BF16_PEAK_TFLOPS, 4), ms=round(gms, 3)),
+                unit="TFLOP/s")
 
 
 def dense_gemm_ceiling(torch, dev, M, w, reps=10):
@@ -446,7 +549,7 @@ def main():
                 same_session_h2d_GBs=round(h2d_ceiling, 2), bytes_per_step=h2d_bytes,
                 copies_per_step=copies, record_bytes=rec)
 
-    ring8 = with_ref = recompute = double_quant = small = dense = None
+    ring8 = with_ref = recompute = double_quant = small = qwen = layer512 = dense = None
     if not args.main_only:
         # the same step with a deeper slot ring (the docs' stream_buffers up to 8):
         # each turnaround reuses 8 layers, so 2 (L - 8) copies per step
@@ -522,6 +625,10 @@ def main():
 
         log("bench: SmolLM2-shaped stack, eager and captured steps")
         small = small_stack_graph(ql, synth, torch, dev)
+        log("bench: Qwen2.5-3B-shaped stack")
+        qwen = qwen3b_stack(ql, synth, torch, dev)
+        log("bench: one 8B-shaped layer's projections at M=512")
+        layer512 = llama8b_layer_m512(ql, synth, torch, dev)
 
         dense = dense_gemm_ceiling(torch, dev, M, w)
         gemm_all["vs_dense_bf16"] = round(gemm_all["tflops"] / dense["tflops"], 4)
@@ -574,6 +681,8 @@ def main():
         "recompute": recompute,
         "double_quant": double_quant,
         "small_stack_graph": small,
+        "qwen3b_stack": qwen,
+        "llama8b_layer_m512": layer512,
         "resident": resident,
         "cpu_baseline": cpu,
     }
