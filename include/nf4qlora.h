@@ -217,7 +217,8 @@ ql_status qlora_linear_bwd(const void* dy, const void* x, const void* u_saved, i
  * may still read the slots), so successive calls may share the slots when
  * they use the same compute stream; with different compute streams the
  * caller orders the streams.
- * Host wait (streamed mode, not while the compute stream is capturing):
+ * Host wait (streamed mode with layer records of 8 MiB or more, not while
+ * the compute stream is capturing):
  * before it enqueues anything, a forward call (stream_layer_stack_fwd or
  * _fwd_ref) blocks the host until the previous streamed forward call on the
  * same device has finished on the GPU, and a backward call likewise for the
