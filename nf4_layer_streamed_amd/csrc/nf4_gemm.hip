@@ -1108,10 +1108,12 @@ __global__ __launch_bounds__(256) void k_split_sum_segs(const SumArgs a) {
 // narrow instead of 4 wide). The geometry depends on shapes only, so resident
 // and streamed runs pick the same kernels.
 constexpr double kNarrowFwd = 0.7, kNarrowBwd = 0.85;
-// Minimum K-steps per forward split slice when narrow tiles alone would fill
-// the chip (measured: the 4096 x 4096 forward at M=2048 runs 84 us split in
-// two, 32 steps each, against 86 us on narrow tiles).
-constexpr int kFwdMinSteps = 32;
+// Minimum K-steps per forward split slice when narrow tiles alone fill at
+// least half the chip, from whole calls (the GEMM and the sum of its
+// partials): the 4096 x 4096 forward at M=2048 takes 111 us split in two, 32
+// steps each, against 99 us on narrow tiles; the M=512 gate forward 97 us
+// split in two against 90.
+constexpr int kFwdMinSteps = 64;
 // 1 if re-cutting t wide tiles (t <= C) into tn narrow ones takes less time.
 int narrow_pays(int t, int tn, int C, double ratio) {
   const int wide_rounds = (t + C - 1) / C, narrow_rounds = (tn + C - 1) / C;
@@ -1131,14 +1133,16 @@ ql_status launch_gemm_fwd(const FwdArgs& a_in, hipStream_t st) {
   }
   // Split reduction over K when wide tiles would leave at least half the chip
   // idle and the caller gave space for partials: up to 8 workgroups per tile,
-  // with at least kFwdMinSteps K-steps per slice when narrow tiles alone
-  // would fill the chip (a split must then beat them), else at least 4
-  // (M=512: the 8B down forward 73 us split against 127, k 31 against 69).
+  // with at least kFwdMinSteps K-steps per slice when narrow tiles alone fill
+  // at least half the chip, else at least 8 (whole calls at M=512: the 8B
+  // down forward 95 us split against 141, k 43 against 76); reductions under
+  // 32 K-steps are not split.
   if (a.partial && 2 * t256 <= C) {
     int S = C / t256;
     if (S > 8) S = 8;
     const int kt = (int)(a.K / BK);
-    const int min_steps = t128 >= C ? kFwdMinSteps : 4;
+    const int min_steps = 2 * t128 >= C ? kFwdMinSteps : 8;
+    if (kt < 32) S = 1;
     while (S > 1 && kt < min_steps * S) --S;
     int64_t ntot = 0;
     for (int s = 0; s < a.nseg; ++s) ntot += a.seg[s].N;
@@ -1254,12 +1258,16 @@ ql_status launch_gemm_bwd(const BwdArgs& a_in, hipStream_t st) {
     if (S > cap) S = cap;
     int ws = 0;
     for (int s = 0; s < a.nseg; ++s) ws += (int)((a.seg[s].N + BK - 1) / BK);
-    // Minimum weight steps per split (measured): when narrow tiles alone
-    // would fill the chip, a split must beat them, which takes about 32 steps
-    // per slice (the o dX at M=2048: 90 us split in two against 99 us narrow;
-    // the v dX, 16 steps, loses); otherwise more workgroups win down to about
-    // 4 steps per slice (M=512: o dX 37 us at 8 splits, 84 us narrow).
-    const int min_steps = t128 >= C ? 32 : 4;
+    // Split depth, from whole calls (the GEMM and the sum of its partials).
+    // When narrow tiles alone fill at least half the chip, slices keep at
+    // least 64 weight steps: split in two, a 4096-column dX at M=2048 (64
+    // steps) takes 137-140 us against 132-135 on narrow tiles, and the M=512
+    // down dX 116 against 111. Otherwise slices keep at least 8 steps
+    // (M=512: the 4096 x 4096 dX 71 us at 8 splits against 103), and a
+    // reduction under 32 steps is not split (M=512 k dX: 44 us whole, 52 in
+    // four slices).
+    const int min_steps = 2 * t128 >= C ? 64 : 8;
+    if (ws < 32) S = 1;
     while (S > 1 && ws < min_steps * S) --S;
     while (S > 1 && (size_t)S * (size_t)a.M * (size_t)a.K * 4 > a.partial_bytes) --S;
     if (S > 1) {
