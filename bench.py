@@ -46,7 +46,11 @@ the whole step (M tokens per step). The JSON line also carries:
   like the 8B stack): tok/s, its H2D rate and the tok/s 64 GB/s would allow.
 * llama8b_layer_m512 - one 8B-shaped layer's seven projections, resident, at
   M = 512 through the single-linear calls: layer time and TFLOP/s, and the
-  fused GEMMs' FLOP-weighted rate against the bf16 peak.
+  fused GEMMs' FLOP-weighted rate against the bf16 peak and against torch's
+  dense bf16 GEMM at the same shapes.
+* hbm_copy_ceiling - a same-session device-to-device copy (2 GiB, 4 GiB
+  moved): the practical HBM rate next to the 8 TB/s the HBM kernels are
+  measured against.
 * resident - the same step with the store resident in HBM (no copies).
 * cpu_baseline - the CPU oracle timed on a bounded sample.
 """
@@ -302,21 +306,29 @@ def llama8b_layer_m512(ql, synth, torch, dev, reps=10):
         gms += kms
         gfl += kfl
     g_tf = gfl / (gms * 1e-3) / 1e12
+    del projs, ws
+    shapes = [synth.proj_shape(p, H, I, KV) for p in synth.PROJ]
+    dense = dense_gemm_ceiling(torch, dev, M, w, fwd=shapes, bwd=shapes,
+                               what="torch.mm bf16 (hipBLASLt), weights pre-dequantised in HBM, the seven "
+                                    "projections' fwd and dX shapes at M=512")
     return dict(workload="llama8b_layer: q, k, v, o, gate, up, down of one 8B-shaped layer, r16 alpha32, M=512, "
                          "resident, each on its own x and dY",
                 ms_per_layer=round(1000 * t, 3), layer_flop=int(flop), tflops=round(flop / t / 1e12, 1),
-                gemm=dict(tflops=round(g_tf, 1), frac=round(g_tf / MFMA_BF16_PEAK_TFLOPS, 4), ms=round(gms, 3)),
-                unit="TFLOP/s")
+                gemm=dict(tflops=round(g_tf, 1), frac=round(g_tf / MFMA_BF16_PEAK_TFLOPS, 4), ms=round(gms, 3),
+                          vs_dense_bf16=round(g_tf / dense["tflops"], 4)),
+                dense_bf16_gemm=dense, unit="TFLOP/s")
 
 
-def dense_gemm_ceiling(torch, dev, M, w, reps=10):
+def dense_gemm_ceiling(torch, dev, M, w, reps=10, fwd=None, bwd=None, what=None):
     """Same-session practical ceiling for the fused NF4 GEMMs: torch's dense
     bf16 GEMM (hipBLASLt) on weights that are already bf16 in HBM, over the
     stack's forward shapes (y = x W^T: q|k|v, o, gate|up, down) and dX shapes
-    (dX = dY W: v, o, gate|up, down), FLOP-weighted like one step's mix."""
+    (dX = dY W: v, o, gate|up, down), FLOP-weighted like one step's mix (or
+    over the given (N, K) lists)."""
     H, I, KV = w["H"], w["I"], w["KV"]
-    fwd = [(H + 2 * KV, H), (H, H), (2 * I, H), (H, I)]     # (N, K)
-    bwd = [(KV, H), (H, H), (2 * I, H), (H, I)]
+    if fwd is None:
+        fwd = [(H + 2 * KV, H), (H, H), (2 * I, H), (H, I)]     # (N, K)
+        bwd = [(KV, H), (H, H), (2 * I, H), (H, I)]
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     ops = []
@@ -342,7 +354,28 @@ def dense_gemm_ceiling(torch, dev, M, w, reps=10):
     tf = flop / (e0.elapsed_time(e1) * 1e-3) / 1e12
     del ops
     return dict(tflops=round(tf, 1), frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                what="torch.mm bf16 (hipBLASLt), weights pre-dequantised in HBM, stack fwd+dX shapes at M=%d" % M)
+                what=what or "torch.mm bf16 (hipBLASLt), weights pre-dequantised in HBM, stack fwd+dX shapes at M=%d" % M)
+
+
+def hbm_copy_ceiling(torch, dev, gib=2, reps=5):
+    """Same-session practical HBM ceiling: a device-to-device copy of a 2 GiB
+    buffer (4 GiB moved: read once, written once), GB/s of bytes moved."""
+    n = gib << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = reps * 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    return dict(GBs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4),
+                what="device-to-device copy of 2 GiB (4 GiB moved), torch copy_")
 
 
 def cpu_baseline(rows=2048, layers=3):
@@ -549,7 +582,7 @@ def main():
                 same_session_h2d_GBs=round(h2d_ceiling, 2), bytes_per_step=h2d_bytes,
                 copies_per_step=copies, record_bytes=rec)
 
-    ring8 = with_ref = recompute = double_quant = small = qwen = layer512 = dense = None
+    ring8 = with_ref = recompute = double_quant = small = qwen = layer512 = dense = hbm_copy = None
     if not args.main_only:
         # the same step with a deeper slot ring (the docs' stream_buffers up to 8):
         # each turnaround reuses 8 layers, so 2 (L - 8) copies per step
@@ -631,6 +664,7 @@ def main():
         layer512 = llama8b_layer_m512(ql, synth, torch, dev)
 
         dense = dense_gemm_ceiling(torch, dev, M, w)
+        hbm_copy = hbm_copy_ceiling(torch, dev)
         gemm_all["vs_dense_bf16"] = round(gemm_all["tflops"] / dense["tflops"], 4)
 
     resident = None
@@ -675,6 +709,7 @@ def main():
         "roofline": roofline,
         "hbm_kernels": hbm,
         "dense_bf16_gemm": dense,
+        "hbm_copy_ceiling": hbm_copy,
         "pcie": pcie,
         "ring8": ring8,
         "with_reference": with_ref,
