@@ -433,7 +433,7 @@ def main():
                          "small-stack / dense-GEMM lines), e.g. for counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: this benchmark runs on one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is a design note only)", file=sys.stderr)
         sys.exit(2)
 

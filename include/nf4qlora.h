@@ -62,7 +62,7 @@ enum {
   QL_ERR_NONFINITE = -5,   /* nf4_quantize met NaN or Inf */
   QL_ERR_WORKSPACE = -6,   /* a workspace or buffer is smaller than required */
   QL_ERR_HIP = -7,         /* a HIP runtime call failed */
-  QL_ERR_UNSUPPORTED = -8  /* a valid request this build does not implement */
+  QL_ERR_UNSUPPORTED = -8  /* a valid request this library does not implement */
 };
 
 enum { QL_BF16 = 0, QL_F32 = 1 };
