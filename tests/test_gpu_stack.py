@@ -343,6 +343,26 @@ def test_qwen3b_stack_full_size_sampled_rows():
     assert identical(got, s.results())
 
 
+def test_queued_steps_of_a_large_record_stack_equal_resident():
+    # Qwen2.5-3B widths, 4 layers: 43 MB records, so each streamed call first
+    # waits on the host for the previous call of its direction to finish on
+    # the GPU. Three training steps queued back to back (no synchronisation
+    # between the calls, slots reused at every turnaround) end bitwise equal
+    # to the resident step.
+    require_gpu()
+    s = GpuStack("qwen3b_stack", L=4, gen_device=DEV)
+    offs, _, _ = ql.stream_layer_stack_layout(s.cfg)
+    assert offs[1] >= 8 << 20
+    assert s.fwd() == ql.QL_OK
+    for _ in range(2):
+        assert s.bwd(reuse=True) == ql.QL_OK
+        assert s.fwd(reuse=True) == ql.QL_OK
+    assert s.bwd(reuse=True) == ql.QL_OK
+    streamed = s.results()
+    assert s.step(resident=True) == ql.QL_OK
+    assert identical(streamed, s.results())
+
+
 def test_llama8b_shapes_at_bench_launch_config_sampled_rows():
     # The 8B layer shapes at M = 2048 (the benchmark's launch configuration),
     # 4 layers so the oracle can follow sampled rows through the whole stack.
