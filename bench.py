@@ -48,6 +48,8 @@ the whole step (M tokens per step). The JSON line also carries:
   M = 512 through the single-linear calls: layer time and TFLOP/s, and the
   fused GEMMs' FLOP-weighted rate against the bf16 peak and against torch's
   dense bf16 GEMM at the same shapes.
+* linear_pr1 - the smallest configuration's single linear (M = 64, K = 256,
+  N = 512, r = 8): microseconds per forward and per backward call.
 * hbm_copy_ceiling - a same-session device-to-device copy (2 GiB, 4 GiB
   moved): the practical HBM rate next to the 8 TB/s the HBM kernels are
   measured against.
@@ -319,6 +321,38 @@ def llama8b_layer_m512(ql, synth, torch, dev, reps=10):
                 dense_bf16_gemm=dense, unit="TFLOP/s")
 
 
+def linear_pr1(ql, synth, torch, dev, reps=200):
+    """The single NF4 + LoRA linear of the smallest configuration (M = 64
+    tokens, K = 256, N = 512, r = 8, alpha = 16): microseconds per forward and
+    per backward call, back to back on one stream. Launch latency bounds it."""
+    M, K, N, r, alpha = 64, 256, 512, 8, 16.0
+    packed, absmax = synth.nf4_store(N * K, "linear_pr1", device=dev)
+    inp = synth.linear_inputs(M, K, N, r, ("linear_pr1",), device=dev)
+    W = ql.NF4Weight(packed, absmax, N, K)
+    L = ql.Lora(inp["A"], inp["B"], r, alpha)
+    fw, bw = ql.qlora_linear_workspace(M, N, K, r)
+    ws = torch.empty(max(fw, bw, 256), dtype=torch.uint8, device=dev)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    U = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    dA = torch.empty(r, K, device=dev)
+    dB = torch.empty(N, r, device=dev)
+    out = {}
+    for name, fn in (("fwd", lambda: ql.qlora_linear_fwd(inp["x"], M, W, L, y, U, ws)),
+                     ("bwd", lambda: ql.qlora_linear_bwd(inp["dy"], inp["x"], U, M, W, L, dx, dA, dB, 0, ws))):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_us"] = round(1000.0 * e0.elapsed_time(e1) / reps, 2)
+    return dict(workload="linear_pr1: M=64, K=256, N=512, r8 alpha16, one NF4 + LoRA linear", **out)
+
+
 def dense_gemm_ceiling(torch, dev, M, w, reps=10, fwd=None, bwd=None, what=None):
     """Same-session practical ceiling for the fused NF4 GEMMs: torch's dense
     bf16 GEMM (hipBLASLt) on weights that are already bf16 in HBM, over the
@@ -582,7 +616,7 @@ def main():
                 same_session_h2d_GBs=round(h2d_ceiling, 2), bytes_per_step=h2d_bytes,
                 copies_per_step=copies, record_bytes=rec)
 
-    ring8 = with_ref = recompute = double_quant = small = qwen = layer512 = dense = hbm_copy = None
+    ring8 = with_ref = recompute = double_quant = small = qwen = layer512 = pr1 = dense = hbm_copy = None
     if not args.main_only:
         # the same step with a deeper slot ring (the docs' stream_buffers up to 8):
         # each turnaround reuses 8 layers, so 2 (L - 8) copies per step
@@ -662,6 +696,7 @@ def main():
         qwen = qwen3b_stack(ql, synth, torch, dev)
         log("bench: one 8B-shaped layer's projections at M=512")
         layer512 = llama8b_layer_m512(ql, synth, torch, dev)
+        pr1 = linear_pr1(ql, synth, torch, dev)
 
         dense = dense_gemm_ceiling(torch, dev, M, w)
         hbm_copy = hbm_copy_ceiling(torch, dev)
@@ -718,6 +753,7 @@ def main():
         "small_stack_graph": small,
         "qwen3b_stack": qwen,
         "llama8b_layer_m512": layer512,
+        "linear_pr1": pr1,
         "resident": resident,
         "cpu_baseline": cpu,
     }
