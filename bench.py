@@ -54,6 +54,8 @@ the whole step (M tokens per step). The JSON line also carries:
   moved): the practical HBM rate next to the 8 TB/s the HBM kernels are
   measured against.
 * resident - the same step with the store resident in HBM (no copies).
+* step_ms - median / min / max of the timed steps (events on the compute
+  stream between steps); clocks_after - SCLK / MCLK from rocm-smi.
 * cpu_baseline - the CPU oracle timed on a bounded sample.
 """
 
@@ -412,6 +414,19 @@ def hbm_copy_ceiling(torch, dev, gib=2, reps=5):
                 what="device-to-device copy of 2 GiB (4 GiB moved), torch copy_")
 
 
+def gpu_clocks():
+    """Current SCLK / MCLK of GPU 0 as rocm-smi reports them (None when it is
+    unavailable)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "-d", "0", "--showclocks", "--json"], capture_output=True, text=True,
+                             timeout=20).stdout
+        card = next(iter(json.loads(out).values()))
+        return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()} or None
+    except Exception:
+        return None
+
+
 def cpu_baseline(rows=2048, layers=3):
     """The oracle on a bounded sample: the first `layers` layers of the 8B
     stack with all 2048 tokens (or `rows` of them), forward + backward in
@@ -505,18 +520,27 @@ def main():
                                        slots if streamed else None, ws, compute, copy)
         return max(s1, s2)
 
-    def timed(c, st, steps, warmup, profile):
+    step_ms = []
+
+    def timed(c, st, steps, warmup, profile, per_step=False):
         for i in range(warmup):
             step(c, st, i > 0)
         torch.cuda.synchronize()
         if profile:
             ql.ql_profile_enable(1)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)] if per_step else None
         t0 = time.perf_counter()
         status = 0
+        if per_step:
+            marks[0].record(compute)
         for i in range(steps):
             status = max(status, step(c, st, warmup > 0 or i > 0))
+            if per_step:
+                marks[i + 1].record(compute)
         torch.cuda.synchronize()
         t = time.perf_counter() - t0
+        if per_step:
+            step_ms[:] = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
         prof = None
         if profile:
             ql.ql_profile_enable(0)
@@ -524,7 +548,7 @@ def main():
         return t, status, prof
 
     log(f"bench: warmup {args.warmup}, timing {args.steps} streamed steps")
-    t, status, _ = timed(cfg, store, args.steps, args.warmup, False)
+    t, status, _ = timed(cfg, store, args.steps, args.warmup, False, per_step=True)
     ms = 1000.0 * t / args.steps
     value = M * args.steps / t
     # kernel durations come from a second pass of the same steps with the
@@ -725,6 +749,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
+        "step_ms": dict(median=round(sorted(step_ms)[len(step_ms) // 2], 3), min=round(min(step_ms), 3),
+                        max=round(max(step_ms), 3), what="GPU time between events on the compute stream") if step_ms else None,
+        "clocks_after": gpu_clocks(),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
