@@ -7,15 +7,15 @@
  * backward, and a decoder stack fed one layer at a time from pinned host
  * memory through two device buffers.
  *
- * Sources (the Soup pages): the frozen base streams from host RAM one decoder
- * layer at a time while only the LoRA adapter trains (Soup README intro,
+ * Sources (the Soup pages): the frozen base is held in host memory and fed to
+ * the GPU layer by layer, and the adapter is the only trained part (Soup README intro,
  * "Citing Soup"; blog "The trick: layer streaming"); it is stored as NF4,
  * quantised once offline, and dequantised on the fly per layer (soup-cli
  * 0.72.2 docs "NF4 streaming (quantization: 4bit)"); copies come from
  * page-locked memory into two pre-allocated device buffers so they overlap
  * compute, and a pageable store falls back with its cost reported (CHANGELOG
  * [0.72.0]; docs "Layer Streaming", "Honest scope" and "Troubleshooting");
- * streaming is a pure scheduling change, so a streamed run is bit-identical to
+ * streaming changes only when the bytes arrive, so a streamed run is bit-identical to
  * a resident one (blog "Why the evidence is better than usual"; CHANGELOG
  * [0.72.2] "Correctness"). The NF4 codebook, block size, scale format and
  * rounding are not on the pages; the library follows the QLoRA paper
@@ -31,8 +31,12 @@
  *    untouched. ql_last_error() then names the offending argument and rule.
  *  - Calls are asynchronous on the given stream(s) unless stated otherwise.
  *    Buffers must stay alive until the stream has passed the call.
- *  - The library never mutates its inputs and keeps no state between calls,
- *    except one 4-byte device flag per device used by nf4_quantize.
+ *  - The library never mutates its inputs and keeps no state between calls.
+ *    It allocates no device memory: nf4_quantize's finiteness flag is one
+ *    word in the library's code object on each device.
+ *  - Matrix dimensions (N, K; hidden, inter) are at most QL_MAX_DIM, so that
+ *    every per-row byte offset the kernels form fits in 32 bits; element
+ *    counts and the products N * K are unrestricted (64-bit).
  *  - The caller allocates every buffer (device memory, pinned host store,
  *    workspaces); the *_workspace / *_layout calls give the sizes.
  *  - Results are deterministic: no atomics take part in any reduction, and
@@ -56,7 +60,7 @@ enum {
      (docs "Layer Streaming": the pageable fallback runs and reports its cost). */
   QL_WARN_PAGEABLE_HOST = 1,
   QL_ERR_ARG = -1,         /* null pointer, bad enum, bad flag */
-  QL_ERR_SHAPE = -2,       /* K % 64, N % 16, negative sizes, mismatched shapes */
+  QL_ERR_SHAPE = -2,       /* K % 64, N % 16, negative sizes, a dimension above QL_MAX_DIM */
   QL_ERR_ALIGN = -3,       /* pointer not aligned as the call requires */
   QL_ERR_RANK = -4,        /* LoRA rank outside 1..64 (the pages refuse r < 1) */
   QL_ERR_NONFINITE = -5,   /* nf4_quantize met NaN or Inf */
@@ -66,6 +70,10 @@ enum {
 };
 
 enum { QL_BF16 = 0, QL_F32 = 1 };
+
+/* Largest matrix dimension (rows or columns of a weight, hidden and
+ * intermediate widths of a stack). */
+#define QL_MAX_DIM (1 << 21)
 
 /* A hipStream_t passed as an opaque pointer; NULL means the null stream. */
 typedef void* ql_stream;
@@ -91,9 +99,11 @@ ql_status nf4_codebook(float* out /* host [16] */);
  * "NF4 streaming": the base is quantised a tensor at a time, once, before
  * training).
  *   packed: uint8 [n/2], absmax: float32 [n/64]; all 16-byte aligned.
- * Non-finite input is refused with QL_ERR_NONFINITE. To detect it the call
- * waits for the stream to finish the kernel (it is synchronous). On
- * QL_ERR_NONFINITE the outputs hold unspecified values.
+ * Non-finite input is refused with QL_ERR_NONFINITE, and then nothing is
+ * written. To refuse it before any output is written, the call first scans w
+ * on the stream and waits for that scan (the one synchronous step of the
+ * library; host threads calling it concurrently take turns); the
+ * quantisation itself is then enqueued asynchronously like every other call.
  */
 ql_status nf4_quantize(const float* w, int64_t n, uint8_t* packed, float* absmax, ql_stream s);
 
@@ -137,7 +147,8 @@ ql_status nf4_dq_expand(const void* dq, int64_t nblocks, float* absmax, ql_strea
 typedef struct {
   const uint8_t* packed; /* uint8 [N*K/2] as written by nf4_quantize */
   const float* absmax;   /* float32 [N*K/64] */
-  int64_t N, K;          /* out-features, in-features; K % 64 == 0, N % 16 == 0 */
+  int64_t N, K;          /* out-features, in-features; K % 64 == 0, N % 16 == 0,
+                            both <= QL_MAX_DIM */
 } ql_nf4_weight;
 
 typedef struct {
@@ -157,8 +168,9 @@ ql_status qlora_linear_workspace(int64_t M, int64_t N, int64_t K, int32_t r,
  * with W = bf16(fl32(level * absmax)) dequantised inside the GEMM's tile
  * loader (never materialised) and float32 accumulation. s B is rounded to
  * bf16 as an MFMA operand (exact when s is a power of two).
- * Forward of the LoRA linear on the pages (blog: "only the LoRA adapter
- * actually trains"; docs "NF4 streaming": NF4 dequantised on the fly).
+ * Forward of the LoRA linear on the pages: the quantised base is frozen and
+ * the adapter is the trained part (blog, "The trick: layer streaming"); the
+ * NF4 weights are decoded on the fly (docs "NF4 streaming").
  *   x: bf16 [M x K]; M >= 0 (M == 0 is a no-op); 16-byte aligned pointers.
  *   ws: device workspace of at least fwd_bytes from qlora_linear_workspace.
  */
@@ -170,9 +182,9 @@ ql_status qlora_linear_fwd(const void* x, int64_t M, ql_nf4_weight W, ql_lora L,
  *   dX = bf16(dY W + s G A)            -> dx, bf16 [M x K]; skipped if dx == NULL
  *   dB = s dY^T U                      -> dB, float32 [N x r]
  *   dA = s G^T x                       -> dA, float32 [r x K]
- * There is no gradient for the frozen W (blog: "only the LoRA adapter actually
- * trains"). With accumulate != 0, dA and dB are added to their current values
- * (float32), else overwritten. Reductions over M use a fixed order.
+ * There is no gradient for the frozen W: only the adapter trains (blog, "The
+ * trick: layer streaming"). With accumulate != 0, dA and dB are added to
+ * their current values (float32), else overwritten. Reductions over M use a fixed order.
  *   u_saved: the U written by qlora_linear_fwd for the same x.
  *   ws: device workspace of at least bwd_bytes from qlora_linear_workspace.
  */
@@ -200,7 +212,7 @@ ql_status qlora_linear_bwd(const void* dy, const void* x, const void* u_saved, i
  * Resident mode (resident == 1): the store is a DEVICE buffer, nothing is
  * copied and the same kernels run in the same order on the same bytes, so the
  * results are bit-identical to streamed mode (blog "Why the evidence is better
- * than usual": streaming is a pure scheduling change).
+ * than usual": streaming reorders copies, not arithmetic).
  * A pageable host store still works, but its copies cannot overlap compute;
  * the call then returns QL_WARN_PAGEABLE_HOST (docs "Layer Streaming":
  * pageable fallback with its cost reported).
@@ -382,6 +394,18 @@ enum {
 };
 ql_status ql_profile_enable(int32_t on);
 ql_status ql_profile_read(int32_t kernel, int64_t* launches, double* ms, double* work);
+
+/* Race check for the streamer (test use). The pages' evidence for streaming
+ * is that a streamed run equals a normal one bit for bit, checked in a
+ * notebook that caps the process's memory (Soup README intro). A read of a
+ * slot before its copy has landed would usually see the previous layer's
+ * bytes: wrong, but finite and easy to miss. With on = 1, every streamed call
+ * fills a slot with 0xFF bytes on the copy stream right before each copy
+ * into it (NaN scales, code 15), so such a read turns the outputs into NaN.
+ * Results of correct runs are unchanged. Refused (QL_ERR_UNSUPPORTED) by
+ * stream_layer_stack_step_capture while on. Process-wide; not thread-safe
+ * against concurrent streamed calls. */
+ql_status ql_debug_poison_slots(int32_t on);
 
 #ifdef __cplusplus
 }

@@ -31,6 +31,7 @@ EXPORTS = (
     "stream_layer_stack_layout", "stream_layer_stack_workspace", "stream_layer_stack_saved_layout",
     "stream_layer_stack_fwd", "stream_layer_stack_fwd_ref", "stream_layer_stack_bwd", "ql_profile_enable",
     "ql_profile_read", "stream_layer_stack_step_capture", "ql_step_graph_launch", "ql_step_graph_destroy",
+    "ql_debug_poison_slots",
 )
 QL_KERNEL_GEMM_FWD, QL_KERNEL_GEMM_BWD, QL_KERNEL_GEMM_FWD_NARROW, QL_KERNEL_GEMM_BWD_NARROW = 0, 1, 2, 3
 QL_KERNEL_LORA_ROW, QL_KERNEL_LORA_COL, QL_KERNEL_DEQUANT = 4, 5, 6
@@ -103,6 +104,7 @@ def load(path=LIB_PATH):
         "stream_layer_stack_bwd": (I32, [ctypes.POINTER(ql_stack_cfg), P, SZ, P, P, I64, P, SZ, P, P, P,
                                          I32, I32, P, SZ, P, SZ, P, P]),
         "ql_profile_enable": (I32, [I32]),
+        "ql_debug_poison_slots": (I32, [I32]),
         "ql_profile_read": (I32, [I32, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_double),
                                   ctypes.POINTER(ctypes.c_double)]),
     }
@@ -384,6 +386,10 @@ def build_store(cfg, layers, pinned=True, device=None):
                 ab = absmax.reshape(-1).view(torch.uint8)
             store[base + ao: base + ao + ab.numel()].copy_(ab)
     return store
+
+
+def ql_debug_poison_slots(on):
+    return _check(load().ql_debug_poison_slots(int(on)))
 
 
 def ql_profile_enable(on):

@@ -39,6 +39,9 @@ static ql_status check_weight(const char* fn, const ql_nf4_weight& W) {
   if (W.K % 64) return set_error(QL_ERR_SHAPE, "%s: W.K (%lld) must be a multiple of 64 (NF4 block)", fn,
                                  (long long)W.K);
   if (W.N % 16) return set_error(QL_ERR_SHAPE, "%s: W.N (%lld) must be a multiple of 16", fn, (long long)W.N);
+  if (W.N > QL_MAX_DIM || W.K > QL_MAX_DIM)
+    return set_error(QL_ERR_SHAPE, "%s: W.N (%lld) and W.K (%lld) must be <= QL_MAX_DIM (%d)", fn, (long long)W.N,
+                     (long long)W.K, QL_MAX_DIM);
   QL_TRY(check_ptr(fn, "W.packed", W.packed, 16));
   QL_TRY(check_ptr(fn, "W.absmax", W.absmax, 16));
   return QL_OK;
@@ -54,19 +57,9 @@ static ql_status check_lora(const char* fn, const ql_lora& L) {
   return QL_OK;
 }
 
-// per-device flag for nf4_quantize's non-finite check
-static std::mutex g_flag_mu;
-static int* g_flag[64] = {};
-
-static ql_status device_flag(int** out) {
-  int dev = 0;
-  QL_HIP_CHECK(hipGetDevice(&dev));
-  if (dev < 0 || dev >= 64) return set_error(QL_ERR_UNSUPPORTED, "device id %d out of range", dev);
-  std::lock_guard<std::mutex> lk(g_flag_mu);
-  if (!g_flag[dev]) QL_HIP_CHECK(hipMalloc((void**)&g_flag[dev], 256));
-  *out = g_flag[dev];
-  return QL_OK;
-}
+// nf4_quantize's finiteness check runs on the device's flag word one call at
+// a time (host threads take turns), so concurrent calls never share it
+static std::mutex g_quant_mu;
 
 // --------------------------------------------------------- linear helpers
 struct LinearWs {
@@ -99,10 +92,12 @@ struct StackLayout {
 static ql_status check_cfg(const char* fn, const ql_stack_cfg* c) {
   if (!c) return set_error(QL_ERR_ARG, "%s: cfg is NULL", fn);
   if (c->n_layers < 1) return set_error(QL_ERR_SHAPE, "%s: n_layers (%d) must be >= 1", fn, c->n_layers);
-  if (c->hidden < 64 || c->hidden % 64)
-    return set_error(QL_ERR_SHAPE, "%s: hidden (%d) must be a positive multiple of 64", fn, c->hidden);
-  if (c->inter < 64 || c->inter % 64)
-    return set_error(QL_ERR_SHAPE, "%s: inter (%d) must be a positive multiple of 64", fn, c->inter);
+  if (c->hidden < 64 || c->hidden % 64 || c->hidden > QL_MAX_DIM)
+    return set_error(QL_ERR_SHAPE, "%s: hidden (%d) must be a positive multiple of 64, at most QL_MAX_DIM (%d)", fn,
+                     c->hidden, QL_MAX_DIM);
+  if (c->inter < 64 || c->inter % 64 || c->inter > QL_MAX_DIM)
+    return set_error(QL_ERR_SHAPE, "%s: inter (%d) must be a positive multiple of 64, at most QL_MAX_DIM (%d)", fn,
+                     c->inter, QL_MAX_DIM);
   if (c->head_dim < 64 || c->head_dim % 64)
     return set_error(QL_ERR_SHAPE, "%s: head_dim (%d) must be a positive multiple of 64", fn, c->head_dim);
   if (c->kv_dim < c->head_dim || c->kv_dim % c->head_dim || c->hidden % c->kv_dim)
@@ -559,8 +554,16 @@ static PtrKind pointer_kind(const void* p) {
   return PK_PAGEABLE;
 }
 
+// Race check (ql_debug_poison_slots): every slot is filled with 0xFF bytes
+// on the copy stream right before a record is copied into it, after the
+// slot's previous readers are done. A kernel that read a slot before its
+// `ready` event would then meet NaN scales and codes 15 instead of a stale
+// but plausible layer, and the outputs would show it.
+static bool g_poison = false;
+
 // One layer record host -> device on the copy stream.
 static ql_status copy_record(void* dst, const void* src, size_t bytes, hipStream_t P) {
+  if (g_poison) QL_HIP_CHECK(hipMemsetAsync(dst, 0xFF, bytes, P));
   QL_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, P));
   return QL_OK;
 }
@@ -766,6 +769,68 @@ static void profile_clear() {
   g_pool_next = 0;
 }
 
+// ------------------------------------------------------- linear backward
+// Argument checks of the linear backward other than its workspace.
+static ql_status check_linear_bwd(const char* fn, const void* dy, const void* x, const void* u_saved, int64_t M,
+                                  const ql_nf4_weight& W, const ql_lora& L, const void* dx, const float* dA,
+                                  const float* dB, int32_t accumulate) {
+  if (M < 0) return set_error(QL_ERR_SHAPE, "%s: M (%lld) must be >= 0", fn, (long long)M);
+  if (accumulate != 0 && accumulate != 1) return set_error(QL_ERR_ARG, "%s: accumulate must be 0 or 1", fn);
+  QL_TRY(check_weight(fn, W));
+  QL_TRY(check_lora(fn, L));
+  QL_TRY(check_ptr(fn, "dA", dA, 16));
+  QL_TRY(check_ptr(fn, "dB", dB, 16));
+  if (M > 0) {
+    QL_TRY(check_ptr(fn, "dy", dy, 16));
+    QL_TRY(check_ptr(fn, "x", x, 16));
+    QL_TRY(check_ptr(fn, "u_saved", u_saved, 16));
+    if (dx) QL_TRY(check_ptr(fn, "dx", dx, 16));
+  }
+  return QL_OK;
+}
+
+// The linear backward with its temporaries in ws (lw.bwd bytes, 256-byte
+// aligned; unused when M == 0). Every temporary is written before it is
+// read, so ws needs no clearing and keeps nothing between calls.
+static ql_status run_linear_bwd(const void* dy, const void* x, const void* u_saved, int64_t M,
+                                const ql_nf4_weight& W, const ql_lora& L, void* dx, float* dA, float* dB,
+                                int32_t accumulate, uint8_t* w8, const LinearWs& lw, hipStream_t st) {
+  const float sc = L.alpha / (float)L.r;
+  if (M == 0) {
+    if (!accumulate) {
+      QL_TRY(launch_zero_f32(dA, (int64_t)L.r * W.K, st));
+      QL_TRY(launch_zero_f32(dB, W.N * L.r, st));
+    }
+    return QL_OK;
+  }
+  uint16_t* bt = (uint16_t*)(w8 + lw.bt_off);
+  uint16_t* G = (uint16_t*)(w8 + lw.g_off);
+  void* scratch = w8 + lw.scratch_off;
+  const size_t scratch_bytes = lw.partial_off - lw.scratch_off;
+  {
+    TransArgs ta{};
+    ta.n = 1; ta.in[0] = (const uint16_t*)L.B; ta.out[0] = bt; ta.rows[0] = W.N; ta.cols[0] = L.r;
+    QL_TRY(launch_transpose_bf16(ta, st));
+    RowArgs ra{};
+    ra.nprob = 1;
+    ra.p[0] = g_prob((const uint16_t*)dy, M, W.N, L.r, bt, G);
+    QL_TRY(launch_rowc(ra, scratch, scratch_bytes, st));
+  }
+  if (dx) {
+    BwdArgs a{};
+    a.M = M; a.K = W.K; a.r = L.r; a.s = sc; a.out = dx; a.nseg = 1;
+    a.seg[0] = BwdSeg{(const uint16_t*)dy, W.packed, W.absmax, G, (const uint16_t*)L.A, W.N};
+    a.partial = (float*)(w8 + lw.partial_off);
+    a.partial_bytes = bwd_partial_bytes(M, W.K);
+    QL_TRY(launch_gemm_bwd(a, st));
+  }
+  ColArgs grads{};
+  grads.nprob = 2;
+  grads.p[0] = db_prob((const uint16_t*)dy, M, W.N, (const uint16_t*)u_saved, L.r, sc, dB, accumulate);
+  grads.p[1] = da_prob((const uint16_t*)x, M, W.K, W.K, 0, 0, G, L.r, sc, dA, accumulate);
+  return launch_colc(grads, scratch, scratch_bytes, st);
+}
+
 }  // namespace ql
 
 using namespace ql;
@@ -807,7 +872,14 @@ ql_status ql_profile_read(int32_t kernel, int64_t* launches, double* ms, double*
   return QL_OK;
 }
 
-int32_t ql_abi_version(void) { return 100; }
+int32_t ql_abi_version(void) { return 101; }
+
+ql_status ql_debug_poison_slots(int32_t on) {
+  clear_error();
+  if (on != 0 && on != 1) return set_error(QL_ERR_ARG, "ql_debug_poison_slots: on must be 0 or 1");
+  g_poison = on != 0;
+  return QL_OK;
+}
 
 ql_status nf4_codebook(float* out) {
   clear_error();
@@ -826,15 +898,13 @@ ql_status nf4_quantize(const float* w, int64_t n, uint8_t* packed, float* absmax
   QL_TRY(check_ptr(fn, "packed", packed, 16));
   QL_TRY(check_ptr(fn, "absmax", absmax, 16));
   hipStream_t st = (hipStream_t)s;
-  int* flag = nullptr;
-  QL_TRY(device_flag(&flag));
-  QL_TRY(launch_clear_i32(flag, 1, st));
-  QL_TRY(launch_nf4_quantize(w, n, packed, absmax, flag, st));
-  int host_flag = 0;
-  QL_HIP_CHECK(hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, st));
-  QL_HIP_CHECK(hipStreamSynchronize(st));
-  if (host_flag) return set_error(QL_ERR_NONFINITE, "%s: w holds NaN or Inf", fn);
-  return QL_OK;
+  {  // refuse non-finite input before anything is written
+    std::lock_guard<std::mutex> lk(g_quant_mu);
+    int nonfinite = 0;
+    QL_TRY(scan_nonfinite(w, n, &nonfinite, st));
+    if (nonfinite) return set_error(QL_ERR_NONFINITE, "%s: w holds NaN or Inf", fn);
+  }
+  return launch_nf4_quantize(w, n, packed, absmax, st);
 }
 
 ql_status nf4_dq_layout(int64_t nblocks, size_t* scale_off, size_t* mean_off, size_t* bytes) {
@@ -896,8 +966,9 @@ ql_status nf4_dequant(const uint8_t* packed, const float* absmax, int64_t n, int
 ql_status qlora_linear_workspace(int64_t M, int64_t N, int64_t K, int32_t r, size_t* fwd_bytes,
                                  size_t* bwd_bytes) {
   clear_error();
-  if (M < 0 || N <= 0 || K <= 0 || K % 64 || N % 16)
-    return set_error(QL_ERR_SHAPE, "qlora_linear_workspace: need M >= 0, N % 16 == 0, K % 64 == 0");
+  if (M < 0 || N <= 0 || K <= 0 || K % 64 || N % 16 || N > QL_MAX_DIM || K > QL_MAX_DIM)
+    return set_error(QL_ERR_SHAPE, "qlora_linear_workspace: need M >= 0, N % 16 == 0, K % 64 == 0, "
+                     "N and K <= QL_MAX_DIM");
   if (r < 1 || r > 64) return set_error(QL_ERR_RANK, "qlora_linear_workspace: r (%d) must be in 1..64", r);
   LinearWs w = linear_ws(M, N, K, r);
   if (fwd_bytes) *fwd_bytes = w.fwd;
@@ -941,59 +1012,13 @@ ql_status qlora_linear_bwd(const void* dy, const void* x, const void* u_saved, i
                            size_t ws_bytes, ql_stream s) {
   clear_error();
   const char* fn = "qlora_linear_bwd";
-  if (M < 0) return set_error(QL_ERR_SHAPE, "%s: M (%lld) must be >= 0", fn, (long long)M);
-  if (accumulate != 0 && accumulate != 1) return set_error(QL_ERR_ARG, "%s: accumulate must be 0 or 1", fn);
-  QL_TRY(check_weight(fn, W));
-  QL_TRY(check_lora(fn, L));
-  QL_TRY(check_ptr(fn, "dA", dA, 16));
-  QL_TRY(check_ptr(fn, "dB", dB, 16));
-  if (M > 0) {
-    QL_TRY(check_ptr(fn, "dy", dy, 16));
-    QL_TRY(check_ptr(fn, "x", x, 16));
-    QL_TRY(check_ptr(fn, "u_saved", u_saved, 16));
-    if (dx) QL_TRY(check_ptr(fn, "dx", dx, 16));
-  }
+  QL_TRY(check_linear_bwd(fn, dy, x, u_saved, M, W, L, dx, dA, dB, accumulate));
   LinearWs lw = linear_ws(M, W.N, W.K, L.r);
   if (M > 0) {
     if (ws_bytes < lw.bwd) return set_error(QL_ERR_WORKSPACE, "%s: ws_bytes (%zu) < %zu", fn, ws_bytes, lw.bwd);
     QL_TRY(check_ptr(fn, "ws", ws, 256));
   }
-  hipStream_t st = (hipStream_t)s;
-  const float sc = L.alpha / (float)L.r;
-  if (M == 0) {
-    if (!accumulate) {
-      QL_TRY(launch_zero_f32(dA, (int64_t)L.r * W.K, st));
-      QL_TRY(launch_zero_f32(dB, W.N * L.r, st));
-    }
-    return QL_OK;
-  }
-  uint8_t* w8 = (uint8_t*)ws;
-  uint16_t* bt = (uint16_t*)(w8 + lw.bt_off);
-  uint16_t* G = (uint16_t*)(w8 + lw.g_off);
-  void* scratch = w8 + lw.scratch_off;
-  const size_t scratch_bytes = lw.partial_off - lw.scratch_off;
-  {
-    TransArgs ta{};
-    ta.n = 1; ta.in[0] = u16(L.B); ta.out[0] = bt; ta.rows[0] = W.N; ta.cols[0] = L.r;
-    QL_TRY(launch_transpose_bf16(ta, st));
-    RowArgs ra{};
-    ra.nprob = 1;
-    ra.p[0] = g_prob(u16(dy), M, W.N, L.r, bt, G);
-    QL_TRY(launch_rowc(ra, scratch, scratch_bytes, st));
-  }
-  if (dx) {
-    BwdArgs a{};
-    a.M = M; a.K = W.K; a.r = L.r; a.s = sc; a.out = dx; a.nseg = 1;
-    a.seg[0] = BwdSeg{u16(dy), W.packed, W.absmax, G, u16(L.A), W.N};
-    a.partial = (float*)(w8 + lw.partial_off);
-    a.partial_bytes = bwd_partial_bytes(M, W.K);
-    QL_TRY(launch_gemm_bwd(a, st));
-  }
-  ColArgs grads{};
-  grads.nprob = 2;
-  grads.p[0] = db_prob(u16(dy), M, W.N, u16(u_saved), L.r, sc, dB, accumulate);
-  grads.p[1] = da_prob(u16(x), M, W.K, W.K, 0, 0, G, L.r, sc, dA, accumulate);
-  return launch_colc(grads, scratch, scratch_bytes, st);
+  return run_linear_bwd(dy, x, u_saved, M, W, L, dx, dA, dB, accumulate, (uint8_t*)ws, lw, (hipStream_t)s);
 }
 
 ql_status stream_layer_stack_layout(const ql_stack_cfg* cfg, int64_t* layer_offsets, int64_t* proj_offsets,
@@ -1295,6 +1320,7 @@ ql_status stream_layer_stack_step_capture(const ql_stack_cfg* cfg, const void* s
   if (turnaround != 0 && turnaround != 1) return set_error(QL_ERR_ARG, "%s: turnaround must be 0 or 1", fn);
   if (profiling_on()) return set_error(QL_ERR_UNSUPPORTED, "%s: kernel timing is on (ql_profile_enable)", fn);
   if (!compute) return set_error(QL_ERR_ARG, "%s: capture needs an explicit compute stream", fn);
+  if (g_poison) return set_error(QL_ERR_UNSUPPORTED, "%s: slot poisoning is on (ql_debug_poison_slots)", fn);
   if (M == 0) return set_error(QL_ERR_SHAPE, "%s: M must be >= 1", fn);
   hipStream_t C = (hipStream_t)compute;
   QL_HIP_CHECK(hipStreamBeginCapture(C, hipStreamCaptureModeRelaxed));

@@ -19,7 +19,7 @@ namespace ql {
 // with ties going to the lower index.
 __global__ __launch_bounds__(256) void k_nf4_quantize(const float4* __restrict__ w, int64_t nblocks,
                                                       uint8_t* __restrict__ packed,
-                                                      float* __restrict__ absmax, int* flag) {
+                                                      float* __restrict__ absmax) {
   __shared__ double mid[15];
   if (threadIdx.x < 15) {
     double a = (double)__builtin_bit_cast(float, kNF4LevelBits[threadIdx.x]);
@@ -33,9 +33,6 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float4* __restrict__
   const bool active = blk < nblocks;
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
   if (active) v = w[blk * 16 + lane16];
-  const bool finite = __builtin_isfinite(v.x) && __builtin_isfinite(v.y) &&
-                      __builtin_isfinite(v.z) && __builtin_isfinite(v.w);
-  if (active && !finite) atomicOr(flag, 1);
   float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
   // max over the 16 lanes of this block (xor offsets stay inside aligned groups of 16)
   for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
@@ -59,26 +56,56 @@ __global__ __launch_bounds__(256) void k_nf4_quantize(const float4* __restrict__
   if (active && (lane16 & 1) == 0) ((uint32_t*)packed)[blk * 8 + (lane16 >> 1)] = mine | (other << 4);
 }
 
-__global__ void k_clear_i32(int* p, int n) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
+// The finiteness flag of nf4_quantize: one word per device, in the code
+// object, so the library keeps no allocation of its own. Host code reaches it
+// only through the address hipGetSymbolAddress gives for the current device.
+static __device__ int g_nonfinite;
+static int* g_nonfinite_dev[64] = {};
+
+// flag = 1 if any element is NaN or infinite (every writer stores the same
+// value, so plain stores suffice); grid-stride over float4 groups
+__global__ __launch_bounds__(256) void k_scan_nonfinite(const float4* __restrict__ w, int64_t n4, int* flag) {
+  bool bad = false;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const float4 v = w[i];
+    bad |= !(__builtin_isfinite(v.x) && __builtin_isfinite(v.y) && __builtin_isfinite(v.z) &&
+             __builtin_isfinite(v.w));
+  }
+  if (bad) *flag = 1;
 }
 
-ql_status launch_clear_i32(int* p, int n, hipStream_t st) {
-  hipLaunchKernelGGL(k_clear_i32, dim3((n + 63) / 64), dim3(64), 0, st, p, n);
+__global__ void k_set_i32(int* p, int v) { *p = v; }
+
+ql_status scan_nonfinite(const float* w, int64_t n, int* nonfinite, hipStream_t st) {
+  int dev = 0;
+  QL_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return set_error(QL_ERR_UNSUPPORTED, "device id %d out of range", dev);
+  if (!g_nonfinite_dev[dev]) QL_HIP_CHECK(hipGetSymbolAddress((void**)&g_nonfinite_dev[dev], HIP_SYMBOL(g_nonfinite)));
+  int* flag = g_nonfinite_dev[dev];
+  hipLaunchKernelGGL(k_set_i32, dim3(1), dim3(1), 0, st, flag, 0);
   QL_HIP_CHECK(hipGetLastError());
+  int64_t grid = (n / 4 + 255) / 256;
+  if (grid > 256 * 16) grid = 256 * 16;
+  if (grid > 0) {
+    hipLaunchKernelGGL(k_scan_nonfinite, dim3((unsigned)grid), dim3(256), 0, st, (const float4*)w, n / 4, flag);
+    QL_HIP_CHECK(hipGetLastError());
+  }
+  int host = 0;
+  QL_HIP_CHECK(hipMemcpyAsync(&host, flag, sizeof(int), hipMemcpyDeviceToHost, st));
+  QL_HIP_CHECK(hipStreamSynchronize(st));
+  *nonfinite = host != 0;
   return QL_OK;
 }
 
-ql_status launch_nf4_quantize(const float* w, int64_t n, uint8_t* packed, float* absmax, int* flag,
-                              hipStream_t st) {
+ql_status launch_nf4_quantize(const float* w, int64_t n, uint8_t* packed, float* absmax, hipStream_t st) {
   const int64_t nblocks = n / 64;
   const int64_t threads = nblocks * 16;
   const int64_t grid = (threads + 255) / 256;
   if (grid > 0x7fffffff) return set_error(QL_ERR_SHAPE, "nf4_quantize: n too large for one launch");
   if (grid == 0) return QL_OK;
   hipLaunchKernelGGL(k_nf4_quantize, dim3((unsigned)grid), dim3(256), 0, st,
-                     (const float4*)w, nblocks, packed, absmax, flag);
+                     (const float4*)w, nblocks, packed, absmax);
   QL_HIP_CHECK(hipGetLastError());
   return QL_OK;
 }

@@ -168,7 +168,11 @@ __device__ __forceinline__ uint4 lora_row8(const uint16_t* row, int j0, int r, f
 
 // Buffer resources: loads through a base in SGPRs and a 32-bit lane offset;
 // a raw buffer load at or past num_records returns zero, which masks the rows
-// past the end of a tile without branches.
+// past the end of a tile without branches. The range is clamped to 2^31 - 1
+// bytes: every descriptor here is based at the block it serves (at most 256
+// rows of activations, or 64 rows of codes in a dX reduction step), and with
+// dimensions of at most QL_MAX_DIM every offset into such a block stays below
+// 2^31 whatever the size of the whole tensor.
 // Base and size are made provably wave-uniform so the descriptor lives in SGPRs.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
   const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
@@ -678,15 +682,12 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
   auto ydesc = [&](int s, int64_t N) {
     return rsrc(s < nseg ? (const void*)(a.seg[s].dY + m0 * N) : nullptr, s < nseg ? xrows * N * 2 : 0);
   };
-  auto cdesc = [&](int s, int64_t N) {
-    return rsrc(s < nseg ? (const void*)(a.seg[s].packed + k0 / 2) : nullptr, s < nseg ? N * (K / 2) - k0 / 2 : 0);
-  };
-  auto sdesc = [&](int s, int64_t N) {
-    return rsrc(s < nseg ? (const void*)(a.seg[s].absmax + k0 / 64) : nullptr, s < nseg ? (N * kbn - k0 / 64) * 4 : 0);
-  };
   const __amdgpu_buffer_rsrc_t yr0 = ydesc(0, N0), yr1 = ydesc(1, N1), yr2 = ydesc(2, N2);
-  const __amdgpu_buffer_rsrc_t cr0 = cdesc(0, N0), cr1 = cdesc(1, N1), cr2 = cdesc(2, N2);
-  const __amdgpu_buffer_rsrc_t sr0 = sdesc(0, N0), sr1 = sdesc(1, N1), sr2 = sdesc(2, N2);
+  // codes and scales of each segment from the tile's first output column
+  auto seg_codes = [&](int s) { return s < nseg ? a.seg[s].packed + k0 / 2 : (const uint8_t*)nullptr; };
+  auto seg_scales = [&](int s) { return s < nseg ? a.seg[s].absmax + k0 / 64 : (const float*)nullptr; };
+  const uint8_t *pk0 = seg_codes(0), *pk1 = seg_codes(1), *pk2 = seg_codes(2);
+  const float *am0 = seg_scales(0), *am1 = seg_scales(1), *am2 = seg_scales(2);
   const int WS_all = (int)((N0 + BK - 1) / BK + (N1 + BK - 1) / BK + (N2 + BK - 1) / BK);
   const int ws_begin = (int)((int64_t)WS_all * sp / a.nsplit);
   const int WS = (int)((int64_t)WS_all * (sp + 1) / a.nsplit) - ws_begin;
@@ -728,10 +729,16 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
     }
     advance(sgA, nbA);
   };
-  // raw codes and scales of the step at (sgR, nbR) into a raw stage
+  // Raw codes and scales of the step at (sgR, nbR) into a raw stage. The
+  // descriptors are based at the step's first weight row, with the offset
+  // formed in 64 bits, so the 32-bit lane offsets stay inside one step (64
+  // rows of at most 2^20 bytes) whatever the size of the weight; rows past the
+  // segment's end lie past the descriptor's range and read as zeros.
   auto dma_raw = [&](uint8_t* R) {
-    const __amdgpu_buffer_rsrc_t cr = sel3(sgR, cr0, cr1, cr2);
-    const __amdgpu_buffer_rsrc_t sr = sel3(sgR, sr0, sr1, sr2);
+    const int64_t N = sel3(sgR, N0, N1, N2);
+    const int64_t rows_left = N - nbR;
+    const __amdgpu_buffer_rsrc_t cr = rsrc(sel3(sgR, pk0, pk1, pk2) + (int64_t)nbR * (K / 2), rows_left * (K / 2) - k0 / 2);
+    const __amdgpu_buffer_rsrc_t sr = rsrc(sel3(sgR, am0, am1, am2) + (int64_t)nbR * kbn, (rows_left * kbn - k0 / 64) * 4);
     const int kh = (int)(K / 2);
 #pragma unroll
     for (int cc = 0; cc < CPR / 4; ++cc) {
@@ -739,10 +746,9 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
       const int slot = ci * 64 + lane;
       const int n = slot / CPR, pc = slot % CPR;
       const int c = pc ^ ((n >> SH) & (CPR - 1));
-      dma16(cr, R + ci * 1024, n * kh + c * 16, __builtin_amdgcn_readfirstlane(nbR * kh));
+      dma16(cr, R + ci * 1024, n * kh + c * 16, 0);
     }
-    dma4(sr, R + ABS + 256 * w, ((16 * w + (lane >> 2)) * (int)kbn + (lane & 3)) * 4,
-         __builtin_amdgcn_readfirstlane(nbR * (int)kbn * 4));
+    dma4(sr, R + ABS + 256 * w, ((16 * w + (lane >> 2)) * (int)kbn + (lane & 3)) * 4, 0);
     advance(sgR, nbR);
   };
 

@@ -108,9 +108,10 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // All launchers enqueue on `st` and report launch errors through the status.
 
-ql_status launch_nf4_quantize(const float* w, int64_t n, uint8_t* packed, float* absmax,
-                              int* flag, hipStream_t st);
-ql_status launch_clear_i32(int* p, int n, hipStream_t st);
+ql_status launch_nf4_quantize(const float* w, int64_t n, uint8_t* packed, float* absmax, hipStream_t st);
+// *nonfinite = 1 if w[0 .. n) holds a NaN or an infinity, else 0; waits for
+// the stream (the scan's flag is one device word, so callers take turns)
+ql_status scan_nonfinite(const float* w, int64_t n, int* nonfinite, hipStream_t st);
 ql_status launch_nf4_dequant(const uint8_t* packed, const float* absmax, int64_t n, int out_f32,
                              void* out, hipStream_t st);
 

@@ -4,7 +4,7 @@ Test infrastructure only (see the package docstring).
 
 The pages: only the LoRA adapter trains, the quantised base is frozen (blog
 post, "How does Soup train an 8B model on a 4 GB GPU?" and "The trick: layer
-streaming"); streaming is a pure scheduling change with the same gradients
+streaming"); streaming only reorders the copies and leaves the gradients unchanged
 ("Why the evidence is better than usual"). The adapter formula is the
 standard LoRA one, y = x W^T + (alpha / r) (x A^T) B^T, with W the dequantised
 NF4 weight [N x K], A [r x K], B [N x r], s = alpha / r. The backward needs dX

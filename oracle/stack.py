@@ -171,8 +171,9 @@ class Layer:
             dB = dB.astype(np.float32).astype(np.float64)
         return dx, dA, dB
 
-    def bwd(self, dh, sv, mode="faithful"):
-        """Returns (dh_in, grads) with grads[p] = (dA, dB)."""
+    def bwd(self, dh, sv, mode="faithful", keep=None):
+        """Returns (dh_in, grads) with grads[p] = (dA, dB). A dict `keep`
+        receives the residual-path gradient dh_mid (for error bounds)."""
         dh = np.asarray(dh, np.float64)
         g = {}
         dact, dAd, dBd = self._lin_bwd("down", dh, sv["act"], sv["U_down"], mode)
@@ -186,6 +187,8 @@ class Layer:
         g["gate"], g["up"] = (dAg, dBg), (dAu, dBu)
         dn2 = _r(dxg + dxu, mode)
         dh_mid = _r(dh + rmsnorm_bwd(sv["h_mid"], dn2), mode)
+        if keep is not None:
+            keep["dh_mid"] = dh_mid
         a = repeat_kv(sv["v"], self.H, self.head_dim)
         da, dAo, dBo = self._lin_bwd("o", dh_mid, a, sv["U_o"], mode)
         g["o"] = (dAo, dBo)

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_codebook():
     lib()
-    assert ql.ql_abi_version() == 100
+    assert ql.ql_abi_version() == 101
     assert np.array_equal(ql.nf4_codebook().numpy().view(np.uint32), onf4.codebook().view(np.uint32))
 
 
@@ -54,7 +54,9 @@ def test_workspace_shape_validation():
     assert f > 0 and b > 0
     for args, st in (((64, 512, 250, 8), ql.QL_ERR_SHAPE), ((64, 500, 256, 8), ql.QL_ERR_SHAPE),
                      ((64, 512, 256, 0), ql.QL_ERR_RANK), ((64, 512, 256, 65), ql.QL_ERR_RANK),
-                     ((-1, 512, 256, 8), ql.QL_ERR_SHAPE)):
+                     ((-1, 512, 256, 8), ql.QL_ERR_SHAPE),
+                     ((64, (1 << 21) + 16, 256, 8), ql.QL_ERR_SHAPE),
+                     ((64, 512, (1 << 21) + 64, 8), ql.QL_ERR_SHAPE)):
         with pytest.raises(ql.QlError) as e:
             ql.qlora_linear_workspace(*args)
         assert e.value.status == st
@@ -75,6 +77,24 @@ def test_linear_validation_refuses_before_device_work():
     with pytest.raises(ql.QlError) as e:
         ql.qlora_linear_fwd(x, 64, W, L, x, x, x, stream=0)
     assert e.value.status == ql.QL_ERR_RANK
+
+
+@pytest.mark.parametrize("N,K", [((1 << 21) + 16, 4096), (4096, (1 << 21) + 64), ((1 << 22), (1 << 22))])
+def test_dimensions_above_the_limit_are_refused(N, K):
+    # Every byte offset the GEMMs form within one row block (64 rows of codes,
+    # 256 rows of activations) must fit in 32 bits; dimensions above
+    # QL_MAX_DIM = 2^21 are refused before any device work, forward and backward.
+    lib()
+    x = torch.zeros(64, 256, dtype=torch.bfloat16)
+    W = ql.NF4Weight(torch.zeros(256, dtype=torch.uint8), torch.zeros(4, dtype=torch.float32), N, K)
+    L = ql.Lora(torch.zeros(8, 256, dtype=torch.bfloat16), torch.zeros(512, 8, dtype=torch.bfloat16), 8, 16.0)
+    with pytest.raises(ql.QlError) as e:
+        ql.qlora_linear_fwd(x, 64, W, L, x, x, x, stream=0)
+    assert e.value.status == ql.QL_ERR_SHAPE and "QL_MAX_DIM" in ql.ql_last_error()
+    dA = torch.zeros(8, 256)
+    with pytest.raises(ql.QlError) as e:
+        ql.qlora_linear_bwd(x, x, x, 64, W, L, x, dA, dA, 0, x, stream=0)
+    assert e.value.status == ql.QL_ERR_SHAPE and "QL_MAX_DIM" in ql.ql_last_error()
 
 
 def test_quantize_dequant_size_validation():
@@ -137,9 +157,10 @@ def test_stack_cfg_validation():
            ql.StackCfg(2, 576, 1536, 200, 64, 8, 16.0), ql.StackCfg(2, 576, 1536, 192, 64, 0, 16.0),
            ql.StackCfg(2, 576, 1536, 192, 64, 8, 16.0, n_buffers=1),
            ql.StackCfg(2, 576, 1536, 192, 64, 8, 16.0, n_buffers=9),
-           ql.StackCfg(2, 576, 1536, 192, 64, 8, 16.0, recompute=2)]
+           ql.StackCfg(2, 576, 1536, 192, 64, 8, 16.0, recompute=2),
+           ql.StackCfg(2, 576, (1 << 21) + 64, 192, 64, 8, 16.0)]
     want = [ql.QL_ERR_SHAPE, ql.QL_ERR_SHAPE, ql.QL_ERR_SHAPE, ql.QL_ERR_RANK, ql.QL_ERR_UNSUPPORTED,
-            ql.QL_ERR_UNSUPPORTED, ql.QL_ERR_ARG]
+            ql.QL_ERR_UNSUPPORTED, ql.QL_ERR_ARG, ql.QL_ERR_SHAPE]
     for cfg, st in zip(bad, want):
         with pytest.raises(ql.QlError) as e:
             ql.stream_layer_stack_layout(cfg)
@@ -168,3 +189,4 @@ def test_profile_read_refuses_unknown_kernel_ids():
         assert e.value.status == ql.QL_ERR_ARG
     n, ms, work = ql.ql_profile_read(ql.QL_KERNEL_DEQUANT)   # nothing recorded: zeros, no GPU work
     assert n == 0 and ms == 0.0 and work == 0.0
+

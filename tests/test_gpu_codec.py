@@ -70,16 +70,25 @@ def test_quantize_full_projection_sampled_blocks():
     assert np.array_equal(ab.view(np.uint32), oa.view(np.uint32))
 
 
-@pytest.mark.parametrize("bad", [float("nan"), float("inf"), float("-inf")])
-def test_quantize_refuses_nonfinite(bad):
+@pytest.mark.parametrize("bad,at,n", [(float("nan"), 100, 256), (float("inf"), 0, 256),
+                                      (float("-inf"), 255, 256), (float("nan"), 3 * 2 ** 20 + 7, 2 ** 22)])
+def test_quantize_refuses_nonfinite(bad, at, n):
+    # refused before anything is written: the outputs keep their contents; a
+    # finite call right after (the device flag cleared) succeeds
     require_gpu()
-    w = torch.zeros(256, dtype=torch.float32, device=DEV)
-    w[100] = bad
-    packed = torch.empty(128, dtype=torch.uint8, device=DEV)
-    absmax = torch.empty(4, dtype=torch.float32, device=DEV)
+    w = torch.zeros(n, dtype=torch.float32, device=DEV)
+    w[at] = bad
+    packed = torch.full((n // 2,), 0x5A, dtype=torch.uint8, device=DEV)
+    absmax = torch.full((n // 64,), -2.5, dtype=torch.float32, device=DEV)
     with pytest.raises(ql.QlError) as e:
         ql.nf4_quantize(w, packed, absmax)
     assert e.value.status == ql.QL_ERR_NONFINITE
+    torch.cuda.synchronize()
+    assert bool((packed == 0x5A).all()) and bool((absmax == -2.5).all())
+    w[at] = 1.0
+    assert ql.nf4_quantize(w, packed, absmax) == ql.QL_OK
+    torch.cuda.synchronize()
+    assert float(absmax[at // 64]) == 1.0
 
 
 def test_quantize_rejects_bad_sizes():

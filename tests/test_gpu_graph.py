@@ -2,14 +2,15 @@
 
 One step of the SmolLM2-shaped streamed stack (about 1,400 kernels, 56 copies)
 is captured once and replayed; every replay, interleaved with eager steps and
-host synchronisations, must equal the eager step bitwise.
+host synchronisations, must equal the eager step bitwise. The first replay's
+results are also compared with the oracle, every layer teacher-forced.
 """
 
 import pytest
 import torch
 
 from gpu_util import ql, require_gpu
-from stack_util import GpuStack, identical
+from stack_util import GpuStack, identical, teacher_forced
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +50,10 @@ def test_replays_with_turnaround_equal_the_eager_step(sm):
         clobber(sm)
         g.launch(sm.compute)
         torch.cuda.synchronize()
-        assert identical(sm.results(), sm.eager), rep
+        replay = sm.results()
+        assert identical(replay, sm.eager), rep
+        if rep == 0:
+            teacher_forced(sm, replay)
         # eager work between replays (it also leaves the slots as a step does)
         assert sm.fwd(reuse=True) == ql.QL_OK
         assert sm.bwd(reuse=True) == ql.QL_OK

@@ -280,12 +280,17 @@ def test_llama8b_layer_projections_full_size():
         del Wf
 
 
-def test_projection_beyond_2_31_elements():
-    # N x K = 32768 x 65536 = 2^31 weights (1 GiB of codes): every index in the
-    # fused loaders must be 64-bit. Sampled outputs: y[:, n] needs row n of W,
-    # dX[:, k] needs column k of W.
+def test_projection_beyond_2_gib_of_codes():
+    # N x K = 65536 x 69632 = 4.56e9 weights: 2.28 GB of codes, past 2^31
+    # bytes, the size above which the pages report a backward that went wrong
+    # silently while the forward stayed right. The dX GEMM's weight loads are
+    # based at each 64-row reduction step (64-bit base, 32-bit offsets within
+    # the step), so rows past 2^31 bytes must read their own codes. Sampled
+    # outputs: y[:, n] needs row n of W, dX[:, k] needs column k of W over all
+    # 65536 rows.
     require_gpu()
-    M, N, K, r, alpha = 16, 32768, 65536, 8, 16.0
+    M, N, K, r, alpha = 16, 65536, 69632, 8, 16.0
+    assert N * K // 2 > 2 ** 31
     packed, absmax = synth.nf4_store(N * K, "big", device=DEV)
     x = synth.normal_bf16((M, K), 1.0, "big", "x", device=DEV)
     dy = synth.normal_bf16((M, N), 1.0, "big", "dy", device=DEV)

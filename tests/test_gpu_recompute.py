@@ -4,14 +4,17 @@ per layer by the streamer, as in the docs' "Layer Streaming" configuration).
 The forward keeps only each layer's input; the backward recomputes the layer
 from it with the weights already in the slot. Same kernels on the same bytes,
 so y, dx0, dA and dB must equal the saved-activation mode bitwise, streamed and
-resident, and with the slots reused at both turnarounds.
+resident, and with the slots reused at both turnarounds. The recompute run is
+also compared with the oracle itself, every layer teacher-forced: each layer's
+output from its kept input, and its input gradient, dA and dB from the GPU's
+upstream gradient (re-derived by 1-layer recompute-mode calls).
 """
 
 import pytest
 import torch
 
 from gpu_util import ql, require_gpu
-from stack_util import GpuStack, identical
+from stack_util import GpuStack, identical, teacher_forced
 
 pytestmark = pytest.mark.gpu
 
@@ -40,6 +43,7 @@ def test_recompute_equals_saved_mode_bitwise(pair):
     assert rc.step(resident=False, reuse=True) == ql.QL_OK
     b = rc.results()
     assert same_outputs(a, b)
+    teacher_forced(rc, b, full_saved=False)
     # the recompute-mode forward keeps exactly the layer inputs of the full mode
     _, per_full = ql.stream_layer_stack_saved_layout(full.cfg, M)
     _, per_rc = ql.stream_layer_stack_saved_layout(rc.cfg, M)

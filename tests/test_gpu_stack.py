@@ -1,30 +1,28 @@
 """GPU parity of the layer-streamed stack (stream_layer_stack_fwd / _bwd) through the C ABI.
 
 The pages require a streamed run to be bit-identical to a resident one, forward
-and backward stated separately; results are checked against the oracle
-end-to-end from the same seeded inputs (all rows for the SmolLM2 shape; sampled
-rows for the larger ones, which is exact because every stand-in layer is
-row-independent).
+and backward stated separately; results are checked against the oracle from
+the same seeded inputs.
 
 Tolerance. One layer agrees element-wise within 2e-2 (relative, with an
-rms-scaled floor), and stacks of up to 4 layers are held to that. Deeper, the
-bf16 rounding of activations (about 1e-4 normwise per layer) propagates: at 8
-layers the GPU stays within 1e-2 normwise of the bf16-faithful oracle, and 2e-2
-normwise is asserted there. At 30 layers the random-weight stand-in's backward
-is ill-conditioned (|dx0| grows about 30x over |dy|), so the bf16-faithful
-oracle itself lands about 24% (normwise) from the float64-exact gradient; the
-GPU lands about 21% from it. There the check is accuracy parity: the GPU must be
-at least as close to the float64-exact result as the bf16-faithful oracle, up
-to a factor 1.25 and 1e-3.
+rms-scaled floor). A deep stack of bf16 layers is ill-conditioned end to end:
+at 30 layers the random-weight stand-in's backward amplifies |dx0| about 30x
+over |dy|, and the bf16-faithful oracle itself lands about 24% (normwise) from
+the float64-exact gradient. So every layer of a deep stack is checked
+teacher-forced (tests/stack_util.py): the oracle layer runs on the GPU's own
+input to that layer, and all of the layer's outputs (saved activations, output,
+input gradient, dA, dB) are compared element-wise at 2e-2. Stacks of up to 8
+layers are also held to 2e-2 normwise end to end; deeper, the end-to-end
+normwise distance is printed as a report only.
 """
 
 import numpy as np
 import pytest
 import torch
 
-from gpu_util import DEV, as_accurate, close, close_norm, f64, ql, require_gpu
+from gpu_util import DEV, close, close_norm, f64, ql, require_gpu
 from oracle import stack as ostack
-from stack_util import GpuStack, identical
+from stack_util import GpuStack, LayerChain, identical, teacher_forced
 
 pytestmark = pytest.mark.gpu
 
@@ -35,32 +33,27 @@ def smol():
     return GpuStack("smollm2_stack")
 
 
+def _end_to_end_report(s, got, tag):
+    """Normwise distance of y and dx0 from the bf16-faithful oracle run end to end (printed)."""
+    layers = s.oracle_layers()
+    h, saved = ostack.stack_fwd(layers, f64(s.x))
+    dx0, _ = ostack.stack_bwd(layers, saved, f64(s.dy))
+    ny = np.linalg.norm(f64(got["y"]) - h) / np.linalg.norm(h)
+    nd = np.linalg.norm(f64(got["dx"]) - dx0) / np.linalg.norm(dx0)
+    print(f"{tag}: end to end vs the faithful oracle, normwise: y {ny:.3g}, dx0 {nd:.3g}")
+    return ny, nd
+
+
 def test_smollm2_stack_matches_oracle(smol):
+    # all 30 layers teacher-forced, every output of each layer element-wise
     st = smol.step(resident=False, reuse=True)
     assert st == ql.QL_OK
     got = smol.results()
-    layers = smol.oracle_layers()
-    x, dy = f64(smol.x), f64(smol.dy)
-    h, saved = ostack.stack_fwd(layers, x)
-    # every saved activation of the first layer, element-wise
-    for name in ("n1", "q", "k", "v", "h_mid", "n2", "gate", "up", "act",
-                 "U_q", "U_k", "U_v", "U_o", "U_gate", "U_up", "U_down"):
-        close(f64(smol.saved_tensor(0, name)), saved[0][name], what=f"L0:{name}")
-    close(f64(smol.saved_tensor(1, "h_in")), saved[1]["h_in"], what="L1:h_in")
-    he, saved_e = ostack.stack_fwd(layers, x, mode="exact")
-    nrm_y = close_norm(f64(got["y"]), h, what="y")
-    as_accurate(f64(got["y"]), h, he, what="y")
-    dx0, grads = ostack.stack_bwd(layers, saved, dy)
-    dxe, grads_e = ostack.stack_bwd(layers, saved_e, dy, mode="exact")
-    eg, ef = as_accurate(f64(got["dx"]), dx0, dxe, what="dx0")
-    for li in range(len(layers)):
-        for p in ql.PROJ:
-            if p in ("q", "k"):
-                assert torch.count_nonzero(got["dA"][li][p]) == 0 and torch.count_nonzero(got["dB"][li][p]) == 0
-                continue
-            for j, nm in ((0, "dA"), (1, "dB")):
-                as_accurate(f64(got[nm][li][p]), grads[li][p][j], grads_e[li][p][j], what=f"L{li}:{p}:{nm}")
-    print(f"y normwise vs faithful {nrm_y:.2e}; dx0 vs exact: gpu {eg:.2e}, faithful {ef:.2e}")
+    teacher_forced(smol, got)
+    # end to end the bf16 roundings of 30 layers add up; measured 0.004 (y)
+    # and 0.013 (dx0) normwise from the faithful oracle, held to 2e-2
+    ny, nd = _end_to_end_report(smol, got, "smollm2 30 layers")
+    assert ny <= 2e-2 and nd <= 2e-2
 
 
 def test_smollm2_8_layers_normwise():
@@ -71,17 +64,13 @@ def test_smollm2_8_layers_normwise():
     layers = s.oracle_layers()
     x, dy = f64(s.x), f64(s.dy)
     h, saved = ostack.stack_fwd(layers, x)
-    he, saved_e = ostack.stack_fwd(layers, x, mode="exact")
     close_norm(f64(got["y"]), h, what="y")
     dx0, grads = ostack.stack_bwd(layers, saved, dy)
-    dxe, grads_e = ostack.stack_bwd(layers, saved_e, dy, mode="exact")
     close_norm(f64(got["dx"]), dx0, what="dx0")
-    as_accurate(f64(got["dx"]), dx0, dxe, what="dx0")
     for li in range(8):
         for p in ("v", "o", "gate", "up", "down"):
             for j, nm in ((0, "dA"), (1, "dB")):
                 close_norm(f64(got[nm][li][p]), grads[li][p][j], what=f"L{li}:{p}:{nm}")
-                as_accurate(f64(got[nm][li][p]), grads[li][p][j], grads_e[li][p][j], what=f"L{li}:{p}:{nm}")
 
 
 def test_streamed_equals_resident_bitwise(smol):
@@ -186,6 +175,45 @@ def test_accumulate_adds_the_step_gradients(smol):
             assert torch.equal(acc["dB"][li][p], base["dB"][li][p] + base["dB"][li][p])
 
 
+class poisoned:
+    """Slot poisoning on for the block (ql_debug_poison_slots)."""
+
+    def __enter__(self):
+        ql.ql_debug_poison_slots(1)
+
+    def __exit__(self, *exc):
+        ql.ql_debug_poison_slots(0)
+
+
+def test_poisoned_slots_training_loop_equals_resident(smol):
+    # every slot is filled with 0xFF before each copy into it: a kernel that
+    # read a slot before its copy landed would produce NaN; the training loop
+    # (both turnarounds reused, no host sync between calls) must still equal
+    # the resident step bitwise
+    with poisoned():
+        assert smol.fwd() == ql.QL_OK
+        for _ in range(2):
+            assert smol.bwd(reuse=True) == ql.QL_OK
+            assert smol.fwd(reuse=True) == ql.QL_OK
+        assert smol.bwd(reuse=True) == ql.QL_OK
+        streamed = smol.results()
+    assert torch.isfinite(streamed["y"].float()).all() and torch.isfinite(streamed["dx"].float()).all()
+    smol.step(resident=True)
+    assert identical(streamed, smol.results())
+
+
+def test_poisoning_refuses_capture_and_switches_off(smol):
+    with poisoned():
+        with pytest.raises(ql.QlError) as e:
+            ql.stream_layer_stack_step_capture(smol.cfg, smol.store, smol.lora, smol.x, smol.dy, smol.M, smol.y,
+                                               smol.saved, smol.dx, smol.dA, smol.dB, 0, 1, smol.slots, smol.ws,
+                                               smol.compute, smol.copy)
+        assert e.value.status == ql.QL_ERR_UNSUPPORTED
+    with pytest.raises(ql.QlError) as e:
+        ql.ql_debug_poison_slots(2)
+    assert e.value.status == ql.QL_ERR_ARG
+
+
 def test_qk_grads_zero_and_the_rest_nonzero_at_layer0(smol):
     smol.step()
     got = smol.results()
@@ -212,13 +240,18 @@ def test_deeper_ring_training_loop_equals_resident(smol8, nb):
     # l % n, the prefetch runs n - 1 layers ahead and each turnaround reuses n
     # layers: fwd, then (bwd, fwd) pairs reusing the slots, must equal the
     # resident step bitwise
+    # (the loop runs with the slots poisoned before every copy: a read ahead
+    # of a copy in the deeper ring would show as NaN)
     smol8.set_buffers(nb)
-    assert smol8.fwd() == ql.QL_OK
-    for _ in range(2):
+    with poisoned():
+        assert smol8.fwd() == ql.QL_OK
+        for _ in range(2):
+            assert smol8.bwd(reuse=True) == ql.QL_OK
+            assert smol8.fwd(reuse=True) == ql.QL_OK
         assert smol8.bwd(reuse=True) == ql.QL_OK
-        assert smol8.fwd(reuse=True) == ql.QL_OK
-    assert smol8.bwd(reuse=True) == ql.QL_OK
-    streamed = smol8.results()
+        streamed = smol8.results()
+    if nb == 8:  # the deepest ring against the oracle, every layer teacher-forced
+        teacher_forced(smol8, streamed)
     smol8.step(resident=True)
     assert identical(streamed, smol8.results())
     # and without reuse (every call copies its first n layers itself)
@@ -313,34 +346,29 @@ def test_stack_argument_errors(smol):
     assert e.value.status == ql.QL_ERR_ARG
 
 
-def _sampled_rows_check(s, rows, elementwise):
-    layers = s.oracle_layers()
-    x, dy = f64(s.x)[rows], f64(s.dy)[rows]
-    got = s.results()
-    h, saved = ostack.stack_fwd(layers, x)
-    dx0, _ = ostack.stack_bwd(layers, saved, dy)
-    if elementwise:
-        close(f64(got["y"])[rows], h, what="y rows")
-        close(f64(got["dx"])[rows], dx0, what="dx0 rows")
-    else:
-        close_norm(f64(got["y"])[rows], h, what="y rows")
-        for l in layers:
-            l.drop_cache()
-        he, saved_e = ostack.stack_fwd(layers, x, mode="exact")
-        dxe, _ = ostack.stack_bwd(layers, saved_e, dy, mode="exact")
-        as_accurate(f64(got["y"])[rows], h, he, what="y rows")
-        as_accurate(f64(got["dx"])[rows], dx0, dxe, what="dx0 rows")
-    return got
-
-
-def test_qwen3b_stack_full_size_sampled_rows():
-    # 36 layers, hidden 2048, intermediate 11008, kv 256, r 16, M = 512.
+@pytest.fixture(scope="module")
+def qwen():
+    # 36 layers, hidden 2048, intermediate 11008, kv 256, r 16, M = 512: the
+    # full Qwen2.5-3B-shaped stack, streamed, with the per-layer upstream
+    # gradients of its backward re-derived by the 1-layer chain
     require_gpu()
     s = GpuStack("qwen3b_stack", gen_device=DEV)
     assert s.step(resident=False, reuse=True) == ql.QL_OK
-    got = _sampled_rows_check(s, np.array([0, 311, 511]), elementwise=False)
-    assert s.step(resident=True) == ql.QL_OK
-    assert identical(got, s.results())
+    s.got = s.results()
+    s.dh = LayerChain(s).upstream(s.got)
+    return s
+
+
+@pytest.mark.parametrize("group", range(4))
+def test_qwen3b_stack_teacher_forced(qwen, group):
+    # layers 9 g .. 9 g + 8 of 36, each teacher-forced, every output element-wise
+    teacher_forced(qwen, qwen.got, layers=range(9 * group, 9 * group + 9), dh=qwen.dh)
+
+
+def test_qwen3b_stack_streamed_equals_resident(qwen):
+    assert qwen.step(resident=True) == ql.QL_OK
+    assert identical(qwen.got, qwen.results())
+    _end_to_end_report(qwen, qwen.got, "qwen3b 36 layers")
 
 
 def test_queued_steps_of_a_large_record_stack_equal_resident():
@@ -353,30 +381,56 @@ def test_queued_steps_of_a_large_record_stack_equal_resident():
     s = GpuStack("qwen3b_stack", L=4, gen_device=DEV)
     offs, _, _ = ql.stream_layer_stack_layout(s.cfg)
     assert offs[1] >= 8 << 20
-    assert s.fwd() == ql.QL_OK
-    for _ in range(2):
+    with poisoned():   # slots filled with 0xFF before every copy
+        assert s.fwd() == ql.QL_OK
+        for _ in range(2):
+            assert s.bwd(reuse=True) == ql.QL_OK
+            assert s.fwd(reuse=True) == ql.QL_OK
         assert s.bwd(reuse=True) == ql.QL_OK
-        assert s.fwd(reuse=True) == ql.QL_OK
-    assert s.bwd(reuse=True) == ql.QL_OK
-    streamed = s.results()
+        streamed = s.results()
     assert s.step(resident=True) == ql.QL_OK
     assert identical(streamed, s.results())
 
 
-def test_llama8b_shapes_at_bench_launch_config_sampled_rows():
-    # The 8B layer shapes at M = 2048 (the benchmark's launch configuration),
-    # 4 layers so the oracle can follow sampled rows through the whole stack.
+def test_llama8b_widths_at_bench_launch_config_teacher_forced():
+    # The 8B layer shapes at M = 2048 (the benchmark's launch configuration:
+    # the same kernels, tile geometry, split-K and batched adapter-gradient
+    # launches as each layer of the 32-layer step), 2 layers, all 2048 rows:
+    # every saved activation, both layer outputs, dx0 and dA, dB of v, o,
+    # gate, up and down element-wise against the oracle.
     require_gpu()
-    s = GpuStack("llama8b_stack", L=4, gen_device=DEV)
+    s = GpuStack("llama8b_stack", L=2, gen_device=DEV)
     assert s.step(resident=False, reuse=True) == ql.QL_OK
-    _sampled_rows_check(s, np.array([0, 1337, 2047]), elementwise=True)
+    got = s.results()
+    teacher_forced(s, got)
+    assert s.step(resident=True) == ql.QL_OK
+    assert identical(got, s.results())
 
 
 def test_llama8b_stack_full_streamed_equals_resident():
     # The benchmark workload itself: 32 layers, M = 2048, 3.93 GB pinned store.
+    # A streamed step allocates nothing: device memory in use is the caller's
+    # buffers, of which the frozen weights take the two slots (the pages'
+    # bounded-memory claim, here measured around the step).
     require_gpu()
     s = GpuStack("llama8b_stack", gen_device=DEV)
     assert s.step(resident=False, reuse=True) == ql.QL_OK
+    torch.cuda.synchronize()
+    in_use = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    free0 = torch.cuda.mem_get_info()[0]
+    assert s.step(resident=False, reuse=True) == ql.QL_OK
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    assert torch.cuda.max_memory_allocated() == in_use
+    assert free0 - free1 <= 64 << 20, (free0, free1)
+    offs, _, _ = ql.stream_layer_stack_layout(s.cfg)
+    assert s.slots.numel() == 2 * offs[1]
+    lora = sum(t.numel() * t.element_size() for d in s.lora for A, B in d.values() for t in (A, B))
+    grads = sum(t.numel() * 4 for d in s.dA + s.dB for t in d.values())
+    print(f"8B streamed step, device bytes: slots {s.slots.numel()} (2 records of {offs[1]}), saved "
+          f"{s.saved.numel()}, ws {s.ws.numel()}, lora {lora}, grads {grads}; store on host {s.store.numel()}; "
+          f"device free before/after the step {free0}/{free1}")
     a = s.results()
     assert torch.isfinite(a["y"].float()).all() and torch.isfinite(a["dx"].float()).all()
     assert s.step(resident=True) == ql.QL_OK

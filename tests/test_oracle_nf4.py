@@ -240,3 +240,41 @@ def test_dequant_bf16_table_form_equals_elementwise_definition():
     got = nf4.dequant_bf16(packed, absmax)
     assert np.array_equal(np.signbit(got), np.signbit(want))
     assert np.array_equal(got, want)
+
+
+def test_dequant_exact_is_the_exact_product():
+    # dequant_exact is the float64 reference behind the exact-mode stack: it
+    # must hold c[code] * absmax with no rounding at all, element by element,
+    # in the packed element order. Exact rationals decide, independently of
+    # float64: random codes and scales, plus zero, subnormal, smallest normal
+    # and the largest finite float32 scales.
+    from fractions import Fraction
+    g = np.random.default_rng(21)
+    nb = 48
+    codes = g.integers(0, 16, size=nb * nf4.BLOCK).astype(np.uint8)
+    codes[: 16] = np.arange(16)
+    absmax = (np.abs(g.standard_normal(nb)) * 0.05).astype(np.float32)
+    specials = np.array([0.0, 1e-45, 2.0 ** -140, 2.0 ** -126, 1.0, 3.4028235e38, 7.0e-3, 0.0271],
+                        np.float32)
+    absmax[: specials.size] = specials
+    got = nf4.dequant_exact(nf4.pack(codes), absmax)
+    assert got.dtype == np.float64 and got.shape == (codes.size,)
+    c = [Fraction(float(v)) for v in nf4.codebook()]
+    for i in range(codes.size):
+        want = c[codes[i]] * Fraction(float(absmax[i // nf4.BLOCK]))
+        assert Fraction(float(got[i])) == want, (i, codes[i], absmax[i // nf4.BLOCK])
+
+
+def test_dequant_exact_rounds_to_the_float32_and_bf16_dequants():
+    # a float32 x float32 product is exact in float64 (48 significant bits,
+    # exponents far inside float64's range), so rounding the exact product once
+    # gives the float32 dequant bitwise, and once more the bf16 one
+    g = np.random.default_rng(22)
+    n = 64 * 4096
+    packed = g.integers(0, 256, size=n // 2).astype(np.uint8)
+    absmax = np.abs(g.standard_normal(n // 64)).astype(np.float32) * np.float32(0.02)
+    absmax[::97] = np.float32(2.0 ** -130)   # subnormal products
+    ex = nf4.dequant_exact(packed, absmax)
+    f32 = nf4.dequant_f32(packed, absmax)
+    assert np.array_equal(ex.astype(np.float32).view(np.uint32), f32.view(np.uint32))
+    assert np.array_equal(nf4.round_bf16(ex.astype(np.float32).astype(np.float64)), nf4.dequant_bf16(packed, absmax))
