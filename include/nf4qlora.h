@@ -192,6 +192,23 @@ ql_status qlora_linear_bwd(const void* dy, const void* x, const void* u_saved, i
                            ql_nf4_weight W, ql_lora L, void* dx, float* dA, float* dB,
                            int32_t accumulate, void* ws, size_t ws_bytes, ql_stream s);
 
+/* qlora_linear_bwd_noalloc: exactly qlora_linear_bwd (same kernels, same
+ * bits) without a workspace argument, for callers that cannot allocate device
+ * memory: code recorded under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc. Its temporaries live in a fixed array of
+ * QL_NOALLOC_SCRATCH_BYTES in the library's code object on each device, held
+ * until the process ends; the call itself allocates nothing. A shape whose
+ * workspace (bwd_bytes of qlora_linear_workspace) exceeds that size is
+ * refused with QL_ERR_WORKSPACE before anything is enqueued. The scratch
+ * needs no clearing (every temporary is written before it is read) and keeps
+ * nothing between calls, but all calls on one device share it: calls that
+ * overlap on one device (concurrent streams, or host threads) race, so order
+ * them on one stream. */
+#define QL_NOALLOC_SCRATCH_BYTES (128u << 20)
+ql_status qlora_linear_bwd_noalloc(const void* dy, const void* x, const void* u_saved, int64_t M,
+                                   ql_nf4_weight W, ql_lora L, void* dx, float* dA, float* dB,
+                                   int32_t accumulate, ql_stream s);
+
 /* ----------------------------------------------------- layer-streamed stack
  * A stack of n_layers decoder-layer stand-ins, each
  *   n1 = RMSNorm(h); q,k,v = P_q,P_k,P_v(n1); a = repeat_kv(v);

@@ -31,8 +31,9 @@ EXPORTS = (
     "stream_layer_stack_layout", "stream_layer_stack_workspace", "stream_layer_stack_saved_layout",
     "stream_layer_stack_fwd", "stream_layer_stack_fwd_ref", "stream_layer_stack_bwd", "ql_profile_enable",
     "ql_profile_read", "stream_layer_stack_step_capture", "ql_step_graph_launch", "ql_step_graph_destroy",
-    "ql_debug_poison_slots",
+    "ql_debug_poison_slots", "qlora_linear_bwd_noalloc",
 )
+QL_NOALLOC_SCRATCH_BYTES = 128 << 20
 QL_KERNEL_GEMM_FWD, QL_KERNEL_GEMM_BWD, QL_KERNEL_GEMM_FWD_NARROW, QL_KERNEL_GEMM_BWD_NARROW = 0, 1, 2, 3
 QL_KERNEL_LORA_ROW, QL_KERNEL_LORA_COL, QL_KERNEL_DEQUANT = 4, 5, 6
 # kernel symbol of each profiling id (the names rocprofv3 reports): the fused
@@ -88,6 +89,7 @@ def load(path=LIB_PATH):
         "qlora_linear_workspace": (I32, [I64, I64, I64, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
         "qlora_linear_fwd": (I32, [P, I64, ql_nf4_weight, ql_lora, P, P, P, SZ, P]),
         "qlora_linear_bwd": (I32, [P, P, P, I64, ql_nf4_weight, ql_lora, P, P, P, I32, P, SZ, P]),
+        "qlora_linear_bwd_noalloc": (I32, [P, P, P, I64, ql_nf4_weight, ql_lora, P, P, P, I32, P]),
         "stream_layer_stack_layout": (I32, [ctypes.POINTER(ql_stack_cfg), P, P, ctypes.POINTER(SZ)]),
         "stream_layer_stack_workspace": (I32, [ctypes.POINTER(ql_stack_cfg), I64, ctypes.POINTER(SZ),
                                                ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
@@ -214,6 +216,12 @@ def qlora_linear_bwd(dy, x, u_saved, M, W, L, dx, dA, dB, accumulate, ws, stream
     return _check(load().qlora_linear_bwd(_ptr(dy), _ptr(x), _ptr(u_saved), M, W.c(), L.c(), _ptr(dx), _ptr(dA),
                                           _ptr(dB), int(accumulate), _ptr(ws),
                                           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def qlora_linear_bwd_noalloc(dy, x, u_saved, M, W, L, dx, dA, dB, accumulate, stream=None):
+    """qlora_linear_bwd with its temporaries in the library's fixed per-device scratch."""
+    return _check(load().qlora_linear_bwd_noalloc(_ptr(dy), _ptr(x), _ptr(u_saved), M, W.c(), L.c(), _ptr(dx),
+                                                  _ptr(dA), _ptr(dB), int(accumulate), _stream(stream)))
 
 
 @dataclass

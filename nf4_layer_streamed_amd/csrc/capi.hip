@@ -831,6 +831,31 @@ static ql_status run_linear_bwd(const void* dy, const void* x, const void* u_sav
   return launch_colc(grads, scratch, scratch_bytes, st);
 }
 
+// The workspace of qlora_linear_bwd_noalloc: a fixed array in the library's
+// code object, one per device, held until the process ends. In host code the
+// array's name stands for a host-side shadow, not device memory, so it is
+// used only to ask the runtime for the device address (on each device, on the
+// first call there, with that device current); kernels get that address.
+static __device__ __align__(256) uint8_t scratch[QL_NOALLOC_SCRATCH_BYTES];
+static std::mutex g_scratch_mu;
+static uint8_t* g_scratch_dev[64] = {};
+
+static ql_status noalloc_scratch(uint8_t** out) {
+  int dev = 0;
+  QL_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return set_error(QL_ERR_UNSUPPORTED, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    QL_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || (uintptr_t)p % 256)
+      return set_error(QL_ERR_HIP, "qlora_linear_bwd_noalloc: scratch address %p is not 256-byte aligned", p);
+    g_scratch_dev[dev] = (uint8_t*)p;
+  }
+  *out = g_scratch_dev[dev];
+  return QL_OK;
+}
+
 }  // namespace ql
 
 using namespace ql;
@@ -1019,6 +1044,26 @@ ql_status qlora_linear_bwd(const void* dy, const void* x, const void* u_saved, i
     QL_TRY(check_ptr(fn, "ws", ws, 256));
   }
   return run_linear_bwd(dy, x, u_saved, M, W, L, dx, dA, dB, accumulate, (uint8_t*)ws, lw, (hipStream_t)s);
+}
+
+ql_status qlora_linear_bwd_noalloc(const void* dy, const void* x, const void* u_saved, int64_t M,
+                                   ql_nf4_weight W, ql_lora L, void* dx, float* dA, float* dB,
+                                   int32_t accumulate, ql_stream s) {
+  clear_error();
+  const char* fn = "qlora_linear_bwd_noalloc";
+  QL_TRY(check_linear_bwd(fn, dy, x, u_saved, M, W, L, dx, dA, dB, accumulate));
+  LinearWs lw = linear_ws(M, W.N, W.K, L.r);
+  uint8_t* ws = nullptr;
+  if (M > 0) {
+    if (lw.bwd > (size_t)QL_NOALLOC_SCRATCH_BYTES)
+      return set_error(QL_ERR_WORKSPACE,
+                       "%s: M %lld, N %lld, K %lld, r %d needs %zu bytes of scratch, more than the fixed %zu "
+                       "(qlora_linear_bwd takes a workspace of any size)",
+                       fn, (long long)M, (long long)W.N, (long long)W.K, (int)L.r, lw.bwd,
+                       (size_t)QL_NOALLOC_SCRATCH_BYTES);
+    QL_TRY(noalloc_scratch(&ws));
+  }
+  return run_linear_bwd(dy, x, u_saved, M, W, L, dx, dA, dB, accumulate, ws, lw, (hipStream_t)s);
 }
 
 ql_status stream_layer_stack_layout(const ql_stack_cfg* cfg, int64_t* layer_offsets, int64_t* proj_offsets,

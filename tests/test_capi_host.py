@@ -190,3 +190,18 @@ def test_profile_read_refuses_unknown_kernel_ids():
     n, ms, work = ql.ql_profile_read(ql.QL_KERNEL_DEQUANT)   # nothing recorded: zeros, no GPU work
     assert n == 0 and ms == 0.0 and work == 0.0
 
+
+def test_noalloc_backward_refuses_shapes_beyond_its_scratch():
+    # qlora_linear_bwd_noalloc has a fixed scratch of QL_NOALLOC_SCRATCH_BYTES;
+    # a shape needing more is refused before any device work (here: the
+    # transposed B of a 2^21-row weight at r = 64 alone is 256 MiB)
+    lib()
+    M, N, K, r = 16, 1 << 21, 64, 64
+    assert ql.qlora_linear_workspace(M, N, K, r)[1] > ql.QL_NOALLOC_SCRATCH_BYTES
+    assert ql.qlora_linear_workspace(2048, 14336, 4096, 16)[1] <= ql.QL_NOALLOC_SCRATCH_BYTES
+    t = torch.zeros(256, dtype=torch.uint8)
+    W = ql.NF4Weight(t, t.view(torch.float32), N, K)
+    L = ql.Lora(t, t, r, 128.0)
+    with pytest.raises(ql.QlError) as e:
+        ql.qlora_linear_bwd_noalloc(t, t, t, M, W, L, t, t.view(torch.float32), t.view(torch.float32), 0, stream=0)
+    assert e.value.status == ql.QL_ERR_WORKSPACE and "scratch" in ql.ql_last_error()
