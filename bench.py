@@ -205,6 +205,7 @@ def small_stack_graph(ql, synth, torch, dev, steps=20, warmup=3):
     te = (time.perf_counter() - t0) / steps
     g = ql.stream_layer_stack_step_capture(cfg, store, lora, x, dy, M, y, saved, dx, dA, dB, 0, 1, slots, ws,
                                            compute, copy)
+    launches, graph_copies, _ = g.info()
     for _ in range(warmup):
         g.launch(compute)
     torch.cuda.synchronize()
@@ -214,9 +215,16 @@ def small_stack_graph(ql, synth, torch, dev, steps=20, warmup=3):
     torch.cuda.synchronize()
     tg = (time.perf_counter() - t0) / steps
     g.destroy()
+    rec = offs[1]
+    copies = 2 * (w["L"] - cfg.n_buffers)
+    pcie = copies * rec / tg / 1e9
     return dict(workload="smollm2_stack: 30 layers, hidden 576, intermediate 1536, kv 192, r8, M=512, streamed",
                 eager=dict(value=round(M / te, 1), ms_per_step=round(1000 * te, 3)),
-                graph=dict(value=round(M / tg, 1), ms_per_step=round(1000 * tg, 3)), unit="tok/s")
+                graph=dict(value=round(M / tg, 1), ms_per_step=round(1000 * tg, 3)), unit="tok/s",
+                kernel_launches_per_step=launches, us_per_launch=round(1e6 * tg / launches, 2),
+                copies_per_step=copies, record_bytes=int(rec),
+                pcie=dict(achieved=round(pcie, 2), peak=PCIE_PEAK_GBS, unit="GB/s", frac=round(pcie / PCIE_PEAK_GBS, 4),
+                          what="layer copies of the captured step over its time"))
 
 
 def qwen3b_stack(ql, synth, torch, dev, steps=10, warmup=2):
@@ -456,18 +464,108 @@ def cpu_baseline(rows=2048, layers=3):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    threads = cores
-    try:
-        from threadpoolctl import threadpool_info
-        info = threadpool_info()
-        if info:
-            threads = max(i.get("num_threads", 0) for i in info) or cores
-    except Exception:
-        pass
+    threads = _blas_threads(cores)
     return dict(value=rows * layers / (w["L"] * t), unit="tok/s", cores=threads, kind="oracle",
                 sample=f"layers 0..{layers - 1} of {w['L']}, {rows} of {w['M']} tokens, fwd+bwd bf16-faithful "
                        f"NumPy float64, {t:.1f} s; tok/s = {rows} / ({w['L']} x t / {layers})",
                 seconds=round(t, 2), host_cores=cores)
+
+
+def _blas_threads(default):
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        if info:
+            return max(i.get("num_threads", 0) for i in info) or default
+    except Exception:
+        pass
+    return default
+
+
+def cpu_baseline_configs(runs=3):
+    """The oracle, as it stands, on each smaller configuration in full (not a
+    sample), median of `runs` runs: wall seconds of one forward + backward and
+    the token rate. Inputs are the same seeded synthetic recipe as the GPU
+    runs; weight quantisation (offline on the pages) is outside the timing.
+
+    linear_pr1     one NF4 + LoRA linear, M=64, K=256, N=512, r=8
+    llama8b_layer  the seven projections of one 8B-shaped layer at M=512, each
+                   on its own x and dY (oracle.linear fwd + bwd per projection)
+    smollm2_stack  30 layers, hidden 576, M=512 (oracle.stack fwd + bwd)
+    qwen3b_stack   36 layers, hidden 2048, intermediate 11008, M=512
+    """
+    import numpy as np
+    import synth
+    from oracle import linear as olin
+    from oracle import nf4 as onf4
+    from oracle import stack as ostack
+
+    def med(fn):
+        ts = []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[len(ts) // 2], ts
+
+    out = {}
+    # linear_pr1
+    M, K, N, r, alpha = 64, 256, 512, 8, 16.0
+    inp = synth.linear_inputs(M, K, N, r, ("linear_pr1",))
+    pk, am = onf4.quantize(inp["W"].numpy().reshape(-1))
+    x, A, B, dy = (synth.as_f64(inp[k]) for k in ("x", "A", "B", "dy"))
+
+    def pr1():
+        y, U = olin.fwd(x, pk, am, N, K, A, B, alpha)
+        olin.bwd(dy, x, U, pk, am, N, K, A, B, alpha)
+    t, ts = med(pr1)
+    out["linear_pr1"] = dict(seconds=round(t, 4), runs=[round(v, 4) for v in ts], value=round(M / t, 1), unit="tok/s")
+    # llama8b_layer
+    w = synth.WORKLOADS["llama8b_layer"]
+    M, H, I, KV, r, alpha = (w[k] for k in ("M", "H", "I", "KV", "r", "alpha"))
+    projs = []
+    for p in synth.PROJ:
+        N, K = synth.proj_shape(p, H, I, KV)
+        pk, am = synth.nf4_store(N * K, "llama8b_layer", p)
+        li = synth.linear_inputs(M, K, N, r, ("llama8b_layer", p))
+        projs.append((N, K, pk.numpy(), am.numpy(), *(synth.as_f64(li[k]) for k in ("x", "A", "B", "dy"))))
+
+    def layer8b():
+        for N, K, pk, am, x, A, B, dy in projs:
+            y, U = olin.fwd(x, pk, am, N, K, A, B, alpha)
+            olin.bwd(dy, x, U, pk, am, N, K, A, B, alpha)
+    t, ts = med(layer8b)
+    out["llama8b_layer"] = dict(seconds=round(t, 3), runs=[round(v, 3) for v in ts], value=round(M / t, 2),
+                                unit="tok/s")
+    del projs
+    # the two streamed stacks
+    for name in ("smollm2_stack", "qwen3b_stack"):
+        w = synth.WORKLOADS[name]
+        L, M, H, I, KV, d, r, alpha = (w[k] for k in ("L", "M", "H", "I", "KV", "head_dim", "r", "alpha"))
+        inp = synth.stack_inputs(L, M, H, I, KV, r, (name, "cpu"))
+        x, dy = synth.as_f64(inp["x"]), synth.as_f64(inp["dy"])
+        layers = []
+        for ld in inp["layers"]:
+            weights = {p: (ld[p]["packed"].numpy(), ld[p]["absmax"].numpy()) for p in ostack.PROJ}
+            lora = {p: (synth.as_f64(ld[p]["A"]), synth.as_f64(ld[p]["B"])) for p in ostack.PROJ}
+            layers.append(ostack.Layer(H, I, KV, d, alpha, weights, lora))
+        del inp
+
+        def stack():
+            h, saved = ostack.stack_fwd(layers, x)
+            ostack.stack_bwd(layers, saved, dy)
+            for lay in layers:
+                lay.drop_cache()
+        t, ts = med(stack)
+        out[name] = dict(seconds=round(t, 2), runs=[round(v, 2) for v in ts], value=round(M / t, 2), unit="tok/s")
+        del layers
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return dict(configs=out, kind="oracle", runs=runs, cores=_blas_threads(cores), host_cores=cores,
+                what="bf16-faithful NumPy float64 oracle, each configuration in full, fwd + bwd, median of %d runs"
+                     % runs)
 
 
 def main():
@@ -601,12 +699,34 @@ def main():
     torch.cuda.synchronize()
     del calib, calib_dst
 
-    # standalone nf4_dequant of one layer's gate projection (14336 x 4096) to bf16
+    # standalone nf4_dequant, cold: one whole 8B-shaped layer per launch
+    # (218 M weights: 122.7 MB of codes and scales in, 436 MB of bf16 out),
+    # alternating between two layers' buffers, so every launch starts with its
+    # 559 MB outside the 256 MB Infinity Cache; and warm: one gate projection
+    # (150 MB in + out) back to back on the same buffers
+    nl = sum(n_ * k_ for n_, k_ in (cfg.proj_shape(p) for p in ql.PROJ))
+    dq_sets = []
+    for i in range(2):
+        pk_ = synth.nf4_store(nl, "dequant_cold", i, device=dev)
+        dq_sets.append((pk_[0], pk_[1], torch.empty(nl, dtype=torch.bfloat16, device=dev)))
+    for i in range(4):
+        pk_, am_, o_ = dq_sets[i % 2]
+        ql.nf4_dequant(pk_, am_, nl, o_)
+    torch.cuda.synchronize()
+    ql.ql_profile_enable(1)
+    for i in range(10):
+        pk_, am_, o_ = dq_sets[i % 2]
+        ql.nf4_dequant(pk_, am_, nl, o_)
+    torch.cuda.synchronize()
+    ql.ql_profile_enable(0)
+    n, kms, kb = ql.ql_profile_read(ql.QL_KERNEL_DEQUANT)
+    dequant_s_per_weight = kms * 1e-3 / (n * nl)
+    hbm["k_nf4_dequant"] = dict(hbm_entry(n, kms, kb, None),
+                                what="nf4_dequant of a whole 8B-shaped layer (%d weights) to bf16 per launch, "
+                                     "alternating between two layers' buffers (cold: 559 MB per launch)" % nl)
+    del dq_sets
     Ng, Kg = cfg.proj_shape("gate")
-    _, proj_offs, _ = ql.stream_layer_stack_layout(cfg)
-    po, ao = proj_offs["gate"]  # layer 0's record starts the store
-    gpk = store[po: po + Ng * Kg // 2].to(dev)
-    gam = store[ao: ao + Ng * Kg // 16].to(dev).view(torch.float32)
+    gpk, gam = synth.nf4_store(Ng * Kg, "dequant_warm", device=dev)
     gout = torch.empty(Ng * Kg, dtype=torch.bfloat16, device=dev)
     for _ in range(3):
         ql.nf4_dequant(gpk, gam, Ng * Kg, gout)
@@ -617,8 +737,9 @@ def main():
     torch.cuda.synchronize()
     ql.ql_profile_enable(0)
     n, kms, kb = ql.ql_profile_read(ql.QL_KERNEL_DEQUANT)
-    hbm["k_nf4_dequant"] = dict(hbm_entry(n, kms, kb, None),
-                                what="nf4_dequant of a %d x %d projection to bf16, back to back" % (Ng, Kg))
+    hbm["k_nf4_dequant_warm"] = dict(hbm_entry(n, kms, kb, None),
+                                     what="nf4_dequant of a %d x %d projection to bf16, 20 launches back to back on "
+                                          "the same buffers (150 MB, inside the Infinity Cache)" % (Ng, Kg))
     del gpk, gam, gout
 
     # same-session PCIe ceiling: one 1 GiB pinned host-to-device copy
@@ -641,6 +762,7 @@ def main():
                 copies_per_step=copies, record_bytes=rec)
 
     ring8 = with_ref = recompute = double_quant = small = qwen = layer512 = pr1 = dense = hbm_copy = None
+    fused_vs_unfused = None
     if not args.main_only:
         # the same step with a deeper slot ring (the docs' stream_buffers up to 8):
         # each turnaround reuses 8 layers, so 2 (L - 8) copies per step
@@ -725,6 +847,21 @@ def main():
         dense = dense_gemm_ceiling(torch, dev, M, w)
         hbm_copy = hbm_copy_ceiling(torch, dev)
         gemm_all["vs_dense_bf16"] = round(gemm_all["tflops"] / dense["tflops"], 4)
+        # the unfused alternative: each layer's weights dequantised to bf16 in
+        # HBM by nf4_dequant (cold rate above) before its forward GEMMs and
+        # again before its dX GEMMs (q and k have none), then dense bf16 GEMMs
+        # at the same-session hipBLASLt rate over the same FLOPs
+        w_fwd = sum(n_ * k_ for n_, k_ in (cfg.proj_shape(p) for p in ql.PROJ))
+        w_bwd = sum(n_ * k_ for n_, k_ in (cfg.proj_shape(p) for p in ("v", "o", "gate", "up", "down")))
+        deq_ms = 1000.0 * dequant_s_per_weight * L * (w_fwd + w_bwd)
+        dense_ms = 1000.0 * (gemm_flop / args.steps) / (dense["tflops"] * 1e12)
+        fused_vs_unfused = dict(
+            fused_gemm_ms_per_step=round(gemm_ms_per_step, 3),
+            unfused_ms_per_step=round(deq_ms + dense_ms, 3), unfused_dequant_ms=round(deq_ms, 3),
+            unfused_dense_gemm_ms=round(dense_ms, 3), unfused_over_fused=round((deq_ms + dense_ms) / gemm_ms_per_step, 4),
+            what="per step at M=2048: the fused NF4 GEMMs (kernel timing) against nf4_dequant of every layer before "
+                 "its forward and again before its dX GEMMs (%d + %d weights per layer, cold dequant rate) plus dense "
+                 "bf16 GEMMs of the same FLOPs at the same-session hipBLASLt rate" % (w_fwd, w_bwd))
 
     resident = None
     if not args.no_resident:
@@ -736,10 +873,13 @@ def main():
                         tflops=round(step_flop / (rt / args.steps) / 1e12, 1))
         del store_dev
 
-    cpu = None
+    cpu = cpu_configs = None
     if not args.no_cpu_baseline:
         log("bench: cpu_baseline (oracle on a bounded sample)")
         cpu = cpu_baseline()
+        if not args.main_only:
+            log("bench: oracle timings of the smaller configurations (in full, median of 3)")
+            cpu_configs = cpu_baseline_configs()
 
     out = {
         "metric": "tok/s fwd+bwd, 8B-shape NF4 streamed QLoRA stack; NF4 GEMM % MFMA peak",
@@ -771,6 +911,7 @@ def main():
         "roofline": roofline,
         "hbm_kernels": hbm,
         "dense_bf16_gemm": dense,
+        "fused_vs_unfused": fused_vs_unfused,
         "hbm_copy_ceiling": hbm_copy,
         "pcie": pcie,
         "ring8": ring8,
@@ -783,6 +924,7 @@ def main():
         "linear_pr1": pr1,
         "resident": resident,
         "cpu_baseline": cpu,
+        "cpu_baseline_configs": cpu_configs,
     }
     print(json.dumps(out), flush=True)
 

@@ -31,7 +31,7 @@ EXPORTS = (
     "stream_layer_stack_layout", "stream_layer_stack_workspace", "stream_layer_stack_saved_layout",
     "stream_layer_stack_fwd", "stream_layer_stack_fwd_ref", "stream_layer_stack_bwd", "ql_profile_enable",
     "ql_profile_read", "stream_layer_stack_step_capture", "ql_step_graph_launch", "ql_step_graph_destroy",
-    "ql_debug_poison_slots", "qlora_linear_bwd_noalloc",
+    "ql_debug_poison_slots", "qlora_linear_bwd_noalloc", "ql_step_graph_info",
 )
 QL_NOALLOC_SCRATCH_BYTES = 128 << 20
 QL_KERNEL_GEMM_FWD, QL_KERNEL_GEMM_BWD, QL_KERNEL_GEMM_FWD_NARROW, QL_KERNEL_GEMM_BWD_NARROW = 0, 1, 2, 3
@@ -103,6 +103,7 @@ def load(path=LIB_PATH):
                                                   ctypes.POINTER(ctypes.c_void_p)]),
         "ql_step_graph_launch": (I32, [P, P]),
         "ql_step_graph_destroy": (I32, [P]),
+        "ql_step_graph_info": (I32, [P, ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I64)]),
         "stream_layer_stack_bwd": (I32, [ctypes.POINTER(ql_stack_cfg), P, SZ, P, P, I64, P, SZ, P, P, P,
                                          I32, I32, P, SZ, P, SZ, P, P]),
         "ql_profile_enable": (I32, [I32]),
@@ -337,6 +338,12 @@ class StepGraph:
 
     def launch(self, stream=None):
         return _check(load().ql_step_graph_launch(self._h, _stream(stream)))
+
+    def info(self):
+        """-> (kernel launches, copies, all nodes) of one replay."""
+        k, c, n = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(load().ql_step_graph_info(self._h, ctypes.byref(k), ctypes.byref(c), ctypes.byref(n)))
+        return k.value, c.value, n.value
 
     def destroy(self):
         if self._h:

@@ -1404,6 +1404,26 @@ ql_status ql_step_graph_launch(ql_step_graph g, ql_stream stream) {
   return QL_OK;
 }
 
+ql_status ql_step_graph_info(ql_step_graph g, int64_t* kernels, int64_t* copies, int64_t* nodes) {
+  clear_error();
+  if (!g || !g->graph) return set_error(QL_ERR_ARG, "ql_step_graph_info: graph is NULL");
+  size_t n = 0;
+  QL_HIP_CHECK(hipGraphGetNodes(g->graph, nullptr, &n));
+  std::vector<hipGraphNode_t> all(n);
+  if (n) QL_HIP_CHECK(hipGraphGetNodes(g->graph, all.data(), &n));
+  int64_t k = 0, c = 0;
+  for (size_t i = 0; i < n; ++i) {
+    hipGraphNodeType t;
+    QL_HIP_CHECK(hipGraphNodeGetType(all[i], &t));
+    if (t == hipGraphNodeTypeKernel) ++k;
+    if (t == hipGraphNodeTypeMemcpy) ++c;
+  }
+  if (kernels) *kernels = k;
+  if (copies) *copies = c;
+  if (nodes) *nodes = (int64_t)n;
+  return QL_OK;
+}
+
 ql_status ql_step_graph_destroy(ql_step_graph g) {
   clear_error();
   if (!g) return QL_OK;

@@ -93,3 +93,14 @@ def test_capture_refusals(sm):
         assert e.value.status == ql.QL_ERR_UNSUPPORTED
     finally:
         ql.ql_profile_enable(0)
+
+
+def test_graph_info_counts_the_step(sm):
+    # one replay: the 2 (L - 2) layer copies of a step with both turnarounds
+    # reused, plus the device copy of x0 into the saved area, and every kernel
+    g = capture(sm, 1)
+    k, c, n = g.info()
+    L = sm.cfg.n_layers
+    assert c == 2 * (L - 2) + 1
+    assert 10 * L <= k <= 60 * L and n >= k + c
+    g.destroy()
