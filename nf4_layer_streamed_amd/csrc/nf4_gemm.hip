@@ -623,8 +623,6 @@ __device__ __forceinline__ int bt_off(int n, int k) {
 // consecutive rows hit distinct banks), then the absmax of 64 rows x 4 blocks.
 template <int BN>
 constexpr int bwd_raw_bytes() { return 64 * (BN / 2) + 1024; }
-template <int BN>
-constexpr int bwd_lds() { return 2 * A_TILE + 2 * bwd_raw_bytes<BN>() + 2 * (64 * BN * 2); }
 // By-value select among three uniform values (a ternary on lvalues would
 // select an address and keep the values in private memory).
 template <typename T>
@@ -646,11 +644,27 @@ __device__ __forceinline__ int raw_slot(int n, int c) {
 // columns k_base + (tile / tiles_m) BN; waves 2 x 2. Reduction order: for
 // each segment its 64-row weight steps, then the LoRA steps of all segments.
 //
-// Pipeline per reduction step s: the dY tile of step s + 1 (DMA, two stages)
-// and the raw codes and scales of step s + 2 (DMA, two stages) stream in
-// while step s's MFMAs run, and every thread decodes its share of step s + 1's
-// raw data into the other bf16 weight tile, interleaved with the MFMAs. One
-// barrier per step: each wave first waits for its own DMAs of the step.
+// LDS: two dY stages and two raw-code stages (the DMA targets) and two decoded
+// weight tiles, in separate arrays. The transposing reads of the weight tiles
+// then provably touch no DMA target, so the compiler does not wait for the
+// DMAs in flight before them, and each sub-step can read the next sub-step's
+// operands while its MFMAs run.
+//
+// Pipeline. Reduction step t's codes arrive by DMA during step t - 2, are
+// loaded into registers at the end of step t - 2, and are decoded during
+// sub-steps 0-2 of step t - 1 into the decoded tile of t; its dY tile is
+// DMAed from sub-step 3 of step t - 2. In step s, sub-step q reads the
+// operands of q + 1. One barrier per step, between sub-steps 2 and 3, where
+// each wave has first waited for its own DMAs and LDS operations: after it,
+// step s + 1's decoded tile and dY tile are complete, and no wave reads step
+// s's stages again, so sub-step 3 prefetches step s + 1's first operands and
+// DMAs step s + 2's dY tile into step s's stage.
+// The dY tile's 16-byte chunks are swizzled by f(r) = (r ^ (r >> 3)) mod 8,
+// as in the forward: a fragment read (16 lanes, 16 consecutive rows, one
+// chunk) then meets 16 distinct bank groups, where f(r) = r mod 8 would put
+// rows r and r + 8 on the same ones.
+constexpr bool BXS = true;
+
 template <int WNB>
 __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m, int tiles_total, int k_base) {
   constexpr int BN = 2 * WNB;
@@ -659,9 +673,17 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
   constexpr int SH = CPR == 8 ? 1 : 2;
   constexpr int RAW = bwd_raw_bytes<BN>();
   constexpr int DEC_BYTES = 64 * BN * 2;
-  constexpr int OFF_R = 2 * A_TILE, OFF_D = OFF_R + 2 * RAW;
   constexpr int ABS = 64 * (BN / 2);
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // one array per stage: with compile-time stages, a read of one stage
+  // provably misses a DMA in flight into the other
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a0[A_TILE], lds_a1[A_TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_r0[RAW], lds_r1[RAW];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b0[DEC_BYTES], lds_b1[DEC_BYTES];
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  auto stage_a = [&](auto si) -> uint8_t* { return decltype(si)::value ? lds_a1 : lds_a0; };
+  auto stage_r = [&](auto si) -> uint8_t* { return decltype(si)::value ? lds_r1 : lds_r0; };
+  auto stage_b = [&](auto si) -> uint8_t* { return decltype(si)::value ? lds_b1 : lds_b0; };
   const int t = threadIdx.x, lane = t & 63, g = lane >> 5, li = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w >> 1, wn = w & 1;
 
@@ -712,7 +734,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
 
   // dY tile (256 rows x 64 columns of segment sgA from nbA) into an A stage;
   // columns past the segment's N read as zeros (offset past the buffer).
-  const int arow = 8 * w + (lane >> 3), alc0 = dma_chunk<false>(lane, w, 0), alc1 = dma_chunk<false>(lane, w, 1);
+  const int arow = 8 * w + (lane >> 3), alc0 = dma_chunk<BXS>(lane, w, 0), alc1 = dma_chunk<BXS>(lane, w, 1);
   auto dma_a = [&](uint8_t* As) {
     const int64_t N = sel3(sgA, N0, N1, N2);
     const __amdgpu_buffer_rsrc_t yr = sel3(sgA, yr0, yr1, yr2);
@@ -754,9 +776,13 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
 
   // decode share of a thread: row dn, 64-column block dc (wide) or half dh of it (narrow)
   constexpr int NCH = BN == 256 ? 2 : 1;  // 16-byte code chunks per thread
+  constexpr int NW = 4 * NCH;             // code words (8 weights each) per thread per step
   const int dn = t & 63, dc = (t >> 6) & (BN / 64 - 1), dh = BN == 256 ? 0 : (t >> 7);
-  uint32_t dcode[4 * NCH];
+  uint32_t dcode[NW];
+  float dscale;
   Lut dlut;
+  // the thread's codes and block scale of one step into registers; the table
+  // is built from the scale later (dec_lut), so nothing waits for these reads
   auto dec_load = [&](const uint8_t* R) {
 #pragma unroll
     for (int h = 0; h < NCH; ++h) {
@@ -766,8 +792,9 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
       dcode[4 * h + 2] = v[2];
       dcode[4 * h + 3] = v[3];
     }
-    dlut = make_lut(*(const float*)(R + ABS + (dn * 4 + dc) * 4));
+    dscale = *(const float*)(R + ABS + (dn * 4 + dc) * 4);
   };
+  auto dec_lut = [&]() { dlut = make_lut(dscale); };
   // word e of the thread's codes -> 8 bf16 at columns 64 dc + 32 dh + 8 e
   auto dec_word = [&](uint8_t* Bd, int e) {
     const uint4 v = decode8(dcode[e], dlut);
@@ -783,15 +810,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
   // transposed-read coordinates: within each group of 16 lanes, lane 4 ra + cbq
   // addresses row ra (of four) and the 4-column piece cbq (of four)
   const int h16 = lane >> 4, s16 = lane & 15, ra = s16 >> 2, cbq = s16 & 3;
-  bf16x8_t af[4], an[4], bfr[4][NTW];
   auto read_a = [&](bf16x8_t (&fa)[4], const uint8_t* As, int q) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8_t*)(As + swz_a<false>(wm * 128 + i * 32 + li, 2 * q + g));
+    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8_t*)(As + swz_a<BXS>(wm * 128 + i * 32 + li, 2 * q + g));
   };
-  // Weight fragments of sub-step q, read transposed. The transposing LDS read
-  // carries no type information, and the compiler then waits for every LDS
-  // DMA in flight before it; all of a step's transposed reads are therefore
-  // issued before the step's DMAs.
+  // weight fragments of sub-step q, read transposed
   auto read_b = [&](bf16x8_t (&fb)[NTW], const uint8_t* Bs, int q) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
@@ -806,12 +829,12 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
       fb[j] = __builtin_bit_cast(bf16x8_t, v);
     }
   };
-  auto mfmas = [&](int q) {
+  auto mfmas = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[NTW]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[q][j], af[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
   auto barrier_all = [&]() {
     __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
@@ -819,55 +842,91 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
-  // one reduction step on A stage / weight tile s & 1; DO_A: DMA the next dY
-  // tile; DO_R: DMA the raw data two steps ahead; DO_DEC: decode the next step
-  auto step_body = [&](int s, auto da_c, auto dr_c, auto dec_c) {
-    constexpr bool DO_A = decltype(da_c)::value, DO_R = decltype(dr_c)::value, DO_DEC = decltype(dec_c)::value;
-    const uint8_t* As = smem + (s & 1) * A_TILE;
-    const uint8_t* Bs = smem + OFF_D + (s & 1) * DEC_BYTES;
-    uint8_t* Bd = smem + OFF_D + ((s + 1) & 1) * DEC_BYTES;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) read_b(bfr[q], Bs, q);
-    read_a(af, As, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (DO_A) dma_a(smem + ((s + 1) & 1) * A_TILE);
-    if (DO_R) dma_raw(smem + OFF_R + (s & 1) * RAW);
-    if (DO_DEC) dec_load(smem + OFF_R + ((s + 1) & 1) * RAW);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q < 3) read_a(an, As, q + 1);
-      if (DO_DEC) {
-#pragma unroll
-        for (int e = 0; e < NCH; ++e) dec_word(Bd, NCH * q + e);
+  // Operands of the current sub-step (af, bq) and of the next (an, bn).
+  bf16x8_t af[4], an[4], bq[NTW], bn[NTW];
+  // Step s on stage SI = s mod 2 (a compile-time constant). Every step runs
+  // the whole pipeline: it DMAs step s + 2's codes and dY tile, loads step
+  // s + 2's codes, decodes step s + 1 and prefetches its first operands. For
+  // the last two steps some of these steps do not exist: their DMAs read
+  // in-range bytes (of the last segment, or none at all) and the results go
+  // to stages that nothing reads afterwards, so no branch is needed.
+  auto step_body = [&](auto si_c) {
+    constexpr int SI = decltype(si_c)::value;
+    using Cur = std::integral_constant<int, SI>;
+    using Oth = std::integral_constant<int, 1 - SI>;
+    const uint8_t* As = stage_a(Cur{});
+    const uint8_t* Bs = stage_b(Cur{});
+    uint8_t* Bd = stage_b(Oth{});
+    auto sub = [&](auto q_c) {
+      constexpr int q = decltype(q_c)::value;
+      // words of step s + 1 decoded in this sub-step: 3, 3, 2 (wide) or 2, 1, 1
+      constexpr int e0 = (q * NW + 2) / 3, e1 = q < 3 ? ((q + 1) * NW + 2) / 3 : e0;
+      constexpr int nwr = e1 - e0;
+      constexpr int nr = 4 + 2 * NTW + (q == 3 ? NCH + 1 : 0);
+      constexpr int nd = q == 0 ? CPR / 4 + 1 : (q == 3 ? 8 : 0);
+      if (q == 0) {
+        dma_raw(stage_r(Cur{}));  // step s + 2's codes (this stage's went to registers at step s - 2)
+        dec_lut();                // the table of step s + 1's codes
       }
-      mfmas(q);
-      __builtin_amdgcn_sched_barrier(0);
       if (q < 3) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = an[i];
+        read_a(an, As, q + 1);
+        read_b(bn, Bs, q + 1);
+      } else {
+        read_a(an, stage_a(Oth{}), 0);
+        read_b(bn, stage_b(Oth{}), 0);
+        dma_a(stage_a(Cur{}));     // step s + 2's dY into this step's stage
+        dec_load(stage_r(Cur{}));  // step s + 2's codes, landed at the barrier
       }
-    }
-    barrier_all();
+#pragma unroll
+      for (int e = e0; e < e1; ++e) dec_word(Bd, e);
+      mfmas(af, bq);
+      // the next operands' LDS reads first, then each MFMA followed by its
+      // share of the VALU and the DMAs, with the decoded words' LDS writes last
+      __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+#pragma unroll
+      for (int k = 0; k < 4 * NTW; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (k < nd) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        if (k >= 4 * NTW - nwr) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = an[i];
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) bq[j] = bn[j];
+      if (q == 2) barrier_all();
+    };
+    sub(std::integral_constant<int, 0>{});
+    sub(std::integral_constant<int, 1>{});
+    sub(std::integral_constant<int, 2>{});
+    sub(std::integral_constant<int, 3>{});
   };
 
   if (WS > 0) {
-    // prologue: dY tile 0 and raw steps 0 and 1 in flight; step 0 decoded
-    dma_a(smem);
-    dma_raw(smem + OFF_R);
-    if (WS > 1) dma_raw(smem + OFF_R + RAW);
+    // prologue: dY tiles and codes of steps 0 and 1 in, step 0 decoded, step
+    // 1's codes in registers, step 0's first operands read
+    dma_a(lds_a0);
+    dma_raw(lds_r0);
+    dma_a(lds_a1);
+    dma_raw(lds_r1);
     barrier_all();
-    dec_load(smem + OFF_R);
+    dec_load(lds_r0);
+    dec_lut();
 #pragma unroll
-    for (int e = 0; e < 4 * NCH; ++e) dec_word(smem + OFF_D, e);
+    for (int e = 0; e < NW; ++e) dec_word(lds_b0, e);
+    dec_load(lds_r1);
     barrier_all();
+    read_a(af, lds_a0, 0);
+    read_b(bq, lds_b0, 0);
     int st = 0;
-    for (; st + 2 < WS; ++st) step_body(st, std::true_type{}, std::true_type{}, std::true_type{});
-    if (st + 1 < WS) {
-      step_body(st, std::true_type{}, std::false_type{}, std::true_type{});
-      ++st;
+    for (; st + 1 < WS; st += 2) {
+      step_body(S0{});
+      step_body(S1{});
     }
-    step_body(st, std::false_type{}, std::false_type{}, std::false_type{});
+    if (st < WS) step_body(S0{});
   }
+  barrier_all();  // every wave done with the stages before the LoRA steps reuse them
 
   // LoRA steps: A = G_s, B rows j < r = s A_s[j][k0 ..], zero past r
   constexpr int UNITS = 64 * (BN / 64);
@@ -876,11 +935,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
   const int64_t dk = k0 + 64 * dblk;
   for (int sg = 0; sg < (sp == a.nsplit - 1 ? nseg : 0); ++sg) {
     const BwdSeg& S = a.seg[sg];
-    uint8_t* As = smem + (sg & 1) * A_TILE;
-    uint8_t* Bs = smem + OFF_D + (sg & 1) * DEC_BYTES;
+    uint8_t* As = (sg & 1) ? lds_a1 : lds_a0;
+    uint8_t* Bs = (sg & 1) ? lds_b1 : lds_b0;
     uint4 ar[8];
     load_a_rank(ar, S.G, a.r, M, m0, t);
-    store_a<false>(As, ar, t);
+    store_a<BXS>(As, ar, t);
     if (dthread) {
       const bool live = drow < a.r && dk < K;
       const uint4* src = (const uint4*)(S.A + (int64_t)drow * K + dk);
@@ -898,11 +957,10 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) read_b(bfr[q], Bs, q);
-#pragma unroll
     for (int q = 0; q < 4; ++q) {
       read_a(af, As, q);
-      mfmas(q);
+      read_b(bq, Bs, q);
+      mfmas(af, bq);
     }
   }
 
@@ -959,10 +1017,6 @@ ql_status ensure_attrs() {
   if (dev >= 0 && dev < 64 && !g_attr_set[dev]) {
     QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_fwd<64>, hipFuncAttributeMaxDynamicSharedMemorySize, fwd_lds<256>()));
     QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_fwd<32>, hipFuncAttributeMaxDynamicSharedMemorySize, fwd_lds<128>()));
-    QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_bwd<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     bwd_lds<256>()));
-    QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_bwd<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     bwd_lds<128>()));
     g_attr_set[dev] = true;
   }
   return QL_OK;
@@ -1220,10 +1274,10 @@ ql_status launch_bwd_tiles(const BwdArgs& a, bool wide, int64_t k_base, int64_t 
   if (prof) QL_TRY_PROF(profile_begin(&e0, &e1));
   const int grid = total * a.nsplit;
   if (wide)
-    hipExtLaunchKernelGGL(k_gemm_bwd<128>, dim3(grid), dim3(NT), bwd_lds<256>(), st, e0, e1, 0, a, tiles_m, total,
+    hipExtLaunchKernelGGL(k_gemm_bwd<128>, dim3(grid), dim3(NT), 0, st, e0, e1, 0, a, tiles_m, total,
                           (int)k_base);
   else
-    hipExtLaunchKernelGGL(k_gemm_bwd<64>, dim3(grid), dim3(NT), bwd_lds<128>(), st, e0, e1, 0, a, tiles_m, total,
+    hipExtLaunchKernelGGL(k_gemm_bwd<64>, dim3(grid), dim3(NT), 0, st, e0, e1, 0, a, tiles_m, total,
                           (int)k_base);
   QL_HIP_CHECK(hipGetLastError());
   if (prof) {
