@@ -561,10 +561,46 @@ static PtrKind pointer_kind(const void* p) {
 // but plausible layer, and the outputs would show it.
 static bool g_poison = false;
 
-// One layer record host -> device on the copy stream.
-static ql_status copy_record(void* dst, const void* src, size_t bytes, hipStream_t P) {
+// Host-to-device copy of a small page-locked record by the library's own
+// kernel. The runtime's copy of a pinned buffer is itself a kernel whose grid
+// grows with the bytes: a 2 MB record takes about 490 workgroups that hold
+// every CU while their loads cross PCIe, so the compute kernels that start
+// beside it (the next layer's first kernels) wait for it (SmolLM2-shaped
+// stack: its first RMSNorm of each layer took 47 us instead of 4). This
+// kernel keeps a fixed grid of 8 workgroups, each thread with 8 16-byte loads
+// in flight, which keeps the link busy for such records. A large record's
+// copy lasts milliseconds, and 8 workgroups held that long would keep 8 CUs
+// from every GEMM launched meanwhile (8B-shaped stack: 136 -> 155 ms per
+// step), so records of kSmallCopy bytes or more take the runtime's copy,
+// whose many short workgroups interleave with the GEMMs. Records are
+// multiples of 256 bytes.
+constexpr int kCopyWGs = 8, kCopyInflight = 8;
+constexpr size_t kSmallCopy = 8u << 20;
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void k_h2d(const u32x4v* __restrict__ src, u32x4v* __restrict__ dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + (kCopyInflight - 1) * stride < n; i += kCopyInflight * stride) {
+    u32x4v v[kCopyInflight];
+#pragma unroll
+    for (int k = 0; k < kCopyInflight; ++k) v[k] = __builtin_nontemporal_load(src + i + k * stride);
+#pragma unroll
+    for (int k = 0; k < kCopyInflight; ++k) dst[i + k * stride] = v[k];
+  }
+  for (; i < n; i += stride) dst[i] = __builtin_nontemporal_load(src + i);
+}
+
+// One layer record host -> device on the copy stream (a pageable store always
+// goes through the runtime's copy, which stages it).
+static ql_status copy_record(void* dst, const void* src, size_t bytes, hipStream_t P, bool pinned) {
   if (g_poison) QL_HIP_CHECK(hipMemsetAsync(dst, 0xFF, bytes, P));
-  QL_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, P));
+  if (pinned && bytes < kSmallCopy) {
+    hipLaunchKernelGGL(k_h2d, dim3(kCopyWGs), dim3(256), 0, P, (const u32x4v*)src, (u32x4v*)dst,
+                       (int64_t)(bytes / 16));
+    QL_HIP_CHECK(hipGetLastError());
+  } else {
+    QL_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, P));
+  }
   return QL_OK;
 }
 
@@ -1143,7 +1179,7 @@ static ql_status stack_fwd(const ql_stack_cfg* cfg, const StackCall& sc, const v
     if (!reuse_bwd_slots) {
       QL_TRY(ev.after_compute(C, P));
       for (int l = 0; l < nb && l < L; ++l) {
-        QL_TRY(copy_record(sl8 + l * rec, st8 + l * rec, rec, P));
+        QL_TRY(copy_record(sl8 + l * rec, st8 + l * rec, rec, P, !sc.pageable));
         QL_HIP_CHECK(hipEventRecord(ev.ready[l], P));
         have_ready[l] = true;
       }
@@ -1182,7 +1218,7 @@ static ql_status stack_fwd(const ql_stack_cfg* cfg, const StackCall& sc, const v
     if (!cfg->resident && l + nb < L) {
       QL_HIP_CHECK(hipEventRecord(ev.free_[slot], C));
       QL_HIP_CHECK(hipStreamWaitEvent(P, ev.free_[slot], 0));
-      QL_TRY(copy_record(sl8 + slot * rec, st8 + (size_t)(l + nb) * rec, rec, P));
+      QL_TRY(copy_record(sl8 + slot * rec, st8 + (size_t)(l + nb) * rec, rec, P, !sc.pageable));
       QL_HIP_CHECK(hipEventRecord(ev.ready[slot], P));
       have_ready[slot] = true;
     }
@@ -1292,7 +1328,7 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
     for (int i = 0; i < nb && i < L; ++i) {
       const int l = L - 1 - i;
       if (reuse_fwd_slots) continue;  // the forward left layers L-1 .. L-nb in their slots
-      QL_TRY(copy_record(sl8 + (l % nb) * rec, st8 + (size_t)l * rec, rec, P));
+      QL_TRY(copy_record(sl8 + (l % nb) * rec, st8 + (size_t)l * rec, rec, P, !sc.pageable));
       QL_HIP_CHECK(hipEventRecord(ev.ready[l % nb], P));
       have_ready[l % nb] = true;
     }
@@ -1330,7 +1366,7 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
     if (streamed && l - nb >= 0) {
       QL_HIP_CHECK(hipEventRecord(ev.free_[slot], C));
       QL_HIP_CHECK(hipStreamWaitEvent(P, ev.free_[slot], 0));
-      QL_TRY(copy_record(sl8 + slot * rec, st8 + (size_t)(l - nb) * rec, rec, P));
+      QL_TRY(copy_record(sl8 + slot * rec, st8 + (size_t)(l - nb) * rec, rec, P, !sc.pageable));
       QL_HIP_CHECK(hipEventRecord(ev.ready[slot], P));
       have_ready[slot] = true;
     }
