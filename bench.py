@@ -578,6 +578,8 @@ def main():
     ap.add_argument("--main-only", action="store_true",
                     help="time only the headline step (no ring8 / reference / recompute / double-quant / "
                          "small-stack / dense-GEMM lines), e.g. for counter runs")
+    ap.add_argument("--section", choices=("llama8b_layer_m512", "small_stack_graph", "qwen3b_stack", "linear_pr1"),
+                    help="run only this one extra line and print it as JSON (e.g. to profile one configuration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this benchmark runs on one GPU; --gpus {args.gpus} is not supported "
@@ -591,6 +593,11 @@ def main():
     ql.load()
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.section:
+        fn = {"llama8b_layer_m512": llama8b_layer_m512, "small_stack_graph": small_stack_graph,
+              "qwen3b_stack": qwen3b_stack, "linear_pr1": linear_pr1}[args.section]
+        print(json.dumps({args.section: fn(ql, synth, torch, dev)}), flush=True)
+        return
     w = synth.WORKLOADS["llama8b_stack"]
     M = w["M"]
     log("bench: building the 8B-shaped store")
@@ -856,12 +863,14 @@ def main():
         deq_ms = 1000.0 * dequant_s_per_weight * L * (w_fwd + w_bwd)
         dense_ms = 1000.0 * (gemm_flop / args.steps) / (dense["tflops"] * 1e12)
         fused_vs_unfused = dict(
-            fused_gemm_ms_per_step=round(gemm_ms_per_step, 3),
+            fused_gemm_ms_per_step_streamed=round(gemm_ms_per_step, 3),
             unfused_ms_per_step=round(deq_ms + dense_ms, 3), unfused_dequant_ms=round(deq_ms, 3),
-            unfused_dense_gemm_ms=round(dense_ms, 3), unfused_over_fused=round((deq_ms + dense_ms) / gemm_ms_per_step, 4),
-            what="per step at M=2048: the fused NF4 GEMMs (kernel timing) against nf4_dequant of every layer before "
-                 "its forward and again before its dX GEMMs (%d + %d weights per layer, cold dequant rate) plus dense "
-                 "bf16 GEMMs of the same FLOPs at the same-session hipBLASLt rate" % (w_fwd, w_bwd))
+            unfused_dense_gemm_ms=round(dense_ms, 3),
+            unfused_over_fused_streamed=round((deq_ms + dense_ms) / gemm_ms_per_step, 4),
+            what="per step at M=2048: the fused NF4 GEMMs (kernel timing, in the streamed step, where the layer "
+                 "copies share the CUs, and in the resident step) against nf4_dequant of every layer before its "
+                 "forward and again before its dX GEMMs (%d + %d weights per layer, cold dequant rate) plus dense bf16 "
+                 "GEMMs of the same FLOPs at the same-session hipBLASLt rate, both timed alone" % (w_fwd, w_bwd))
 
     resident = None
     if not args.no_resident:
@@ -869,8 +878,21 @@ def main():
         store_dev = store.to(dev)
         rcfg = ql.StackCfg(**{**cfg.__dict__, "resident": 1})
         rt, _, _ = timed(rcfg, store_dev, args.steps, 1, False)
+        # the fused GEMMs once more, in this copy-free step (kernel timing pass)
+        _, _, rprof = timed(rcfg, store_dev, args.steps, 1, True)
+        r_ms = sum(rprof[k][1] for k in ql.KERNEL_SYMBOLS) / args.steps
+        r_fl = sum(rprof[k][2] for k in ql.KERNEL_SYMBOLS) / args.steps
         resident = dict(value=round(M * args.steps / rt, 1), unit="tok/s", ms_per_step=round(1000 * rt / args.steps, 3),
-                        tflops=round(step_flop / (rt / args.steps) / 1e12, 1))
+                        tflops=round(step_flop / (rt / args.steps) / 1e12, 1),
+                        gemm_ms_per_step=round(r_ms, 3),
+                        gemm_all=dict(tflops=round(r_fl / (r_ms * 1e-3) / 1e12, 1),
+                                      frac=round(r_fl / (r_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)))
+        if dense is not None:
+            resident["gemm_all"]["vs_dense_bf16"] = round(resident["gemm_all"]["tflops"] / dense["tflops"], 4)
+        if fused_vs_unfused is not None:
+            # the copy-free comparison: fused GEMMs of the resident step
+            fused_vs_unfused["fused_gemm_ms_per_step_resident"] = round(r_ms, 3)
+            fused_vs_unfused["unfused_over_fused_resident"] = round(fused_vs_unfused["unfused_ms_per_step"] / r_ms, 4)
         del store_dev
 
     cpu = cpu_configs = None
