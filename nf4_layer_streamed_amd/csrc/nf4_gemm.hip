@@ -54,6 +54,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int NT = 256;
 constexpr int BM = 256;
@@ -189,6 +190,20 @@ __device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, int voff, int
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
+// A lane offset past every descriptor's range (buffer loads return zeros,
+// stores are dropped).
+constexpr uint32_t kPastRange = 0x80000000u;
+
+// s * v for 8 bf16 values, rounded back to bf16.
+__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float s) {
+  const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = pack_bf16x2(s * __builtin_bit_cast(float, wv[e] << 16), s * __builtin_bit_cast(float, wv[e] & 0xffff0000u));
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // Buffer-to-LDS DMA (gfx950): each lane's 16 bytes land at lds + 16 * lane.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
@@ -207,6 +222,16 @@ __device__ __forceinline__ int dma_chunk(int lane, int w, int odd) {
 // A tile of the LoRA step: rows of a [M x r] bf16 matrix, zero past r (outside the main loop).
 __device__ __forceinline__ void load_a_rank(uint4 (&ar)[8], const uint16_t* U, int r, int64_t M, int64_t m0,
                                             int t) {
+  if ((r & 7) == 0) {  // whole 16-byte groups: buffer loads, zero past M and past r, no branches
+    const __amdgpu_buffer_rsrc_t ur = rsrc(U + m0 * r, (M - m0) * r * 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = t + NT * i;
+      const int row = c >> 3, ch = c & 7;
+      ar[i] = bload16(ur, ch * 8 < r ? (row * r + ch * 8) * 2 : (int)kPastRange, 0);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = t + NT * i;
@@ -245,6 +270,50 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int q) {
   return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
+}
+
+// Epilogue stores of one 32-row block: lane value v[it] holds row it * RPI + rr
+// (of the block) and columns col .. col + 3 (float32). MODE 0 stores float32
+// partials, 1 bf16, 2 float32; with hres the bf16 residual (row stride ldr
+// elements) is added first. Output row stride ld elements. Offsets of lanes
+// with !col_ok lie past every descriptor's range (stores dropped, loads zero).
+// Branch-free, so the loads and stores issue back to back.
+template <int MODE, int NIT, int RPI>
+__device__ __forceinline__ void epilogue_rows(const f32x4_t (&v)[NIT], __amdgpu_buffer_rsrc_t orr,
+                                              __amdgpu_buffer_rsrc_t rrr, int rr, int col, bool col_ok, int ld,
+                                              bool hres, int ldr) {
+  constexpr uint32_t kPast = 0x80000000u;
+  constexpr int ESZ = MODE == 1 ? 2 : 4;
+  if constexpr (MODE == 0) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const uint32_t off = col_ok ? (uint32_t)(((it * RPI + rr) * ld + col) * 4) : kPast;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v[it]), orr, off, 0, 0);
+    }
+  } else {
+    uint2 rv[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const uint32_t off = col_ok ? (uint32_t)(((it * RPI + rr) * ldr + col) * 2) : kPast;
+      rv[it] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rrr, off, 0, 0));
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      float f[4] = {v[it][0], v[it][1], v[it][2], v[it][3]};
+      const float r[4] = {__builtin_bit_cast(float, rv[it].x << 16), __builtin_bit_cast(float, rv[it].x & 0xffff0000u),
+                          __builtin_bit_cast(float, rv[it].y << 16), __builtin_bit_cast(float, rv[it].y & 0xffff0000u)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = hres ? f[e] + r[e] : f[e];
+      const uint32_t off = col_ok ? (uint32_t)(((it * RPI + rr) * ld + col) * ESZ) : kPast;
+      if constexpr (MODE == 2)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4_t{__builtin_bit_cast(uint32_t, f[0]), __builtin_bit_cast(uint32_t, f[1]),
+                    __builtin_bit_cast(uint32_t, f[2]), __builtin_bit_cast(uint32_t, f[3])},
+            orr, off, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])}, orr, off, 0, 0);
+    }
+  }
 }
 
 // =============================================================== forward
@@ -538,12 +607,25 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
   // with a split reduction, in the last split only)
   if (a.r > 0 && sp == a.nsplit - 1) {
     uint4 lb[NTW][4];
+    if ((a.r & 7) == 0) {  // buffer loads, zero past N and past r, no branches
+      const __amdgpu_buffer_rsrc_t br = rsrc(S.B + n0 * a.r, (N - n0) * a.r * 2);
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int64_t n = n0 + w * WN + 32 * j + li;
+      for (int j = 0; j < NTW; ++j) {
+        const int nl = w * WN + 32 * j + li;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        lb[j][q] = n < N ? lora_row8(S.B + n * a.r, 32 * g + 8 * q, a.r, a.s) : make_uint4(0, 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+          const int j0 = 32 * g + 8 * q;
+          lb[j][q] = scale_bf16x8(bload16(br, j0 < a.r ? (nl * a.r + j0) * 2 : (int)kPastRange, 0), a.s);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int64_t n = n0 + w * WN + 32 * j + li;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          lb[j][q] = n < N ? lora_row8(S.B + n * a.r, 32 * g + 8 * q, a.r, a.s) : make_uint4(0, 0, 0, 0);
+      }
     }
     const uint8_t* As = A_of(2);
 #pragma unroll
@@ -565,37 +647,62 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_fwd(const FwdArgs a, int tiles_m
   // Epilogue. The products above are C = W X^T (the weight operand first), so
   // lane (li, g) of accumulator [i][j] holds output row m = m0 + 32 i + li and,
   // in entries 4 v .. 4 v + 3, the four consecutive columns
-  // n = n0 + w WN + 32 j + 8 v + 4 g + (0..3): one 8-byte bf16 store (16-byte
-  // float32) per group. N % 16 == 0, so a group is wholly inside or outside.
+  // n0 + w WN + 32 j + 8 v + 4 g + (0..3). Stored as they are, one store
+  // instruction would touch 32 rows with 16 or 32 bytes each. Instead each
+  // 32-row block of a wave's columns goes through LDS (stage 0's X tile, whose
+  // last reads precede the barrier of step KT - 2 and which no DMA targets
+  // after it) and comes back as whole row segments: lanes 16 r' + c read
+  // 16-byte chunk c of row r', so each store covers WN / 16 rows with
+  // WN * 4 (float32) or WN * 2 (bf16) contiguous bytes per row. Chunks are
+  // XOR-swizzled by row so the writes, 32 rows of one chunk, spread over the
+  // banks. N % 16 == 0, so a 4-column group is wholly inside or outside.
+  constexpr int CPRW = WN / 4;       // 16-byte chunks per staged row
+  constexpr int RPI = 64 / CPRW;     // rows per read instruction
+  uint8_t* E = A_of(0) + w * (32 * WN * 4);
+  const int rc = lane % CPRW, rr = lane / CPRW;
+  const int64_t n = n0 + w * WN + 4 * rc;
+  // Stores go through buffer descriptors based at each 32-row block, whose
+  // ranges end at the last valid element: rows past M are dropped by the
+  // hardware, lanes past column N get an offset beyond every range, and no
+  // store or residual load sits behind a branch, so they issue back to back
+  // with no per-row wait. Offsets stay below 32 rows of at most QL_MAX_DIM
+  // float32 columns.
+  const int mode = a.nsplit > 1 ? 0 : (a.out_f32 ? 2 : 1);  // partial, float32, bf16 (uniform)
+  const bool hres = mode != 0 && S.resid != nullptr;
+  const int esz = mode == 1 ? 2 : 4;
+  const int64_t ldo = mode == 0 ? N : S.ldo;  // elements per output row
+  const uint8_t* obase = mode == 0 ? (const uint8_t*)(a.partial + ppart + ((int64_t)sp * M + m0) * N)
+                                   : (const uint8_t*)S.out + (m0 * S.ldo + S.col0) * esz;
+  const uint8_t* rbase = hres ? (const uint8_t*)(S.resid + m0 * S.ldo + S.col0) : nullptr;
+  const bool n_ok = n < N;
+  auto epilogue = [&](auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+    f32x4_t fv[32 / RPI];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t m = m0 + 32 * i + li;
-    if (m >= M) continue;
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
-    for (int j = 0; j < NTW; ++j)
+      for (int j = 0; j < NTW; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t n = n0 + w * WN + 32 * j + 8 * v + 4 * g;
-        if (n >= N) continue;
-        const int64_t o = m * S.ldo + S.col0 + n;
-        float f[4] = {acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]};
-        if (a.nsplit > 1) {  // float32 partial of this split; the sum kernel finishes
-          *(float4*)(a.partial + ppart + ((int64_t)sp * M + m) * N + n) = make_float4(f[0], f[1], f[2], f[3]);
-          continue;
+        for (int v = 0; v < 4; ++v) {
+          const int c = 8 * j + 2 * v + g;
+          *(f32x4_t*)(E + li * (WN * 4) + ((c ^ (li & (CPRW - 1))) << 4)) =
+              f32x4_t{acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]};
         }
-        if (S.resid) {
-          const uint2 rv = *(const uint2*)(S.resid + o);
-          f[0] += __builtin_bit_cast(float, rv.x << 16);
-          f[1] += __builtin_bit_cast(float, rv.x & 0xffff0000u);
-          f[2] += __builtin_bit_cast(float, rv.y << 16);
-          f[3] += __builtin_bit_cast(float, rv.y & 0xffff0000u);
-        }
-        if (a.out_f32)
-          *(float4*)((float*)S.out + o) = make_float4(f[0], f[1], f[2], f[3]);
-        else
-          *(uint2*)((uint16_t*)S.out + o) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+#pragma unroll
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int row = it * RPI + rr;
+        fv[it] = *(const f32x4_t*)(E + row * (WN * 4) + ((rc ^ (row & (CPRW - 1))) << 4));
       }
-  }
+      const int64_t rows = M - m0 - 32 * i < 32 ? M - m0 - 32 * i : 32;
+      const int64_t span = rows > 0 ? (rows - 1) * ldo + N : 0;  // elements
+      const __amdgpu_buffer_rsrc_t orr = rsrc(obase + 32 * i * ldo * esz, span * esz);
+      const __amdgpu_buffer_rsrc_t rrr = rsrc(hres ? rbase + 32 * i * ldo * 2 : nullptr, hres ? span * 2 : 0);
+      epilogue_rows<MODE, 32 / RPI, RPI>(fv, orr, rrr, rr, (int)n, n_ok, (int)ldo, hres, (int)ldo);
+    }
+  };
+  if (mode == 0) epilogue(std::integral_constant<int, 0>{});
+  else if (mode == 1) epilogue(std::integral_constant<int, 1>{});
+  else epilogue(std::integral_constant<int, 2>{});
 }
 
 // =============================================================== backward dX
@@ -940,20 +1047,15 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
     uint4 ar[8];
     load_a_rank(ar, S.G, a.r, M, m0, t);
     store_a<BXS>(As, ar, t);
-    if (dthread) {
+    if (dthread) {  // buffer loads of A's rows, zero past r and past K, no branches
       const bool live = drow < a.r && dk < K;
-      const uint4* src = (const uint4*)(S.A + (int64_t)drow * K + dk);
+      const __amdgpu_buffer_rsrc_t ar_ = rsrc(S.A, (int64_t)a.r * K * 2);
+      const int base = live ? (int)((drow * K + dk) * 2) : (int)kPastRange;
+      uint4 lv[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint4 lv4 = live ? src[c] : make_uint4(0, 0, 0, 0);
-        const uint32_t wv[4] = {lv4.x, lv4.y, lv4.z, lv4.w};
-        uint32_t o[4];
+      for (int c = 0; c < 8; ++c) lv[c] = bload16(ar_, live ? base + 16 * c : (int)kPastRange, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          o[e] = pack_bf16x2(a.s * __builtin_bit_cast(float, wv[e] << 16),
-                             a.s * __builtin_bit_cast(float, wv[e] & 0xffff0000u));
-        *(uint4*)(Bs + bt_off<BN>(drow, 64 * dblk + 8 * c)) = make_uint4(o[0], o[1], o[2], o[3]);
-      }
+      for (int c = 0; c < 8; ++c) *(uint4*)(Bs + bt_off<BN>(drow, 64 * dblk + 8 * c)) = scale_bf16x8(lv[c], a.s);
     }
     __syncthreads();
 #pragma unroll
@@ -967,37 +1069,54 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
   // Epilogue. The products are C = W^T dY^T (weight operand first), so lane
   // (li, g) of accumulator [i][j] holds output row m = m0 + 128 wm + 32 i + li
   // and, in entries 4 v .. 4 v + 3, the four consecutive columns
-  // k = k0 + WNB wn + 32 j + 8 v + 4 g + (0..3). K % 64 == 0, so a group is
-  // wholly inside or outside.
+  // k0 + WNB wn + 32 j + 8 v + 4 g + (0..3). As in the forward, each 32-row
+  // block of a wave's columns is staged through LDS (the dY stages, free after
+  // the barrier below; waves 0, 1 in one, 2, 3 in the other) and stored as
+  // whole row segments of WNB * 4 (float32) or WNB * 2 (bf16) bytes. K % 64
+  // == 0, so a 4-column group is wholly inside or outside.
+  __syncthreads();  // every wave done with the LoRA steps' stages
+  constexpr int CPRW = WNB / 4;  // 16-byte chunks per staged row
+  constexpr int RPI = 64 / CPRW;  // rows per read instruction
+  uint8_t* E = (wm ? lds_a1 : lds_a0) + wn * (32 * WNB * 4);
+  const int rc = lane % CPRW, rr = lane / CPRW;
+  const int64_t k = k0 + wn * WNB + 4 * rc;
+  // buffer-descriptor stores per 32-row block, as in the forward
+  const int64_t mw = m0 + wm * 128;
+  const int mode = a.nsplit > 1 ? 0 : (a.out_f32 ? 2 : 1);  // partial, float32, bf16 (uniform)
+  const bool hres = mode != 0 && a.resid != nullptr;
+  const int esz = mode == 1 ? 2 : 4;
+  const uint8_t* obase = mode == 0 ? (const uint8_t*)(a.partial + ((int64_t)sp * M + mw) * K)
+                                   : (const uint8_t*)a.out + mw * K * esz;
+  const uint8_t* rbase = hres ? (const uint8_t*)(a.resid + mw * K) : nullptr;
+  const bool n_ok = k < K;
+  auto epilogue = [&](auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+    f32x4_t fv[32 / RPI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + wm * 128 + 32 * i + li;
-    if (m >= M) continue;
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < NTW; ++j)
+      for (int j = 0; j < NTW; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t k = k0 + wn * WNB + 32 * j + 8 * v + 4 * g;
-        if (k >= K) continue;
-        const int64_t o = m * K + k;
-        float f[4] = {acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]};
-        if (a.nsplit > 1) {  // float32 partial of this split; the sum kernel finishes the output
-          *(float4*)(a.partial + (int64_t)sp * M * K + o) = make_float4(f[0], f[1], f[2], f[3]);
-          continue;
+        for (int v = 0; v < 4; ++v) {
+          const int c = 8 * j + 2 * v + g;
+          *(f32x4_t*)(E + li * (WNB * 4) + ((c ^ (li & (CPRW - 1))) << 4)) =
+              f32x4_t{acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]};
         }
-        if (a.resid) {
-          const uint2 rv = *(const uint2*)(a.resid + o);
-          f[0] += __builtin_bit_cast(float, rv.x << 16);
-          f[1] += __builtin_bit_cast(float, rv.x & 0xffff0000u);
-          f[2] += __builtin_bit_cast(float, rv.y << 16);
-          f[3] += __builtin_bit_cast(float, rv.y & 0xffff0000u);
-        }
-        if (a.out_f32)
-          *(float4*)((float*)a.out + o) = make_float4(f[0], f[1], f[2], f[3]);
-        else
-          *(uint2*)((uint16_t*)a.out + o) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+#pragma unroll
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int row = it * RPI + rr;
+        fv[it] = *(const f32x4_t*)(E + row * (WNB * 4) + ((rc ^ (row & (CPRW - 1))) << 4));
       }
-  }
+      const int64_t rows = M - mw - 32 * i < 32 ? M - mw - 32 * i : 32;
+      const int64_t span = rows > 0 ? rows * K : 0;  // elements
+      const __amdgpu_buffer_rsrc_t orr = rsrc(obase + 32 * i * K * esz, span * esz);
+      const __amdgpu_buffer_rsrc_t rrr = rsrc(hres ? rbase + 32 * i * K * 2 : nullptr, hres ? span * 2 : 0);
+      epilogue_rows<MODE, 32 / RPI, RPI>(fv, orr, rrr, rr, (int)k, n_ok, (int)K, hres, (int)K);
+    }
+  };
+  if (mode == 0) epilogue(std::integral_constant<int, 0>{});
+  else if (mode == 1) epilogue(std::integral_constant<int, 1>{});
+  else epilogue(std::integral_constant<int, 2>{});
 }
 
 #define QL_TRY_PROF(expr)         \
