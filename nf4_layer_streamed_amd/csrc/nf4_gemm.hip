@@ -1293,6 +1293,14 @@ constexpr double kNarrowFwd = 0.7, kNarrowBwd = 0.85;
 // steps each, against 99 us on narrow tiles; the M=512 gate forward 97 us
 // split in two against 90.
 constexpr int kFwdMinSteps = 64;
+// A split on wide tiles whose slices are shorter than this many steps is
+// re-planned on narrow tiles when those leave at least half the chip idle:
+// twice the tiles, so half the split depth for the same workgroups, half the
+// float32 partials and twice the steps per slice. Whole calls at M = 512:
+// the 4096 x 4096 forward 46 us (narrow, 4 splits) against 56 (wide, 8),
+// the 1024 x 4096 forward 35 against 44, the 4096-column dX 62 against 68;
+// with 28-step slices (the 14336-row reductions) wide tiles stay ahead.
+constexpr int kShortSlice = 16;
 // 1 if re-cutting t wide tiles (t <= C) into tn narrow ones takes less time.
 int narrow_pays(int t, int tn, int C, double ratio) {
   const int wide_rounds = (t + C - 1) / C, narrow_rounds = (tn + C - 1) / C;
@@ -1326,9 +1334,20 @@ ql_status launch_gemm_fwd(const FwdArgs& a_in, hipStream_t st) {
     int64_t ntot = 0;
     for (int s = 0; s < a.nseg; ++s) ntot += a.seg[s].N;
     while (S > 1 && (size_t)S * (size_t)a.M * (size_t)ntot * 4 > a.partial_bytes) --S;
+    bool wide = true;
+    if (S > 1 && kt / S < kShortSlice && 2 * t128 <= C) {
+      int Sn = C / t128;
+      if (Sn > 8) Sn = 8;
+      while (Sn > 1 && kt < min_steps * Sn) --Sn;
+      while (Sn > 1 && (size_t)Sn * (size_t)a.M * (size_t)ntot * 4 > a.partial_bytes) --Sn;
+      if (Sn > 1) {
+        S = Sn;
+        wide = false;
+      }
+    }
     if (S > 1) {
       a.nsplit = S;
-      QL_TRY_PROF(launch_fwd_tiles(a, true, st));
+      QL_TRY_PROF(launch_fwd_tiles(a, wide, st));
       SumArgs sa{};
       sa.M = a.M;
       sa.nsplit = S;
@@ -1449,9 +1468,20 @@ ql_status launch_gemm_bwd(const BwdArgs& a_in, hipStream_t st) {
     if (ws < 32) S = 1;
     while (S > 1 && ws < min_steps * S) --S;
     while (S > 1 && (size_t)S * (size_t)a.M * (size_t)a.K * 4 > a.partial_bytes) --S;
+    bool wide = true;  // short slices: narrow tiles, as in the forward
+    if (S > 1 && ws / S < kShortSlice && 2 * t128 <= C) {
+      int Sn = C / t128;
+      if (Sn > cap) Sn = cap;
+      while (Sn > 1 && ws < min_steps * Sn) --Sn;
+      while (Sn > 1 && (size_t)Sn * (size_t)a.M * (size_t)a.K * 4 > a.partial_bytes) --Sn;
+      if (Sn > 1) {
+        S = Sn;
+        wide = false;
+      }
+    }
     if (S > 1) {
       a.nsplit = S;
-      QL_TRY_PROF(launch_bwd_tiles(a, true, 0, a.K, st));
+      QL_TRY_PROF(launch_bwd_tiles(a, wide, 0, a.K, st));
       const int64_t MK = a.M * a.K;
       int64_t grid = (MK / 4 + 255) / 256;
       if (grid > 4096) grid = 4096;
