@@ -469,16 +469,24 @@ __global__ __launch_bounds__(256) void k_colc_reduce(const ColArgs a) {
 }
 
 // ------------------------------------------------------------- misc
+// A thread writes 8 consecutive elements of one output row (16 bytes) and
+// gathers them from 8 input rows: rows % 8 == 0. Consecutive threads take
+// consecutive 8-element groups of the same output row, so the stores are
+// contiguous; the small input stays in cache across the gathers.
 __global__ __launch_bounds__(256) void k_transpose_bf16(const TransArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= a.end[a.n - 1]) return;
   int b = 0;
 #pragma unroll
   for (int i = 0; i < kMaxTrans - 1; ++i) b += (i < a.n - 1 && idx >= a.end[i]) ? 1 : 0;
-  const int64_t local = idx - (b ? a.end[b - 1] : 0);
-  const int64_t rows = a.rows[b], cols = a.cols[b];
-  const int64_t rr = local / cols, cc = local - rr * cols;
-  a.out[b][cc * rows + rr] = a.in[b][local];
+  const int64_t local = idx - (b ? a.end[b - 1] : 0);  // unit: 8 output elements
+  const int64_t rows = a.rows[b], cols = a.cols[b], g8 = rows / 8;
+  const int64_t c = local / g8, r0 = 8 * (local - c * g8);
+  const uint16_t* in = a.in[b] + r0 * cols + c;
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = (uint32_t)in[(2 * e) * cols] | ((uint32_t)in[(2 * e + 1) * cols] << 16);
+  *(uint4*)(a.out[b] + c * rows + r0) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 __global__ void k_zero_f32(float* p, int64_t n) {
@@ -763,9 +771,10 @@ ql_status launch_colc(ColArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
 
 ql_status launch_transpose_bf16(TransArgs a, hipStream_t st) {
   if (a.n < 1 || a.n > kMaxTrans) return set_error(QL_ERR_ARG, "transpose: %d matrices", a.n);
-  int64_t tot = 0;
+  int64_t tot = 0;  // in units of 8 output elements
   for (int i = 0; i < a.n; ++i) {
-    tot += a.rows[i] * a.cols[i];
+    if (a.rows[i] % 8) return set_error(QL_ERR_SHAPE, "transpose: rows (%lld) must be a multiple of 8", (long long)a.rows[i]);
+    tot += a.rows[i] / 8 * a.cols[i];
     a.end[i] = tot;
   }
   if (tot == 0) return QL_OK;

@@ -274,14 +274,15 @@ struct ColArgs {
 size_t colc_ws_bytes(int64_t M, int64_t C, int32_t np);
 ql_status launch_colc(ColArgs a, void* ws, size_t ws_bytes, hipStream_t st);
 
-// out_i = in_i^T (bf16 [rows x cols] -> [cols x rows]) for up to kMaxTrans matrices.
+// out_i = in_i^T (bf16 [rows x cols] -> [cols x rows], rows % 8 == 0, outputs
+// 16-byte aligned) for up to kMaxTrans matrices.
 constexpr int kMaxTrans = 6;
 struct TransArgs {
   int32_t n;
   const uint16_t* in[kMaxTrans];
   uint16_t* out[kMaxTrans];
   int64_t rows[kMaxTrans], cols[kMaxTrans];
-  int64_t end[kMaxTrans];  // launcher: cumulative element counts
+  int64_t end[kMaxTrans];  // launcher: cumulative counts of 8-element output groups
 };
 ql_status launch_transpose_bf16(TransArgs a, hipStream_t st);
 ql_status launch_zero_f32(float* p, int64_t n, hipStream_t st);
