@@ -287,16 +287,24 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
   auto S = [&](int i) { return (uint16_t*)(sv + SV.off[i]); };
   void* scratch = ws + WS.scratch;
   const uint16_t* h_in = S(QL_SAVED_H_IN);
-
-  QL_TRY(launch_rmsnorm_fwd(h_in, M, H, c->rms_eps, S(QL_SAVED_N1), st));
-  if (on) {  // LoRA down of q, k, v (they share n1)
+  // n = RMSNorm(h) and the LoRA down of the nseg projections that read n
+  // (first at p0): one launch that makes n as it contracts it when their
+  // columns fit one, else the standalone RMSNorm and a plain row launch
+  auto norm_down = [&](const uint16_t* h, int n_slot, int p0, int nseg) -> ql_status {
+    if (!on) return launch_rmsnorm_fwd(h, M, H, c->rms_eps, S(n_slot), st);
+    const bool fuse = r * nseg <= 64 && rowc_ws_bytes(M, H, r * nseg) == 0;
+    if (!fuse) QL_TRY(launch_rmsnorm_fwd(h, M, H, c->rms_eps, S(n_slot), st));
     RowArgs ra{};
     ra.nprob = 1;
+    ra.mode = fuse ? 3 : 0;
     RowProb& a = ra.p[0];
-    a.X = S(QL_SAVED_N1); a.M = M; a.K = H; a.ldx = H; a.r = r; a.nseg = 3;
-    for (int p = 0; p < 3; ++p) { a.Bt[p] = u16(lo[p].A); a.out[p] = S(QL_SAVED_U0 + p); }
-    QL_TRY(launch_rowc(ra, scratch, WS.scratch_bytes, st));
-  }
+    a.X = fuse ? h : S(n_slot); a.M = M; a.K = H; a.ldx = H; a.r = r; a.nseg = nseg;
+    a.Xout[0] = fuse ? S(n_slot) : nullptr; a.eps = c->rms_eps;
+    for (int p = 0; p < nseg; ++p) { a.Bt[p] = u16(lo[p0 + p].A); a.out[p] = S(QL_SAVED_U0 + p0 + p); }
+    return launch_rowc(ra, scratch, WS.scratch_bytes, st);
+  };
+
+  QL_TRY(norm_down(h_in, QL_SAVED_N1, QL_PROJ_Q, 3));  // q, k, v share n1
   {  // q | k | v in one launch
     FwdArgs a{};
     a.X = S(QL_SAVED_N1); a.M = M; a.K = H; a.ldx = H; a.r = r; a.s = s; a.nseg = 3;
@@ -332,17 +340,8 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     g.out = S(QL_SAVED_H_MID); g.N = H; g.ldo = H; g.resid = h_in;
     QL_TRY(launch_gemm_fwd(a, st));
   }
-  QL_TRY(launch_rmsnorm_fwd(S(QL_SAVED_H_MID), M, H, c->rms_eps, S(QL_SAVED_N2), st));
+  QL_TRY(norm_down(S(QL_SAVED_H_MID), QL_SAVED_N2, QL_PROJ_GATE, 2));  // gate, up share n2
   {  // gate | up
-    if (on) {
-      RowArgs ra{};
-      ra.nprob = 1;
-      RowProb& u = ra.p[0];
-      u.X = S(QL_SAVED_N2); u.M = M; u.K = H; u.ldx = H; u.r = r; u.nseg = 2;
-      u.Bt[0] = u16(lo[QL_PROJ_GATE].A); u.out[0] = S(QL_SAVED_U0 + QL_PROJ_GATE);
-      u.Bt[1] = u16(lo[QL_PROJ_UP].A); u.out[1] = S(QL_SAVED_U0 + QL_PROJ_UP);
-      QL_TRY(launch_rowc(ra, scratch, WS.scratch_bytes, st));
-    }
     FwdArgs a{};
     a.X = S(QL_SAVED_N2); a.M = M; a.K = H; a.ldx = H; a.r = r; a.s = s; a.nseg = 2;
     const int outs[2] = {QL_SAVED_GATE, QL_SAVED_UP};

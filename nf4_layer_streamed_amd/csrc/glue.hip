@@ -7,11 +7,6 @@
 namespace ql {
 namespace {
 
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
 // One wave per row, 8 elements per lane per chunk (H % 8 == 0): lane l
 // takes chunks l, l + 64, ... (NQL of them, the last ones masked when H is
 // not a multiple of 512). All of a lane's chunks are loaded before the first
@@ -35,23 +30,15 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const uint16_t* __restrict_
 #pragma unroll
   for (int i = 0; i < NQL; ++i) {
     if (lane + 64 * i >= nq) continue;
-    float f[8];
-    unpack8(v[i], f);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) ss += f[k] * f[k];
+    add_squares8(v[i], ss);
   }
-  ss = wave_sum(ss);
-  const float rs = 1.0f / sqrtf(ss / (float)H + eps);
+  const float rs = rms_scale(wave_sum(ss), H, eps);
   uint4* orow = (uint4*)(out + row * H);
 #pragma unroll
   for (int i = 0; i < NQL; ++i) {
     const int q = lane + 64 * i;
     if (q >= nq) continue;
-    float f[8];
-    unpack8(v[i], f);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) f[k] *= rs;
-    orow[q] = pack8(f);
+    orow[q] = scale8(v[i], rs);
   }
 }
 
@@ -119,22 +106,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd_long(const uint16_t* __rest
   const uint4* hr = (const uint4*)(h + row * H);
   const int64_t nq = H / 8;
   float ss = 0.f;
-  for (int64_t q = lane; q < nq; q += 64) {
-    float f[8];
-    unpack8(hr[q], f);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) ss += f[k] * f[k];
-  }
-  ss = wave_sum(ss);
-  const float rs = 1.0f / sqrtf(ss / (float)H + eps);
+  for (int64_t q = lane; q < nq; q += 64) add_squares8(hr[q], ss);
+  const float rs = rms_scale(wave_sum(ss), H, eps);
   uint4* orow = (uint4*)(out + row * H);
-  for (int64_t q = lane; q < nq; q += 64) {
-    float f[8];
-    unpack8(hr[q], f);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) f[k] *= rs;
-    orow[q] = pack8(f);
-  }
+  for (int64_t q = lane; q < nq; q += 64) orow[q] = scale8(hr[q], rs);
 }
 
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd_long(const uint16_t* __restrict__ h,

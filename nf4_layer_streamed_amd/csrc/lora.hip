@@ -77,14 +77,18 @@ __device__ __forceinline__ i16x4_t lds_tr(const uint8_t* p) {
 constexpr int RC_ROWS = 16;
 constexpr int RC_STEP = 128;  // reduction elements per wave step (4 MFMAs)
 constexpr int RC_WAVES = 4;
+static_assert(RC_ROWS % RC_WAVES == 0, "the RMSNorm statistics give each wave whole rows");
 
 // MODE 0: X is read. MODE 1: X = SwiGLU(gate, up) is made from Xin and
 // stored. MODE 2: dg, du are made from gate, up, dact and stored; column
 // groups 0 .. NCG/2-1 contract dg with Bt[0], the rest du with Bt[1].
+// MODE 3: X = RMSNorm(Xin = h) is made and stored: the workgroup first
+// computes its rows' statistics exactly as the standalone RMSNorm does (one
+// wave per row, the same sums), then scales each chunk it contracts.
 template <int NCG, int MODE>
 __global__ __launch_bounds__(64 * RC_WAVES) void k_rowc(const RowArgs a) {
   constexpr int W = RC_WAVES;
-  constexpr int NIN = MODE == 0 ? 1 : (MODE == 1 ? 2 : 3);  // operand streams loaded per chunk
+  constexpr int NIN = MODE == 1 ? 2 : (MODE == 2 ? 3 : 1);  // operand streams loaded per chunk
   constexpr int NCGS = MODE == 2 ? NCG / 2 : NCG;           // column groups per projection (modes 1, 2)
   __shared__ f32x4_t red[(W - 1) * NCG][64];
   // w is wave-uniform; readfirstlane tells the compiler, so the step loops stay scalar
@@ -108,10 +112,10 @@ __global__ __launch_bounds__(64 * RC_WAVES) void k_rowc(const RowArgs a) {
   const int64_t roff = (mrow ? m : 0) * P.ldx;
   const uint16_t* xin[NIN];
 #pragma unroll
-  for (int i = 0; i < NIN; ++i) xin[i] = (MODE == 0 ? P.X : P.Xin[i]) + roff;
+  for (int i = 0; i < NIN; ++i) xin[i] = (MODE == 0 || MODE == 3 ? P.X : P.Xin[i]) + roff;
   // output column of group c for this lane: projection sg, column j
   auto colmap = [&](int c, int& sg, int& j) -> bool {
-    if (MODE == 0) {
+    if (MODE == 0 || MODE == 3) {
       const int jt = 16 * c + s16;
       sg = jt < np ? jt / r : 0;
       j = jt < np ? jt - sg * r : 0;
@@ -130,6 +134,7 @@ __global__ __launch_bounds__(64 * RC_WAVES) void k_rowc(const RowArgs a) {
     colmap(c, sg, j);
     bcol[c] = pick3(sg, P.Bt[0], P.Bt[1], P.Bt[2]) + (int64_t)j * K;
   }
+  float rs = 0.f;  // MODE 3: the RMSNorm scale of this lane's row, m0 + lane % 16
   // Loads have no branches (a branch around them would make the compiler
   // wait for the prefetch too): reduction elements past K load element 0 and
   // are zeroed in both operands before use.
@@ -157,6 +162,9 @@ __global__ __launch_bounds__(64 * RC_WAVES) void k_rowc(const RowArgs a) {
       if (MODE == 1) {
         x0 = swiglu_act8(xa[0][q], xa[1][q]);
         if (in && mrow) *(uint4*)(P.Xout[0] + roff + k) = x0;
+      } else if (MODE == 3) {
+        x0 = scale8(xa[0][q], rs);
+        if (in && mrow) *(uint4*)(P.Xout[0] + roff + k) = x0;
       } else if (MODE == 2) {
         swiglu_grad8(xa[0][q], xa[1][q], xa[2][q], x0, x1);
         if (in && mrow) {
@@ -177,9 +185,39 @@ __global__ __launch_bounds__(64 * RC_WAVES) void k_rowc(const RowArgs a) {
   // two register sets take turns (no copies, which would wait for the
   // prefetch); a step past the end reloads the current one (cache hits)
   int64_t st = s_lo + w;
-  if (st < s_hi) {
-    uint4 xa0[NIN][4], xb0[NCG][4], xa1[NIN][4], xb1[NCG][4];
+  uint4 xa0[NIN][4], xb0[NCG][4], xa1[NIN][4], xb1[NCG][4];
+  if constexpr (MODE == 3) {
+    // the first chunk is in flight meanwhile (a load of any step stays in
+    // bounds); wave w sums rows w, w + W, ... of the tile, each in the order
+    // of the standalone kernel; rows past M repeat row M - 1 (never stored)
     load(st, xa0, xb0);
+    __shared__ float rsh[RC_ROWS];
+    constexpr int RPW = RC_ROWS / W;
+    const uint4* hr[RPW];
+    float ss[RPW];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int64_t mr = m0 + w + W * j;
+      hr[j] = (const uint4*)(P.X + (mr < M ? mr : M - 1) * P.ldx);
+      ss[j] = 0.f;
+    }
+    for (int64_t q = lane; q < K / 8; q += 64) {
+      uint4 v[RPW];
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) v[j] = hr[j][q];
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) add_squares8(v[j], ss[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const float v = rms_scale(wave_sum(ss[j]), K, P.eps);
+      if (lane == 0) rsh[w + W * j] = v;
+    }
+    __syncthreads();
+    rs = rsh[s16];
+  }
+  if (st < s_hi) {
+    if constexpr (MODE != 3) load(st, xa0, xb0);
     while (true) {
       load(st + W < s_hi ? st + W : st, xa1, xb1);
       mma(st, xa0, xb0);
@@ -549,7 +587,7 @@ double rowc_bytes(const RowArgs& a) {
     if (P.M <= 0) continue;
     const double M = (double)P.M, K = (double)P.K, np = (double)(P.r * P.nseg);
     const double xcols = P.n_rep > 0 ? K / P.n_rep : K;
-    const int nin = a.mode == 0 ? 1 : (a.mode == 1 ? 2 : 3), nout = a.mode;
+    const int nin = a.mode == 1 ? 2 : (a.mode == 2 ? 3 : 1), nout = a.mode == 3 ? 1 : a.mode;
     b += 2.0 * M * xcols * nin + 2.0 * M * K * nout + 2.0 * np * K + 2.0 * M * np;
     if (P.nsplit > 1) b += 8.0 * P.nsplit * M * np;
   }
@@ -584,7 +622,7 @@ size_t rowc_ws_bytes(int64_t M, int64_t K, int32_t np) {
 
 ql_status launch_rowc(RowArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
   if (a.nprob < 1 || a.nprob > kMaxRowProb) return set_error(QL_ERR_ARG, "row contraction: %d problems", a.nprob);
-  if (a.mode < 0 || a.mode > 2) return set_error(QL_ERR_ARG, "row contraction: mode %d", a.mode);
+  if (a.mode < 0 || a.mode > 3) return set_error(QL_ERR_ARG, "row contraction: mode %d", a.mode);
   for (int i = 0; i < a.nprob; ++i) {
     const RowProb& P = a.p[i];
     QL_TRY(check_row(P));
@@ -593,6 +631,9 @@ ql_status launch_rowc(RowArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
     if (a.mode == 2 && (P.nseg != 2 || P.n_rep > 0 || P.r > kSwigluBwdMaxR))
       return set_error(QL_ERR_ARG, "row contraction: the SwiGLU backward mode takes two projections of r <= %d",
                        kSwigluBwdMaxR);
+    if (a.mode == 3 && (P.n_rep > 0 || P.ldx != P.K || P.r * P.nseg > 64 || !P.Xout[0]))
+      return set_error(QL_ERR_ARG, "row contraction: the RMSNorm mode takes contiguous rows, no remap, at most 64 "
+                       "columns and an output");
   }
   // more than 64 columns: one launch per projection (keeps the operand
   // registers of a wave in bounds)
@@ -656,6 +697,14 @@ ql_status launch_rowc(RowArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
       case 2: launch_rowc_t<2, 1>(a, grid, st, e0, e1m); break;
       case 3: launch_rowc_t<3, 1>(a, grid, st, e0, e1m); break;
       case 4: launch_rowc_t<4, 1>(a, grid, st, e0, e1m); break;
+      default: return set_error(QL_ERR_UNSUPPORTED, "row contraction: %d column groups", ncg);
+    }
+  } else if (a.mode == 3) {
+    switch (ncg) {
+      case 1: launch_rowc_t<1, 3>(a, grid, st, e0, e1m); break;
+      case 2: launch_rowc_t<2, 3>(a, grid, st, e0, e1m); break;
+      case 3: launch_rowc_t<3, 3>(a, grid, st, e0, e1m); break;
+      case 4: launch_rowc_t<4, 3>(a, grid, st, e0, e1m); break;
       default: return set_error(QL_ERR_UNSUPPORTED, "row contraction: %d column groups", ncg);
     }
   } else {

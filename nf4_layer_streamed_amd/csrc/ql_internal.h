@@ -60,6 +60,29 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
                     pack_bf16x2(f[6], f[7]));
 }
 
+// RMSNorm statistics, one code path for the standalone kernels and the row
+// kernel that fuses them: a lane's sum of squares of its 8-element chunks
+// (added in chunk order), the wave's lanes combined by a fixed butterfly, and
+// the scale 1 / sqrt(mean + eps).
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ void add_squares8(uint4 q, float& ss) {
+  float f[8];
+  unpack8(q, f);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ss += f[k] * f[k];
+}
+__device__ __forceinline__ float rms_scale(float ss, int64_t H, float eps) { return 1.0f / sqrtf(ss / (float)H + eps); }
+__device__ __forceinline__ uint4 scale8(uint4 q, float rs) {
+  float f[8];
+  unpack8(q, f);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) f[k] *= rs;
+  return pack8(f);
+}
+
 // SwiGLU on 8 bf16 elements (one code path for the elementwise kernels and
 // the kernels that fuse it): act = bf16(g sig(g) u);
 // dg = bf16(dact u sig(g) (1 + g (1 - sig(g)))), du = bf16(dact g sig(g)).
@@ -230,8 +253,12 @@ struct RowProb {
   //  1: Xin = gate, up; X := act = swiglu(gate, up), stored to Xout[0]; nseg 1
   //  2: Xin = gate, up, dact; dg, du stored to Xout[0], Xout[1]; projection 0
   //     contracts dg, projection 1 du (nseg 2)
+  // RMSNorm producer mode:
+  //  3: X = h; X := rmsnorm(h) (unit gain, eps), stored to Xout[0] with the
+  //     bits of the standalone RMSNorm; no remap
   const uint16_t* Xin[3];
   uint16_t* Xout[2];
+  float eps;
   // ---- launcher
   float* part;  // float32 [nsplit][M][r * nseg] when nsplit > 1
   int32_t nsplit, tile0, rtile0;
