@@ -274,7 +274,10 @@ enum { QL_PROJ_Q = 0, QL_PROJ_K, QL_PROJ_V, QL_PROJ_O, QL_PROJ_GATE, QL_PROJ_UP,
 /* Store layout. layer_offsets (host int64 [n_layers + 1]) gets each record's
  * byte offset and the total; proj_offsets (host int64 [2 * QL_NPROJ], may be
  * NULL) gets, within a record, the byte offset of projection p's packed codes
- * at [2p] and of its absmax at [2p+1]. Every offset is a multiple of 256. */
+ * at [2p] and of its absmax at [2p+1]. Every offset is a multiple of 256.
+ * A record holds four contiguous weight groups, q|k|v, o, gate|up, down, each
+ * its projections' codes then their absmax; the streamer may copy a record
+ * group by group. */
 ql_status stream_layer_stack_layout(const ql_stack_cfg* cfg, int64_t* layer_offsets,
                                     int64_t* proj_offsets, size_t* store_bytes);
 

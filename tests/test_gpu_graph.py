@@ -105,3 +105,27 @@ def test_graph_info_counts_the_step(sm):
     assert c == 1 + 2 * (L - 2)
     assert 10 * L <= k <= 60 * L and n >= k + c
     g.destroy()
+
+
+def test_weight_group_copies_replay_equal_eager():
+    # 4 layers of Qwen2.5-3B widths (43 MB records): each pass's last copy goes
+    # by weight group (four copies), the rest whole. The captured step holds
+    # those copies and their group events; replays equal the eager step
+    # bitwise.
+    require_gpu()
+    s = GpuStack("qwen3b_stack", L=4, gen_device="cuda:0")
+    s.fwd()
+    s.bwd(reuse=True)
+    assert s.fwd(reuse=True) == ql.QL_OK
+    assert s.bwd(reuse=True) == ql.QL_OK
+    eager = s.results()
+    g = capture(s, 1)
+    for rep in range(2):
+        clobber(s)
+        g.launch(s.compute)
+        torch.cuda.synchronize()
+        assert identical(s.results(), eager), rep
+    k, c, n = g.info()
+    L = s.cfg.n_layers
+    assert c == 1 + 2 * (L - 2) + 2 * 3
+    g.destroy()

@@ -392,6 +392,31 @@ def test_queued_steps_of_a_large_record_stack_equal_resident():
     assert identical(streamed, s.results())
 
 
+@pytest.mark.parametrize("L,nb,recompute", [(3, 2, 0), (5, 3, 0), (4, 2, 1)])
+def test_weight_group_handoffs_equal_resident(L, nb, recompute):
+    # Stacks of records of 8 MiB or more copy each pass's last layer one
+    # weight group at a time (q|k|v, o, gate|up, down; the backward in
+    # reverse), and that layer starts each GEMM once its group has landed.
+    # With every group poisoned just before its copy, a GEMM that ran ahead of
+    # its group would read NaN: forward, (backward, forward) pairs reusing the
+    # slots, then a backward must equal the resident step bitwise. With 3
+    # slots the ring is deeper; with recomputation the backward's last layer
+    # first reruns its forward on the groups as they land.
+    require_gpu()
+    s = GpuStack("qwen3b_stack", L=L, gen_device=DEV, n_buffers=nb, recompute=recompute)
+    offs, _, _ = ql.stream_layer_stack_layout(s.cfg)
+    assert offs[1] >= 8 << 20
+    with poisoned():
+        assert s.fwd() == ql.QL_OK
+        for _ in range(2):
+            assert s.bwd(reuse=True) == ql.QL_OK
+            assert s.fwd(reuse=True) == ql.QL_OK
+        assert s.bwd(reuse=True) == ql.QL_OK
+        streamed = s.results()
+    assert s.step(resident=True) == ql.QL_OK
+    assert identical(streamed, s.results())
+
+
 def test_llama8b_widths_at_bench_launch_config_teacher_forced():
     # The 8B layer shapes at M = 2048 (the benchmark's launch configuration:
     # the same kernels, tile geometry, split-K and batched adapter-gradient
