@@ -1323,13 +1323,14 @@ ql_status launch_gemm_fwd(const FwdArgs& a_in, hipStream_t st) {
   // with at least kFwdMinSteps K-steps per slice when narrow tiles alone fill
   // at least half the chip, else at least 8 (whole calls at M=512: the 8B
   // down forward 95 us split against 141, k 43 against 76); reductions under
-  // 32 K-steps are not split.
+  // 24 K-steps are not split (the SmolLM2-shaped down forward, 24 steps on
+  // 10 tiles, in three slices: that stack's step 9.67 against 10.03 ms).
   if (a.partial && 2 * t256 <= C) {
     int S = C / t256;
     if (S > 8) S = 8;
     const int kt = (int)(a.K / BK);
     const int min_steps = 2 * t128 >= C ? kFwdMinSteps : 8;
-    if (kt < 32) S = 1;
+    if (kt < 24) S = 1;
     while (S > 1 && kt < min_steps * S) --S;
     int64_t ntot = 0;
     for (int s = 0; s < a.nseg; ++s) ntot += a.seg[s].N;
