@@ -175,8 +175,9 @@ def build_dq_store(ql, torch, cfg, store, dev):
 
 def small_stack_graph(ql, synth, torch, dev, steps=20, warmup=3):
     """The SmolLM2-shaped streamed stack (30 layers, hidden 576, M = 512): a
-    step issues about 1,400 kernels, so launches bound it. tok/s of eager steps
-    and of the same step captured once and replayed (stream_layer_stack_step_capture)."""
+    step issues about 700 short kernels, so their fixed costs bound it. tok/s
+    of eager steps and of the same step captured once and replayed
+    (stream_layer_stack_step_capture)."""
     w = synth.WORKLOADS["smollm2_stack"]
     M = w["M"]
     cfg, store, offs, lora, x, dy = build_inputs(ql, synth, torch, w, dev)

@@ -1,6 +1,6 @@
 """GPU checks of the captured training step (stream_layer_stack_step_capture).
 
-One step of the SmolLM2-shaped streamed stack (about 660 kernels, 57 copies)
+One step of the SmolLM2-shaped streamed stack (about 690 kernels, 57 copies)
 is captured once and replayed; every replay, interleaved with eager steps and
 host synchronisations, must equal the eager step bitwise. The first replay's
 results are also compared with the oracle, every layer teacher-forced.
