@@ -259,39 +259,52 @@ static LayerW layer_weights(const StackLayout& L, const uint8_t* base) {
   return w;
 }
 
-// The layer's weights in a slot (or the resident store). With double-quantised
-// scales, the seven blocks are first expanded into the workspace's float32
-// area (one launch, on the compute stream, after the layer's copy has landed)
-// and the GEMMs read the scales from there.
-static ql_status layer_weights_ready(const ql_stack_cfg* c, const StackLayout& L, const StackWs& WS,
-                                     const uint8_t* base, uint8_t* ws, hipStream_t st, LayerW& W) {
-  W = layer_weights(L, base);
-  if (!c->absmax_dq) return QL_OK;
+// Expansion of double-quantised scales into the workspace's float32 area for
+// the projections p with group_of[p] == g (g < 0: all seven).
+static DqExpandArgs dq_expand_args(const StackLayout& L, const StackWs& WS, const uint8_t* base, uint8_t* ws,
+                                   int g) {
   DqExpandArgs a{};
-  a.nblk = QL_NPROJ;
   int64_t cum = 0;
   for (int p = 0; p < QL_NPROJ; ++p) {
+    if (g >= 0 && kGroupOf[p] != g) continue;
     const int64_t nb = L.N[p] * (L.K[p] / 64);
     const DqLayout dl = dq_layout(nb);
-    a.src[p] = base + L.absmax_off[p];
-    a.scale_off[p] = dl.scale_off;
-    a.mean_off[p] = dl.mean_off;
-    a.dst[p] = (float*)(ws + WS.absx[p]);
+    const int i = a.nblk++;
+    a.src[i] = base + L.absmax_off[p];
+    a.scale_off[i] = dl.scale_off;
+    a.mean_off[i] = dl.mean_off;
+    a.dst[i] = (float*)(ws + WS.absx[p]);
     cum += nb;
-    a.end[p] = cum;
-    W.absmax[p] = a.dst[p];
+    a.end[i] = cum;
   }
-  return launch_dq_expand(a, st);
+  return a;
+}
+
+// The layer's weights in a slot (or the resident store). With double-quantised
+// scales the GEMMs read float32 scales from the workspace: all seven blocks
+// are expanded there in one launch once the layer's record has landed, or,
+// with by_group, group by group as each group lands (group_wait).
+static ql_status layer_weights_ready(const ql_stack_cfg* c, const StackLayout& L, const StackWs& WS,
+                                     const uint8_t* base, uint8_t* ws, hipStream_t st, LayerW& W,
+                                     bool by_group = false) {
+  W = layer_weights(L, base);
+  if (!c->absmax_dq) return QL_OK;
+  for (int p = 0; p < QL_NPROJ; ++p) W.absmax[p] = (const float*)(ws + WS.absx[p]);
+  return by_group ? QL_OK : launch_dq_expand(dq_expand_args(L, WS, base, ws, -1), st);
 }
 
 // A layer whose record lands one weight group at a time: before the GEMM
 // that reads group g (the only kernels that read the slot) the compute stream
-// waits for ready[g]. Null: the caller waited for the whole record.
+// waits for ready[g], then expands the group's double-quantised scales
+// (dq[g].nblk > 0). Null: the caller waited for the whole record.
 struct GroupReady {
   hipEvent_t ready[kGroups] = {};
+  DqExpandArgs dq[kGroups] = {};
 };
 static ql_status group_wait(const GroupReady* gr, int g, hipStream_t C) {
-  if (gr) QL_HIP_CHECK(hipStreamWaitEvent(C, gr->ready[g], 0));
+  if (!gr) return QL_OK;
+  QL_HIP_CHECK(hipStreamWaitEvent(C, gr->ready[g], 0));
+  if (gr->dq[g].nblk > 0) QL_TRY(launch_dq_expand(gr->dq[g], C));
   return QL_OK;
 }
 
@@ -1239,9 +1252,9 @@ static ql_status stack_fwd(const ql_stack_cfg* cfg, const StackCall& sc, const v
   bool have_ready[QL_MAX_BUFFERS] = {};
   // The pass's last copy lands one weight group at a time, and the last
   // layer starts each GEMM as soon as its group is in, instead of idling
-  // through the whole copy (records of 8 MiB or more with float32 scales;
-  // 8B-shaped stack at M = 2048: 133.1 against 134.8 ms per step).
-  const bool grouped = !cfg->resident && rec >= kThrottleRecord && !cfg->absmax_dq && L > nb;
+  // through the whole copy (records of 8 MiB or more; 8B-shaped stack at
+  // M = 2048: 133.1 against 134.8 ms per step).
+  const bool grouped = !cfg->resident && rec >= kThrottleRecord && L > nb;
   if (!cfg->resident) {
     QL_TRY(ev.create(nb, grouped));
     if (!reuse_bwd_slots) {
@@ -1262,11 +1275,14 @@ static ql_status stack_fwd(const ql_stack_cfg* cfg, const StackCall& sc, const v
       if (have_ready[slot]) QL_HIP_CHECK(hipStreamWaitEvent(C, ev.ready[slot], 0));
       base = sl8 + slot * rec;
     }
+    const bool by_group = grouped && l == L - 1;
     LayerW W;
-    QL_TRY(layer_weights_ready(cfg, sc.SL, sc.WS, base, w8, C, W));
+    QL_TRY(layer_weights_ready(cfg, sc.SL, sc.WS, base, w8, C, W, by_group));
     GroupReady gr;
     std::copy(ev.gready[slot], ev.gready[slot] + kGroups, gr.ready);
-    const GroupReady* grp = grouped && l == L - 1 ? &gr : nullptr;
+    for (int g = 0; g < kGroups && by_group && cfg->absmax_dq; ++g)
+      gr.dq[g] = dq_expand_args(sc.SL, sc.WS, base, w8, g);
+    const GroupReady* grp = by_group ? &gr : nullptr;
     if (lora) {
       uint8_t* svl = sv + (size_t)l * sc.SV.per_layer;
       uint16_t* h_out = (l + 1 < L) ? (uint16_t*)(sv + (size_t)(l + 1) * sc.SV.per_layer + sc.SV.off[QL_SAVED_H_IN])
@@ -1402,7 +1418,7 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
   bool have_ready[QL_MAX_BUFFERS] = {};
   // the pass's last copy (layer 0) by weight group, as in the forward, in the
   // order the backward reads them: down, gate|up, o, q|k|v
-  const bool grouped = streamed && rec >= kThrottleRecord && !cfg->absmax_dq && L > nb;
+  const bool grouped = streamed && rec >= kThrottleRecord && L > nb;
   if (streamed) {
     QL_TRY(ev.create(nb, grouped));
     if (!reuse_fwd_slots) QL_TRY(ev.after_compute(C, P));
@@ -1427,11 +1443,14 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
       base = sl8 + slot * rec;
     }
     uint16_t* out = (l == 0 && dx0) ? (uint16_t*)dx0 : (((L - 1 - l) & 1) ? dhB : dhA);
+    const bool by_group = grouped && l == 0;
     LayerW W;
-    QL_TRY(layer_weights_ready(cfg, sc.SL, sc.WS, base, w8, C, W));
+    QL_TRY(layer_weights_ready(cfg, sc.SL, sc.WS, base, w8, C, W, by_group));
     GroupReady gr;
     std::copy(ev.gready[slot], ev.gready[slot] + kGroups, gr.ready);
-    const GroupReady* grp = grouped && l == 0 ? &gr : nullptr;
+    for (int g = 0; g < kGroups && by_group && cfg->absmax_dq; ++g)
+      gr.dq[g] = dq_expand_args(sc.SL, sc.WS, base, w8, g);
+    const GroupReady* grp = by_group ? &gr : nullptr;
     const uint8_t* svl = sv + (size_t)l * sc.SV.per_layer;
     if (cfg->recompute) {
       // recompute the layer's activations from its saved input, with the

@@ -392,8 +392,8 @@ def test_queued_steps_of_a_large_record_stack_equal_resident():
     assert identical(streamed, s.results())
 
 
-@pytest.mark.parametrize("L,nb,recompute", [(3, 2, 0), (5, 3, 0), (4, 2, 1)])
-def test_weight_group_handoffs_equal_resident(L, nb, recompute):
+@pytest.mark.parametrize("L,nb,recompute,dq", [(3, 2, 0, 0), (5, 3, 0, 0), (4, 2, 1, 0), (4, 2, 0, 1)])
+def test_weight_group_handoffs_equal_resident(L, nb, recompute, dq):
     # Stacks of records of 8 MiB or more copy each pass's last layer one
     # weight group at a time (q|k|v, o, gate|up, down; the backward in
     # reverse), and that layer starts each GEMM once its group has landed.
@@ -401,9 +401,10 @@ def test_weight_group_handoffs_equal_resident(L, nb, recompute):
     # its group would read NaN: forward, (backward, forward) pairs reusing the
     # slots, then a backward must equal the resident step bitwise. With 3
     # slots the ring is deeper; with recomputation the backward's last layer
-    # first reruns its forward on the groups as they land.
+    # first reruns its forward on the groups as they land; with
+    # double-quantised scales each group's scales are expanded as it lands.
     require_gpu()
-    s = GpuStack("qwen3b_stack", L=L, gen_device=DEV, n_buffers=nb, recompute=recompute)
+    s = GpuStack("qwen3b_stack", L=L, gen_device=DEV, n_buffers=nb, recompute=recompute, absmax_dq=dq)
     offs, _, _ = ql.stream_layer_stack_layout(s.cfg)
     assert offs[1] >= 8 << 20
     with poisoned():
