@@ -426,7 +426,12 @@ def hbm_copy_ceiling(torch, dev, gib=2, reps=5):
 def gpu_clocks():
     """Current SCLK / MCLK of GPU 0 as rocm-smi reports them (None when it is
     unavailable)."""
+    import os
     import subprocess
+    # Under rocprofv3 a child inherits the profiler's preloaded library, which
+    # starts the GPU before rocm-smi's interpreter takes over the process.
+    if any(k.startswith("ROCPROF") for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return None
     try:
         out = subprocess.run(["rocm-smi", "-d", "0", "--showclocks", "--json"], capture_output=True, text=True,
                              timeout=20).stdout
