@@ -151,6 +151,33 @@ def test_stack_layout_sizes(name, L, H, I, KV, d, r):
     assert ws_r == ws + per + 512 * cfg.hidden * 2
 
 
+@pytest.mark.parametrize("absmax_dq", [0, 1])
+def test_stack_record_is_four_contiguous_weight_groups(absmax_dq):
+    # A record holds q|k|v, o, gate|up, down in that order, each group its
+    # projections' codes then their scales (float32 absmax, or the
+    # double-quantised block), every tensor 256-byte aligned, so that a group
+    # is one contiguous byte range (the streamer may copy a record group by
+    # group).
+    lib()
+    cfg = ql.StackCfg(2, 4096, 14336, 1024, 128, 16, 32.0, absmax_dq=absmax_dq)
+    offs, proj, _ = ql.stream_layer_stack_layout(cfg)
+
+    def up256(n):
+        return -(-n // 256) * 256
+
+    pos = 0
+    for group in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+        for p in group:  # codes, in order
+            N, K = cfg.proj_shape(p)
+            assert proj[p][0] == pos, p
+            pos += up256(N * K // 2)
+        for p in group:  # then scales, in order
+            N, K = cfg.proj_shape(p)
+            assert proj[p][1] == pos, p
+            pos += ql.nf4_dq_layout(N * K // 64)[2] if absmax_dq else up256(N * K // 64 * 4)
+    assert pos == offs[1]
+
+
 def test_stack_cfg_validation():
     lib()
     bad = [ql.StackCfg(0, 576, 1536, 192, 64, 8, 16.0), ql.StackCfg(2, 577, 1536, 192, 64, 8, 16.0),
