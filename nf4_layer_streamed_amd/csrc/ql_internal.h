@@ -266,7 +266,7 @@ struct RowProb {
 constexpr int kMaxRowProb = 2;
 struct RowArgs {
   int32_t nprob;
-  int32_t mode;  // 0: plain X; 1, 2: SwiGLU producers (see RowProb)
+  int32_t mode;  // 0: plain X; 1, 2: SwiGLU producers; 3: RMSNorm producer (see RowProb)
   RowProb p[kMaxRowProb];
 };
 // Largest rank the SwiGLU-backward producer mode takes (two projections'
