@@ -253,7 +253,9 @@ ql_status qlora_linear_bwd_noalloc(const void* dy, const void* x, const void* u_
  * same device has finished on the GPU, and a backward call likewise for the
  * previous backward. So at most one of each is queued, and the call's own
  * work stays asynchronous. Deeper device queues slow the hand-off between
- * the copy and compute streams.
+ * the copy and compute streams. With n_buffers == 2 the call also blocks
+ * the host, before it enqueues each layer, until the layer two back has
+ * finished on the GPU: the host stays at most two layers ahead.
  */
 #define QL_MAX_BUFFERS 8
 

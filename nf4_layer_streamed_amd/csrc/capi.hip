@@ -726,6 +726,39 @@ struct Events {
 // hides the host's enqueue time of their launch-bound steps (SmolLM2-shaped
 // stack, 2 MB records: 12.9 ms eager steps unthrottled, 13.3 throttled).
 constexpr size_t kThrottleRecord = 8u << 20;
+
+// Within such a call with two slots, the host also stays at most
+// kLayersAhead layers ahead of the GPU: before it enqueues a layer it waits
+// for the layer kLayersAhead back to finish. The Qwen2.5-3B-shaped stack (43
+// MB records, short layers) steps in 54.0 ms against 58-59 unlimited; the
+// 8B-shaped step is unchanged (133.1 against 133.2-133.8 ms). With deeper
+// rings every limit measured slower (8 slots: 112-115 against 107 ms; 3
+// slots: 131-133 against 129-130 ms), so they keep only the call-level wait.
+constexpr int kLayersAhead = 2;
+struct LayerAhead {
+  bool on = false;
+  hipEvent_t done[kLayersAhead] = {};
+  ql_status init(bool enable) {
+    on = enable;
+    for (int i = 0; i < kLayersAhead && on; ++i)
+      QL_HIP_CHECK(hipEventCreateWithFlags(&done[i], hipEventDisableTiming));
+    return QL_OK;
+  }
+  // before enqueueing the pass's layer number idx (0, 1, ... in pass order)
+  ql_status before(int idx) {
+    if (on && idx >= kLayersAhead) QL_HIP_CHECK(hipEventSynchronize(done[idx % kLayersAhead]));
+    return QL_OK;
+  }
+  // after enqueueing it (and its refill)
+  ql_status after(int idx, hipStream_t C) {
+    if (on) QL_HIP_CHECK(hipEventRecord(done[idx % kLayersAhead], C));
+    return QL_OK;
+  }
+  ~LayerAhead() {
+    for (int i = 0; i < kLayersAhead; ++i)
+      if (done[i]) (void)hipEventDestroy(done[i]);
+  }
+};
 struct InFlight {
   std::mutex mu;
   hipEvent_t done[64][2] = {};
@@ -1266,7 +1299,10 @@ static ql_status stack_fwd(const ql_stack_cfg* cfg, const StackCall& sc, const v
       }
     }
   }
+  LayerAhead ahead;
+  QL_TRY(ahead.init(throttle && nb == 2));
   for (int l = 0; l < L; ++l) {
+    QL_TRY(ahead.before(l));
     const int slot = l % nb;
     const uint8_t* base;
     if (cfg->resident) {
@@ -1316,6 +1352,7 @@ static ql_status stack_fwd(const ql_stack_cfg* cfg, const StackCall& sc, const v
         have_ready[slot] = true;
       }
     }
+    QL_TRY(ahead.after(l, C));
   }
   if (throttle) QL_TRY(inflight_mark(0, C));
   return sc.pageable ? QL_WARN_PAGEABLE_HOST : QL_OK;
@@ -1433,7 +1470,10 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
   uint16_t* dhA = (uint16_t*)(w8 + sc.WS.dhA);
   uint16_t* dhB = (uint16_t*)(w8 + sc.WS.dhB);
   const uint16_t* dh = (const uint16_t*)dy;
+  LayerAhead ahead;
+  QL_TRY(ahead.init(throttle && nb == 2));
   for (int l = L - 1; l >= 0; --l) {
+    QL_TRY(ahead.before(L - 1 - l));
     const int slot = l % nb;
     const uint8_t* base;
     if (!streamed) {
@@ -1480,6 +1520,7 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
         have_ready[slot] = true;
       }
     }
+    QL_TRY(ahead.after(L - 1 - l, C));
   }
   if (throttle) QL_TRY(inflight_mark(1, C));
   return sc.pageable ? QL_WARN_PAGEABLE_HOST : QL_OK;
