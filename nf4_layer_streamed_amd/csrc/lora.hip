@@ -667,7 +667,9 @@ ql_status launch_rowc(RowArgs a, void* ws, size_t ws_bytes, hipStream_t st) {
     P.nsplit = 1;
     P.part = nullptr;
     if (P.M <= 0) continue;
-    P.nsplit = rowc_split(P.M, P.K);
+    // the RMSNorm producer runs unsplit: its workgroups read whole rows for
+    // the statistics, which a split would repeat per slice
+    P.nsplit = a.mode == 3 ? 1 : rowc_split(P.M, P.K);
     tiles += (int)((P.M + RC_ROWS - 1) / RC_ROWS) * P.nsplit;
     if (P.nsplit > 1) {
       P.part = (float*)((uint8_t*)ws + off);
