@@ -49,6 +49,26 @@ def test_policy_outputs_unchanged(st):
     assert torch.equal(a["saved"], b["saved"])
 
 
+@pytest.mark.parametrize("M", [5, 200])
+def test_fused_rmsnorm_equals_standalone_bitwise(M):
+    # The policy forward makes n1 = RMSNorm(h) inside its LoRA row launch; the
+    # adapter-off reference forward has no row launch and runs the standalone
+    # RMSNorm kernel. On layer 0 both normalise the same input x, so their n1
+    # agree bitwise (the fused kernel sums in the standalone kernel's order),
+    # also for a row count that leaves the last 16-row tile partial.
+    require_gpu()
+    s = GpuStack("smollm2_stack", L=1, M=M)
+    _, per = ql.stream_layer_stack_saved_layout(s.cfg, s.M)
+    s.ref_scratch = torch.empty(per, dtype=torch.uint8, device=DEV)
+    s.ref_y = torch.empty_like(s.y)
+    assert run_ref(s) == ql.QL_OK
+    torch.cuda.synchronize()
+    pol = s.saved_tensor(0, "n1")
+    ref = s.saved_tensor(0, "n1", buf=s.ref_scratch)
+    assert torch.equal(pol.view(torch.int16), ref.view(torch.int16))
+    assert torch.count_nonzero(pol.float()) > 0
+
+
 def test_reference_matches_oracle_with_adapters_off(st):
     assert run_ref(st) == ql.QL_OK
     torch.cuda.synchronize()
