@@ -221,10 +221,13 @@ ql_status qlora_linear_bwd_noalloc(const void* dy, const void* x, const void* u_
  *
  * The frozen NF4 weights live in one "store" of n_layers records (layout from
  * stream_layer_stack_layout). Streamed mode (resident == 0): the store is HOST
- * memory, ideally page-locked; each layer's record is copied with one
- * asynchronous host-to-device copy on the `copy` stream into one of n_buffers
- * device slots, while the `compute` stream works on another; events order the
- * two (docs "Layer Streaming": pre-allocated device buffers, two by default).
+ * memory, ideally page-locked; each layer's record is copied asynchronously
+ * host-to-device on the `copy` stream into one of n_buffers device slots,
+ * while the `compute` stream works on another; events order the two (docs
+ * "Layer Streaming": pre-allocated device buffers, two by default). A record
+ * goes as one copy, except each pass's last one (records of 8 MiB or more),
+ * which goes weight group by weight group so that its layer starts each GEMM
+ * as soon as that GEMM's group has landed.
  * Peak device memory for weights is the n_buffers slots.
  * Resident mode (resident == 1): the store is a DEVICE buffer, nothing is
  * copied and the same kernels run in the same order on the same bytes, so the
@@ -283,8 +286,9 @@ enum { QL_PROJ_Q = 0, QL_PROJ_K, QL_PROJ_V, QL_PROJ_O, QL_PROJ_GATE, QL_PROJ_UP,
 ql_status stream_layer_stack_layout(const ql_stack_cfg* cfg, int64_t* layer_offsets,
                                     int64_t* proj_offsets, size_t* store_bytes);
 
-/* Buffer sizes for M tokens: slots (2 device layer buffers), saved activations
- * (written by the forward, read by the backward), and workspace. */
+/* Buffer sizes for M tokens: slots (n_buffers device layer records; none in
+ * resident mode), saved activations (written by the forward, read by the
+ * backward), and workspace. */
 ql_status stream_layer_stack_workspace(const ql_stack_cfg* cfg, int64_t M, size_t* slots_bytes,
                                        size_t* saved_bytes, size_t* ws_bytes);
 
