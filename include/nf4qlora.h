@@ -227,7 +227,11 @@ ql_status qlora_linear_bwd_noalloc(const void* dy, const void* x, const void* u_
  * "Layer Streaming": pre-allocated device buffers, two by default). A record
  * goes as one copy, except each pass's last one (records of 8 MiB or more),
  * which goes weight group by weight group so that its layer starts each GEMM
- * as soon as that GEMM's group has landed.
+ * as soon as that GEMM's group has landed. With two slots, part of each
+ * pass's first refill (the groups its slot's layer has finished with) runs
+ * on a side copy stream that the library creates on first use, one per
+ * device with default priority, and keeps for the process; calls recorded
+ * into a graph do not use it.
  * Peak device memory for weights is the n_buffers slots.
  * Resident mode (resident == 1): the store is a DEVICE buffer, nothing is
  * copied and the same kernels run in the same order on the same bytes, so the

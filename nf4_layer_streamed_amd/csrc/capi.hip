@@ -293,18 +293,28 @@ static ql_status layer_weights_ready(const ql_stack_cfg* c, const StackLayout& L
   return by_group ? QL_OK : launch_dq_expand(dq_expand_args(L, WS, base, ws, -1), st);
 }
 
-// A layer whose record lands one weight group at a time: before the GEMM
-// that reads group g (the only kernels that read the slot) the compute stream
-// waits for ready[g], then expands the group's double-quantised scales
-// (dq[g].nblk > 0). Null: the caller waited for the whole record.
+// Hand-offs with the copy streams inside a layer (only the GEMMs read the
+// slot). With wait, the record lands one weight group at a time: before the
+// GEMM that reads group g the compute stream waits for ready[g], then
+// expands the group's double-quantised scales (dq[g].nblk > 0). With early,
+// the event is recorded after the GEMM of group early_after, the layer's last
+// reader of that group, so that a refill can start on it before the layer
+// ends. Null: the caller handles the whole record.
 struct GroupReady {
+  bool wait = false;
   hipEvent_t ready[kGroups] = {};
   DqExpandArgs dq[kGroups] = {};
+  hipEvent_t early = nullptr;
+  int early_after = -1;
 };
 static ql_status group_wait(const GroupReady* gr, int g, hipStream_t C) {
-  if (!gr) return QL_OK;
+  if (!gr || !gr->wait) return QL_OK;
   QL_HIP_CHECK(hipStreamWaitEvent(C, gr->ready[g], 0));
   if (gr->dq[g].nblk > 0) QL_TRY(launch_dq_expand(gr->dq[g], C));
+  return QL_OK;
+}
+static ql_status group_done(const GroupReady* gr, int g, hipStream_t C) {
+  if (gr && gr->early && gr->early_after == g) QL_HIP_CHECK(hipEventRecord(gr->early, C));
   return QL_OK;
 }
 
@@ -357,6 +367,7 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     }
     QL_TRY(group_wait(gr, 0, st));
     QL_TRY(launch_gemm_fwd(a, st));
+    QL_TRY(group_done(gr, 0, st));
   }
   const int n_rep = (int)(H / KV);
   {  // o: input a = repeat_kv(v) read through the column remap; residual h_in
@@ -379,6 +390,7 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     g.out = S(QL_SAVED_H_MID); g.N = H; g.ldo = H; g.resid = h_in;
     QL_TRY(group_wait(gr, 1, st));
     QL_TRY(launch_gemm_fwd(a, st));
+    QL_TRY(group_done(gr, 1, st));
   }
   QL_TRY(norm_down(S(QL_SAVED_H_MID), QL_SAVED_N2, QL_PROJ_GATE, 2));  // gate, up share n2
   {  // gate | up
@@ -394,6 +406,7 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     }
     QL_TRY(group_wait(gr, 2, st));
     QL_TRY(launch_gemm_fwd(a, st));
+    QL_TRY(group_done(gr, 2, st));
   }
   {  // down, residual h_mid
     if (on) {  // act = SwiGLU(gate, up) and U of down in one pass
@@ -418,6 +431,7 @@ static ql_status layer_fwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     a.partial_bytes = WS.partial_bytes;
     QL_TRY(group_wait(gr, 3, st));
     QL_TRY(launch_gemm_fwd(a, st));
+    QL_TRY(group_done(gr, 3, st));
   }
   return QL_OK;
 }
@@ -501,6 +515,7 @@ static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     a.partial = (float*)(ws + WS.partial); a.partial_bytes = WS.partial_bytes;
     QL_TRY(group_wait(gr, 3, st));
     QL_TRY(launch_gemm_bwd(a, st));
+    QL_TRY(group_done(gr, 3, st));
   }
   add(db_prob(dh, M, H, S(QL_SAVED_U0 + QL_PROJ_DOWN), r, s, dB[QL_PROJ_DOWN], accumulate));
   add(da_prob(S(QL_SAVED_ACT), M, I, I, 0, 0, Gd, r, s, dA[QL_PROJ_DOWN], accumulate));
@@ -533,6 +548,7 @@ static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     a.partial = (float*)(ws + WS.partial); a.partial_bytes = WS.partial_bytes;
     QL_TRY(group_wait(gr, 2, st));
     QL_TRY(launch_gemm_bwd(a, st));
+    QL_TRY(group_done(gr, 2, st));
   }
   add(db_prob(T(WS.dg), M, I, S(QL_SAVED_U0 + QL_PROJ_GATE), r, s, dB[QL_PROJ_GATE], accumulate));
   add(db_prob(T(WS.du), M, I, S(QL_SAVED_U0 + QL_PROJ_UP), r, s, dB[QL_PROJ_UP], accumulate));
@@ -554,6 +570,7 @@ static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     a.partial = (float*)(ws + WS.partial); a.partial_bytes = WS.partial_bytes;
     QL_TRY(group_wait(gr, 1, st));
     QL_TRY(launch_gemm_bwd(a, st));
+    QL_TRY(group_done(gr, 1, st));
   }
   add(db_prob(dhm, M, H, S(QL_SAVED_U0 + QL_PROJ_O), r, s, dB[QL_PROJ_O], accumulate));
   add(da_prob(S(QL_SAVED_V), M, H, KV, c->head_dim, n_rep, Go, r, s, dA[QL_PROJ_O], accumulate));
@@ -568,6 +585,7 @@ static ql_status layer_bwd(const ql_stack_cfg* c, const StackLayout& SL, const L
     a.partial = (float*)(ws + WS.partial); a.partial_bytes = WS.partial_bytes;
     QL_TRY(group_wait(gr, 0, st));  // of q|k|v only v is read here
     QL_TRY(launch_gemm_bwd(a, st));
+    QL_TRY(group_done(gr, 0, st));
   }
   add(db_prob(T(WS.dv), M, KV, S(QL_SAVED_U0 + QL_PROJ_V), r, s, dB[QL_PROJ_V], accumulate));
   add(da_prob(S(QL_SAVED_N1), M, H, H, 0, 0, Gv, r, s, dA[QL_PROJ_V], accumulate));
@@ -675,9 +693,30 @@ static ql_status copy_groups(const StackLayout& SL, uint8_t* dst, const uint8_t*
 }
 constexpr int kFwdOrder[kGroups] = {0, 1, 2, 3}, kBwdOrder[kGroups] = {3, 2, 1, 0};
 
+// The library's side copy stream on the current device (default priority,
+// created on first use, kept for the process). It carries the part of a
+// pass's first refill that starts before the slot's layer has finished, so
+// that the copy stream itself never waits between copies on an event
+// recorded in the middle of a layer: with such waits on the copy stream the
+// 8B-shaped step took 139-150 ms instead of 133; with the side stream it
+// takes 132.2 against 133.2 ms (Qwen2.5-3B-shaped: 53.75 against 54.0 ms).
+// Only two-slot rings take it: with 3 or 8 slots it measured 2-2.5 ms slower.
+static ql_status side_stream(hipStream_t* out) {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  QL_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return set_error(QL_ERR_UNSUPPORTED, "device ordinal %d", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!streams[dev]) QL_HIP_CHECK(hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking));
+  *out = streams[dev];
+  return QL_OK;
+}
+
 struct Events {
   hipEvent_t ready[QL_MAX_BUFFERS] = {}, free_[QL_MAX_BUFFERS] = {}, entry = nullptr;
   hipEvent_t gready[QL_MAX_BUFFERS][kGroups] = {};  // per weight group
+  hipEvent_t early = nullptr, side = nullptr;        // a pass's early refill part
   int n = 0;
   ~Events() {
     for (int i = 0; i < n; ++i) {
@@ -687,6 +726,8 @@ struct Events {
         if (gready[i][g]) (void)hipEventDestroy(gready[i][g]);
     }
     if (entry) (void)hipEventDestroy(entry);
+    if (early) (void)hipEventDestroy(early);
+    if (side) (void)hipEventDestroy(side);
   }
   // `ready` (copy -> compute) keeps the default system-scope fence: the
   // compute stream must observe bytes the copy engine wrote. `free_` and
@@ -702,6 +743,10 @@ struct Events {
         QL_HIP_CHECK(hipEventCreateWithFlags(&gready[i][g], hipEventDisableTiming));
     }
     QL_HIP_CHECK(hipEventCreateWithFlags(&entry, hipEventDisableTiming | hipEventDisableSystemFence));
+    if (groups) {
+      QL_HIP_CHECK(hipEventCreateWithFlags(&early, hipEventDisableTiming | hipEventDisableSystemFence));
+      QL_HIP_CHECK(hipEventCreateWithFlags(&side, hipEventDisableTiming));
+    }
     return QL_OK;
   }
   // The slots may still be read by work enqueued earlier on the compute
@@ -1314,11 +1359,20 @@ static ql_status stack_fwd(const ql_stack_cfg* cfg, const StackCall& sc, const v
     const bool by_group = grouped && l == L - 1;
     LayerW W;
     QL_TRY(layer_weights_ready(cfg, sc.SL, sc.WS, base, w8, C, W, by_group));
+    // with two slots the first refill (layer 2 into layer 0's slot) starts
+    // on q|k|v and o, on the side stream, once layer 0's o GEMM is done (not
+    // in a capture, not when the slot also serves the reference forward)
+    const bool early = grouped && nb == 2 && l == 0 && !ref_y && !capturing(C) && l + nb < L - 1;
     GroupReady gr;
+    gr.wait = by_group;
     std::copy(ev.gready[slot], ev.gready[slot] + kGroups, gr.ready);
     for (int g = 0; g < kGroups && by_group && cfg->absmax_dq; ++g)
       gr.dq[g] = dq_expand_args(sc.SL, sc.WS, base, w8, g);
-    const GroupReady* grp = by_group ? &gr : nullptr;
+    if (early) {
+      gr.early = ev.early;
+      gr.early_after = 1;
+    }
+    const GroupReady* grp = (by_group || early) ? &gr : nullptr;
     if (lora) {
       uint8_t* svl = sv + (size_t)l * sc.SV.per_layer;
       uint16_t* h_out = (l + 1 < L) ? (uint16_t*)(sv + (size_t)(l + 1) * sc.SV.per_layer + sc.SV.off[QL_SAVED_H_IN])
@@ -1341,13 +1395,23 @@ static ql_status stack_fwd(const ql_stack_cfg* cfg, const StackCall& sc, const v
     if (!cfg->resident && l + nb < L) {
       uint8_t* dst = sl8 + slot * rec;
       const uint8_t* src = st8 + (size_t)(l + nb) * rec;
+      size_t head = 0;  // bytes the side stream copies
+      if (early) {
+        hipStream_t P2;
+        QL_TRY(side_stream(&P2));
+        head = (size_t)sc.SL.grp_off[2];
+        QL_HIP_CHECK(hipStreamWaitEvent(P2, ev.early, 0));
+        QL_TRY(copy_record(dst, src, head, P2, !sc.pageable));
+        QL_HIP_CHECK(hipEventRecord(ev.side, P2));
+      }
       QL_HIP_CHECK(hipEventRecord(ev.free_[slot], C));
       QL_HIP_CHECK(hipStreamWaitEvent(P, ev.free_[slot], 0));
       if (grouped && l + nb == L - 1) {
         QL_TRY(copy_groups(sc.SL, dst, src, P, !sc.pageable, kFwdOrder, ev.gready[slot]));
         have_ready[slot] = false;
       } else {
-        QL_TRY(copy_record(dst, src, rec, P, !sc.pageable));
+        QL_TRY(copy_record(dst + head, src + head, rec - head, P, !sc.pageable));
+        if (early) QL_HIP_CHECK(hipStreamWaitEvent(P, ev.side, 0));
         QL_HIP_CHECK(hipEventRecord(ev.ready[slot], P));
         have_ready[slot] = true;
       }
@@ -1486,11 +1550,22 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
     const bool by_group = grouped && l == 0;
     LayerW W;
     QL_TRY(layer_weights_ready(cfg, sc.SL, sc.WS, base, w8, C, W, by_group));
+    // with two slots the first refill (layer L - 3 into layer L - 1's slot)
+    // starts on down, on the side stream, once the layer's down dX GEMM is
+    // done (a recomputed forward reads down before that GEMM)
+    const bool early = grouped && nb == 2 && l == L - 1 && !capturing(C) && l - nb > 0;
     GroupReady gr;
+    gr.wait = by_group;
     std::copy(ev.gready[slot], ev.gready[slot] + kGroups, gr.ready);
     for (int g = 0; g < kGroups && by_group && cfg->absmax_dq; ++g)
       gr.dq[g] = dq_expand_args(sc.SL, sc.WS, base, w8, g);
+    GroupReady gb = gr;  // the backward's own: only it records the early event
+    if (early) {
+      gb.early = ev.early;
+      gb.early_after = 3;
+    }
     const GroupReady* grp = by_group ? &gr : nullptr;
+    const GroupReady* gbp = (by_group || early) ? &gb : nullptr;
     const uint8_t* svl = sv + (size_t)l * sc.SV.per_layer;
     if (cfg->recompute) {
       // recompute the layer's activations from its saved input, with the
@@ -1504,18 +1579,28 @@ ql_status stream_layer_stack_bwd(const ql_stack_cfg* cfg, const void* store, siz
       svl = ck;
     }
     QL_TRY(layer_bwd(cfg, sc.SL, W, lora + l * QL_NPROJ, M, sc.SVF, svl, dh, out, dA + l * QL_NPROJ,
-                     dB + l * QL_NPROJ, accumulate, w8, sc.WS, C, grp));
+                     dB + l * QL_NPROJ, accumulate, w8, sc.WS, C, gbp));
     dh = out;
     if (streamed && l - nb >= 0) {
       uint8_t* dst = sl8 + slot * rec;
       const uint8_t* src = st8 + (size_t)(l - nb) * rec;
+      size_t body = rec;  // bytes the copy stream copies (the rest: the side stream)
+      if (early) {
+        hipStream_t P2;
+        QL_TRY(side_stream(&P2));
+        body = (size_t)sc.SL.grp_off[3];
+        QL_HIP_CHECK(hipStreamWaitEvent(P2, ev.early, 0));
+        QL_TRY(copy_record(dst + body, src + body, rec - body, P2, !sc.pageable));
+        QL_HIP_CHECK(hipEventRecord(ev.side, P2));
+      }
       QL_HIP_CHECK(hipEventRecord(ev.free_[slot], C));
       QL_HIP_CHECK(hipStreamWaitEvent(P, ev.free_[slot], 0));
       if (grouped && l - nb == 0) {
         QL_TRY(copy_groups(sc.SL, dst, src, P, !sc.pageable, kBwdOrder, ev.gready[slot]));
         have_ready[slot] = false;
       } else {
-        QL_TRY(copy_record(dst, src, rec, P, !sc.pageable));
+        QL_TRY(copy_record(dst, src, body, P, !sc.pageable));
+        if (early) QL_HIP_CHECK(hipStreamWaitEvent(P, ev.side, 0));
         QL_HIP_CHECK(hipEventRecord(ev.ready[slot], P));
         have_ready[slot] = true;
       }
