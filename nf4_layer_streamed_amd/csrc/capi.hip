@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -623,7 +624,7 @@ static PtrKind pointer_kind(const void* p) {
 // slot's previous readers are done. A kernel that read a slot before its
 // `ready` event would then meet NaN scales and codes 15 instead of a stale
 // but plausible layer, and the outputs would show it.
-static bool g_poison = false;
+static std::atomic<bool> g_poison{false};
 
 // Host-to-device copy of a small page-locked record by the library's own
 // kernel. The runtime's copy of a pinned buffer is itself a kernel whose grid
@@ -657,7 +658,7 @@ __global__ __launch_bounds__(256) void k_h2d(const u32x4v* __restrict__ src, u32
 // One layer record host -> device on the copy stream (a pageable store always
 // goes through the runtime's copy, which stages it).
 static ql_status copy_record(void* dst, const void* src, size_t bytes, hipStream_t P, bool pinned) {
-  if (g_poison) QL_HIP_CHECK(hipMemsetAsync(dst, 0xFF, bytes, P));
+  if (g_poison.load()) QL_HIP_CHECK(hipMemsetAsync(dst, 0xFF, bytes, P));
   if (pinned && bytes < kSmallCopy) {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     QL_HIP_CHECK(hipStreamIsCapturing(P, &cap));
@@ -1092,7 +1093,7 @@ int32_t ql_abi_version(void) { return 101; }
 ql_status ql_debug_poison_slots(int32_t on) {
   clear_error();
   if (on != 0 && on != 1) return set_error(QL_ERR_ARG, "ql_debug_poison_slots: on must be 0 or 1");
-  g_poison = on != 0;
+  g_poison.store(on != 0);
   return QL_OK;
 }
 
@@ -1637,7 +1638,7 @@ ql_status stream_layer_stack_step_capture(const ql_stack_cfg* cfg, const void* s
   if (turnaround != 0 && turnaround != 1) return set_error(QL_ERR_ARG, "%s: turnaround must be 0 or 1", fn);
   if (profiling_on()) return set_error(QL_ERR_UNSUPPORTED, "%s: kernel timing is on (ql_profile_enable)", fn);
   if (!compute) return set_error(QL_ERR_ARG, "%s: capture needs an explicit compute stream", fn);
-  if (g_poison) return set_error(QL_ERR_UNSUPPORTED, "%s: slot poisoning is on (ql_debug_poison_slots)", fn);
+  if (g_poison.load()) return set_error(QL_ERR_UNSUPPORTED, "%s: slot poisoning is on (ql_debug_poison_slots)", fn);
   if (M == 0) return set_error(QL_ERR_SHAPE, "%s: M must be >= 1", fn);
   hipStream_t C = (hipStream_t)compute;
   QL_HIP_CHECK(hipStreamBeginCapture(C, hipStreamCaptureModeRelaxed));

@@ -43,6 +43,7 @@
 // made to land on one XCD and share its L2.
 #include <hip/hip_ext.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "ql_internal.h"
@@ -1128,30 +1129,35 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
 template <int BN>
 constexpr int fwd_lds() { return FWD_STAGES * fwd_stage_bytes<BN>(); }
 
-bool g_attr_set[64] = {};
+// Per-device caches, filled on a device's first launch. Several host threads
+// may launch at once: the flags and counts are atomics, and setting the
+// attribute twice is harmless.
+constexpr int kMaxDevices = 64;
+std::atomic<bool> g_attr_set[kMaxDevices] = {};
+std::atomic<int> g_cus[kMaxDevices] = {};
 
 ql_status ensure_attrs() {
   int dev = 0;
   QL_HIP_CHECK(hipGetDevice(&dev));
-  if (dev >= 0 && dev < 64 && !g_attr_set[dev]) {
+  if (dev < 0 || dev >= kMaxDevices) return set_error(QL_ERR_UNSUPPORTED, "device ordinal %d", dev);
+  if (!g_attr_set[dev].load(std::memory_order_acquire)) {
     QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_fwd<64>, hipFuncAttributeMaxDynamicSharedMemorySize, fwd_lds<256>()));
     QL_HIP_CHECK(hipFuncSetAttribute((const void*)k_gemm_fwd<32>, hipFuncAttributeMaxDynamicSharedMemorySize, fwd_lds<128>()));
-    g_attr_set[dev] = true;
+    g_attr_set[dev].store(true, std::memory_order_release);
   }
   return QL_OK;
 }
 
+// Compute units of the current device (the launch geometry's round size).
+// ensure_attrs has checked the device ordinal.
 int cu_count() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
-  return cus;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int c = g_cus[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  c = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  g_cus[dev].store(c, std::memory_order_relaxed);
+  return c;
 }
 
 }  // namespace
