@@ -38,7 +38,7 @@ QL_KERNEL_GEMM_FWD, QL_KERNEL_GEMM_BWD, QL_KERNEL_GEMM_FWD_NARROW, QL_KERNEL_GEM
 QL_KERNEL_LORA_ROW, QL_KERNEL_LORA_COL, QL_KERNEL_DEQUANT = 4, 5, 6
 # kernel symbol of each profiling id (the names rocprofv3 reports): the fused
 # GEMMs (work in FLOPs) and the HBM-bound kernels (work in bytes)
-KERNEL_SYMBOLS = {0: "k_gemm_fwd<64>", 1: "k_gemm_bwd<128>", 2: "k_gemm_fwd<32>", 3: "k_gemm_bwd<64>"}
+KERNEL_SYMBOLS = {0: "k_gemm_fwd<64>", 1: "k_gemm_bwd<128, 8>", 2: "k_gemm_fwd<32>", 3: "k_gemm_bwd<64, 4>"}
 HBM_KERNEL_SYMBOLS = {4: "k_rowc", 5: "k_colc", 6: "k_nf4_dequant"}
 
 

@@ -31,7 +31,8 @@
 // its own W rows straight into MFMA B registers, so W never touches LDS and
 // each weight is decoded once per workgroup.
 //
-// dX layout: 256 x BN outputs per workgroup of 4 waves (2 x 2). The reduction
+// dX layout: 256 x BN outputs per workgroup, 8 waves (2 x 4, two per SIMD) on
+// 256 x 256 tiles and 4 waves (2 x 2) on 256 x 128 tiles. The reduction
 // runs over N, while the codes are K-contiguous, so each thread decodes one
 // row-block (64 weights) into an LDS tile [n][k], and the MFMA B operand is
 // read from it transposed with ds_read_b64_tr_b16 (gfx950): within a group of
@@ -748,9 +749,15 @@ __device__ __forceinline__ int raw_slot(int n, int c) {
   return n * CPR + (c ^ ((n >> SH) & (CPR - 1)));
 }
 
-// WNB: output columns per wave (128 or 64); workgroup tile 256 x (2 WNB) at
-// columns k_base + (tile / tiles_m) BN; waves 2 x 2. Reduction order: for
-// each segment its 64-row weight steps, then the LoRA steps of all segments.
+// Workgroup tile 256 x BN (BN = 2 WNB) at columns k_base + (tile / tiles_m) BN.
+// NWV = 4: waves 2 x 2, each 128 rows x WNB columns, one wave per SIMD with
+// 256 accumulator registers. NWV = 8: waves 2 x 4, each 128 rows x BN / 4
+// columns with 128 accumulators, two waves per SIMD, so that one wave's VALU
+// and LDS work issues while the other's MFMAs run. The workgroup decodes each
+// weight step once either way; with 8 waves each thread decodes half a block
+// row (32 weights) and every dY fragment feeds half as many MFMAs. Reduction
+// order: for each segment its 64-row weight steps, then the LoRA steps of all
+// segments.
 //
 // LDS: two dY stages and two raw-code stages (the DMA targets) and two decoded
 // weight tiles, in separate arrays. The transposing reads of the weight tiles
@@ -773,10 +780,14 @@ __device__ __forceinline__ int raw_slot(int n, int c) {
 // rows r and r + 8 on the same ones.
 constexpr bool BXS = true;
 
-template <int WNB>
-__global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m, int tiles_total, int k_base) {
+template <int WNB, int NWV>
+__global__ __launch_bounds__(64 * NWV, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m, int tiles_total, int k_base) {
   constexpr int BN = 2 * WNB;
-  constexpr int NTW = WNB / 32;
+  // NWV = 4: waves 2 x 2 of 128 x WNB; NWV = 8: waves 2 x 4 of 128 x BN / 4 (two per SIMD)
+  constexpr int WAVES_K = NWV / 2;
+  constexpr int WC = BN / WAVES_K;
+  constexpr int NTH = 64 * NWV;
+  constexpr int NTW = WC / 32;
   constexpr int CPR = BN / 32;
   constexpr int SH = CPR == 8 ? 1 : 2;
   constexpr int RAW = bwd_raw_bytes<BN>();
@@ -793,7 +804,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
   auto stage_r = [&](auto si) -> uint8_t* { return decltype(si)::value ? lds_r1 : lds_r0; };
   auto stage_b = [&](auto si) -> uint8_t* { return decltype(si)::value ? lds_b1 : lds_b0; };
   const int t = threadIdx.x, lane = t & 63, g = lane >> 5, li = lane & 31;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w >> 1, wn = w & 1;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w / WAVES_K, wn = w % WAVES_K;
 
   // grid = tiles x nsplit; split sp of a tile takes weight steps [WS sp / S, WS (sp + 1) / S)
   const int gt = (int)xcd_remap(blockIdx.x, (uint32_t)(tiles_total * a.nsplit));
@@ -842,7 +853,10 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
 
   // dY tile (256 rows x 64 columns of segment sgA from nbA) into an A stage;
   // columns past the segment's N read as zeros (offset past the buffer).
-  const int arow = 8 * w + (lane >> 3), alc0 = dma_chunk<BXS>(lane, w, 0), alc1 = dma_chunk<BXS>(lane, w, 1);
+  // 1-KB block b = NWV i + w holds rows 8 b .. 8 b + 7 (with 8 waves b mod 8 = w for every i)
+  constexpr int DPI = 32 / NWV;  // dY DMAs per wave
+  const int arow = 8 * w + (lane >> 3), alc0 = dma_chunk<BXS>(lane, w, 0),
+            alc1 = dma_chunk<BXS>(lane, w, NWV == 4 ? 1 : 0);
   auto dma_a = [&](uint8_t* As) {
     const int64_t N = sel3(sgA, N0, N1, N2);
     const __amdgpu_buffer_rsrc_t yr = sel3(sgA, yr0, yr1, yr2);
@@ -852,10 +866,10 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
     const int past0 = -(int)(nbA + 8 * alc0 >= N), past1 = -(int)(nbA + 8 * alc1 >= N);
     const int so = __builtin_amdgcn_readfirstlane(nbA * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < DPI; ++i) {
       const int alc = (i & 1) ? alc1 : alc0, past = (i & 1) ? past1 : past0;
-      const int vo = (((arow + 32 * i) * ldy * 2 + alc * 16) & ~past) | (ylim & past);
-      dma16(yr, As + (4 * i + w) * 1024, vo, so);
+      const int vo = (((arow + 8 * NWV * i) * ldy * 2 + alc * 16) & ~past) | (ylim & past);
+      dma16(yr, As + (NWV * i + w) * 1024, vo, so);
     }
     advance(sgA, nbA);
   };
@@ -871,21 +885,21 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
     const __amdgpu_buffer_rsrc_t sr = rsrc(sel3(sgR, am0, am1, am2) + (int64_t)nbR * kbn, (rows_left * kbn - k0 / 64) * 4);
     const int kh = (int)(K / 2);
 #pragma unroll
-    for (int cc = 0; cc < CPR / 4; ++cc) {
-      const int ci = w + 4 * cc;
+    for (int cc = 0; cc < CPR / NWV; ++cc) {
+      const int ci = w + NWV * cc;
       const int slot = ci * 64 + lane;
       const int n = slot / CPR, pc = slot % CPR;
       const int c = pc ^ ((n >> SH) & (CPR - 1));
       dma16(cr, R + ci * 1024, n * kh + c * 16, 0);
     }
-    dma4(sr, R + ABS + 256 * w, ((16 * w + (lane >> 2)) * (int)kbn + (lane & 3)) * 4, 0);
+    if (NWV == 4 || w < 4) dma4(sr, R + ABS + 256 * w, ((16 * w + (lane >> 2)) * (int)kbn + (lane & 3)) * 4, 0);
     advance(sgR, nbR);
   };
 
   // decode share of a thread: row dn, 64-column block dc (wide) or half dh of it (narrow)
-  constexpr int NCH = BN == 256 ? 2 : 1;  // 16-byte code chunks per thread
-  constexpr int NW = 4 * NCH;             // code words (8 weights each) per thread per step
-  const int dn = t & 63, dc = (t >> 6) & (BN / 64 - 1), dh = BN == 256 ? 0 : (t >> 7);
+  constexpr int NCH = 2 * BN / NTH;  // 16-byte code chunks per thread
+  constexpr int NW = 4 * NCH;        // code words (8 weights each) per thread per step
+  const int dn = t & 63, dc = (t >> 6) & (BN / 64 - 1), dh = NCH == 2 ? 0 : (t >> 6) / (BN / 64);
   uint32_t dcode[NW];
   float dscale;
   Lut dlut;
@@ -927,7 +941,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
       // lanes 32 g + c (c < 32) need column c and reduction rows 16 q + 8 g .. + 8
-      const int col = wn * WNB + 32 * j + 16 * (h16 & 1) + 4 * cbq;
+      const int col = wn * WC + 32 * j + 16 * (h16 & 1) + 4 * cbq;
       const int row = 16 * q + 8 * (h16 >> 1) + ra;
       const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4_t*)(Bs + bt_off<BN>(row, col)));
@@ -971,7 +985,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
       constexpr int e0 = (q * NW + 2) / 3, e1 = q < 3 ? ((q + 1) * NW + 2) / 3 : e0;
       constexpr int nwr = e1 - e0;
       constexpr int nr = 4 + 2 * NTW + (q == 3 ? NCH + 1 : 0);
-      constexpr int nd = q == 0 ? CPR / 4 + 1 : (q == 3 ? 8 : 0);
+      constexpr int nd = q == 0 ? CPR / NWV + 1 : (q == 3 ? DPI : 0);
       if (q == 0) {
         dma_raw(stage_r(Cur{}));  // step s + 2's codes (this stage's went to registers at step s - 2)
         dec_lut();                // the table of step s + 1's codes
@@ -1045,9 +1059,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
     const BwdSeg& S = a.seg[sg];
     uint8_t* As = (sg & 1) ? lds_a1 : lds_a0;
     uint8_t* Bs = (sg & 1) ? lds_b1 : lds_b0;
-    uint4 ar[8];
-    load_a_rank(ar, S.G, a.r, M, m0, t);
-    store_a<BXS>(As, ar, t);
+    if (NWV == 4 || t < NT) {
+      uint4 ar[8];
+      load_a_rank(ar, S.G, a.r, M, m0, t);
+      store_a<BXS>(As, ar, t);
+    }
     if (dthread) {  // buffer loads of A's rows, zero past r and past K, no branches
       const bool live = drow < a.r && dk < K;
       const __amdgpu_buffer_rsrc_t ar_ = rsrc(S.A, (int64_t)a.r * K * 2);
@@ -1076,11 +1092,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
   // whole row segments of WNB * 4 (float32) or WNB * 2 (bf16) bytes. K % 64
   // == 0, so a 4-column group is wholly inside or outside.
   __syncthreads();  // every wave done with the LoRA steps' stages
-  constexpr int CPRW = WNB / 4;  // 16-byte chunks per staged row
+  constexpr int CPRW = WC / 4;  // 16-byte chunks per staged row
   constexpr int RPI = 64 / CPRW;  // rows per read instruction
-  uint8_t* E = (wm ? lds_a1 : lds_a0) + wn * (32 * WNB * 4);
+  uint8_t* E = (wm ? lds_a1 : lds_a0) + wn * (32 * WC * 4);
   const int rc = lane % CPRW, rr = lane / CPRW;
-  const int64_t k = k0 + wn * WNB + 4 * rc;
+  const int64_t k = k0 + wn * WC + 4 * rc;
   // buffer-descriptor stores per 32-row block, as in the forward
   const int64_t mw = m0 + wm * 128;
   const int mode = a.nsplit > 1 ? 0 : (a.out_f32 ? 2 : 1);  // partial, float32, bf16 (uniform)
@@ -1100,13 +1116,13 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_bwd(const BwdArgs a, int tiles_m
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int c = 8 * j + 2 * v + g;
-          *(f32x4_t*)(E + li * (WNB * 4) + ((c ^ (li & (CPRW - 1))) << 4)) =
+          *(f32x4_t*)(E + li * (WC * 4) + ((c ^ (li & (CPRW - 1))) << 4)) =
               f32x4_t{acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]};
         }
 #pragma unroll
       for (int it = 0; it < 32 / RPI; ++it) {
         const int row = it * RPI + rr;
-        fv[it] = *(const f32x4_t*)(E + row * (WNB * 4) + ((rc ^ (row & (CPRW - 1))) << 4));
+        fv[it] = *(const f32x4_t*)(E + row * (WC * 4) + ((rc ^ (row & (CPRW - 1))) << 4));
       }
       const int64_t rows = M - mw - 32 * i < 32 ? M - mw - 32 * i : 32;
       const int64_t span = rows > 0 ? rows * K : 0;  // elements
@@ -1419,10 +1435,10 @@ ql_status launch_bwd_tiles(const BwdArgs& a, bool wide, int64_t k_base, int64_t 
   if (prof) QL_TRY_PROF(profile_begin(&e0, &e1));
   const int grid = total * a.nsplit;
   if (wide)
-    hipExtLaunchKernelGGL(k_gemm_bwd<128>, dim3(grid), dim3(NT), 0, st, e0, e1, 0, a, tiles_m, total,
+    hipExtLaunchKernelGGL((k_gemm_bwd<128, 8>), dim3(grid), dim3(512), 0, st, e0, e1, 0, a, tiles_m, total,
                           (int)k_base);
   else
-    hipExtLaunchKernelGGL(k_gemm_bwd<64>, dim3(grid), dim3(NT), 0, st, e0, e1, 0, a, tiles_m, total,
+    hipExtLaunchKernelGGL((k_gemm_bwd<64, 4>), dim3(grid), dim3(NT), 0, st, e0, e1, 0, a, tiles_m, total,
                           (int)k_base);
   QL_HIP_CHECK(hipGetLastError());
   if (prof) {
