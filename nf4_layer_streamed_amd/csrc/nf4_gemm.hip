@@ -750,8 +750,8 @@ __device__ __forceinline__ int raw_slot(int n, int c) {
 }
 
 // Workgroup tile 256 x BN (BN = 2 WNB) at columns k_base + (tile / tiles_m) BN.
-// NWV = 4: waves 2 x 2, each 128 rows x WNB columns, one wave per SIMD with
-// 256 accumulator registers. NWV = 8: waves 2 x 4, each 128 rows x BN / 4
+// NWV = 4: waves 2 x 2, each 128 rows x WNB columns (2 WNB accumulator
+// registers per lane), one wave per SIMD. NWV = 8: waves 2 x 4, each 128 rows x BN / 4
 // columns with 128 accumulators, two waves per SIMD, so that one wave's VALU
 // and LDS work issues while the other's MFMAs run. The workgroup decodes each
 // weight step once either way; with 8 waves each thread decodes half a block
