@@ -83,6 +83,16 @@ def test_ragged_shapes_match_oracle(M, K, N, r, alpha):
     _compare(c.run(), c.oracle(), f"ragged{M}x{K}x{N}r{r}")
 
 
+def test_wide_dx_tiles_ragged_rows_odd_rank():
+    # K = 32768 output columns at M = 300 make 2 x 128 = 256 dX tiles of 256 x
+    # 256, one whole round, so the dX runs unsplit on the wide 8-wave build:
+    # its last row tile holds 44 rows, and r = 5 takes the LoRA step's
+    # element-wise A-tile loads (done by half of its threads).
+    require_gpu()
+    c = Case(300, 32768, 256, 5, 7.0, ("wide-dx", 300, 32768, 256, 5))
+    _compare(c.run(), c.oracle(), "wide-dx")
+
+
 def test_accumulate_adds_to_existing_grads():
     require_gpu()
     c = Case(64, 256, 512, 8, 16.0, ("linear_pr1",))
