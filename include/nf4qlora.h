@@ -203,7 +203,9 @@ ql_status qlora_linear_bwd(const void* dy, const void* x, const void* u_saved, i
  * needs no clearing (every temporary is written before it is read) and keeps
  * nothing between calls, but all calls on one device share it: calls that
  * overlap on one device (concurrent streams, or host threads) race, so order
- * them on one stream. */
+ * them on one stream. The wide dX kernel keeps a few values in per-lane
+ * private memory (register spills, 44 bytes per lane), which the HIP runtime
+ * backs from its own scratch pool when such a kernel first runs on a queue. */
 #define QL_NOALLOC_SCRATCH_BYTES (128u << 20)
 ql_status qlora_linear_bwd_noalloc(const void* dy, const void* x, const void* u_saved, int64_t M,
                                    ql_nf4_weight W, ql_lora L, void* dx, float* dA, float* dB,
